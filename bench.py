@@ -1,0 +1,325 @@
+"""Benchmark: forward convolution through the HIP library on one MI355X.
+
+A step is one pass of the whole path over the workload's batch: for every
+layer, the filter pack, the input lowering (im2win strips by default) and the
+MFMA contraction with its fused bias epilogue; chained layers feed each
+other's outputs.  Inputs are resident in device memory before timing starts.
+
+Default workload (N=1): the MSCRED-style encoder stack -- 1280 images of three
+30x30 symmetric signature matrices, fp32 NCHW, four convolutions 3x3 3->32 s1
+p1, 3x3 32->64 s2, 2x2 64->128 s2, 2x2 128->256 s2 ("GPU-Accelerating MSCRED
+with CUDA, im2col, GEMM, and a Custom PyTorch Extension", sections
+"Experimental Setup" and "Where the Performance Bottleneck Appeared").  The
+other workloads (c1, c3, c4, c5) can be timed with --workload.
+
+Prints one JSON line: TFLOP/s of the whole step (2*N*K*P*Q*C*R*S summed over
+layers / step time), the roofline position of the dominant kernel measured
+with HIP events on its own stream over the timed region, and the fp64
+reference convolution timed on the host cores on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "conv2d fwd TFLOPS and % of MFMA peak; workspace bytes vs im2col"
+# MI355X published peaks: dense MFMA per storage type, HBM3E bandwidth
+PEAK_TFLOPS = {"f32": 157.3, "f16": 2516.6, "bf16": 2516.6}
+PEAK_HBM_GBS = 8000.0
+WORKLOAD_TEXT = {
+    "c1": "single conv2d fp32 NCHW N=1 3x30x30, 3x3 3->32 s1 p1",
+    "c2": "MSCRED-style encoder stack fp32 NCHW N=1280 (256 windows x 5 steps) of 3x30x30 symmetric signature "
+          "matrices: 3x3 3->32 s1p1; 3x3 32->64 s2; 2x2 64->128 s2; 2x2 128->256 s2",
+    "c3": "ResNet-style 3x3 fp16 NHWC N=64 C=K=256 14x14 s1 p1",
+    "c4": "mixed bf16 NHWC N=128: 7x7 s2p3 3->64 224x224; 1x1 1024->256 14x14; 3x3 512->512 7x7",
+    "c5": "kernel-size sweep fp16 NHWC N=32 C=K=128 64x64 same padding R=S in {1,3,5,7,11}",
+}
+CSRC = os.path.join(ROOT, "cnn_convolution_lowering_amd", "csrc")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def build_layers(wl, dev, algo):
+    import cnn_convolution_lowering_amd as cl
+    import torch
+    spec = wl.spec
+    layers = []
+    prev_y = None
+    for L in wl.layers:
+        x = L.x.to(dev) if L.x is not None else prev_y
+        d = cl.Conv2d(*(_x_dims(x.shape, spec.layout)), L.K, L.R, L.S, stride=L.stride, padding=L.padding,
+                      dilation=L.dilation, layout=spec.layout, dtype=spec.dtype, algo=algo)
+        y = d.new_output(dev)
+        layers.append(dict(spec=L, desc=d, x=x, w=L.w.to(dev), b=L.b.to(dev), y=y,
+                           flops=2 * spec.N * L.K * d.P * d.Q * L.C * L.R * L.S))
+        prev_y = y if spec.chained else None
+    ws_bytes = max(l["desc"].workspace_bytes for l in layers)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    return layers, ws
+
+
+def _x_dims(shape, layout):
+    if layout == "nchw":
+        N, C, H, W = shape
+    else:
+        N, H, W, C = shape
+    return N, C, H, W
+
+
+STAGES = ("pack", "lower", "contract")
+
+
+def run_stage(l, stage, ws, stream):
+    d = l["desc"]
+    if stage == "pack":
+        d.pack_filter(l["w"], ws, stream)
+    elif stage == "lower":
+        d.lower_input(l["x"], ws, stream)
+    else:
+        d.contract(l["x"], l["w"], l["b"], l["y"], ws, stream)
+
+
+def stage_launches(l, stage) -> bool:
+    info = l["desc"].info
+    if stage == "pack":
+        return info["ws_filter_bytes"] > 0
+    if stage == "lower":
+        return info["lowering_elided"] == 0
+    return True
+
+
+def kernel_breakdown(layers, ws, stream, reps=10):
+    """Average duration (ms) of every launched kernel, from HIP events on `stream`."""
+    import torch
+    out = {}
+    for i, l in enumerate(layers):
+        for st in STAGES:
+            if not stage_launches(l, st):
+                continue
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+            for a, b in evs:
+                for st2 in STAGES:          # keep the data flow of a real step
+                    if st2 == st:
+                        a.record(stream)
+                        run_stage(l, st2, ws, stream)
+                        b.record(stream)
+                    else:
+                        run_stage(l, st2, ws, stream)
+            torch.cuda.synchronize()
+            out[(i, st)] = sum(a.elapsed_time(b) for a, b in evs) / reps
+    return out
+
+
+def kernel_work(l, stage):
+    """(algorithmic flops, algorithmic bytes) of one launch of a stage kernel."""
+    info = l["desc"].info
+    eb = info["elem_bytes"]
+    d = l["desc"]
+    p = d.params
+    x_bytes = p.N * p.C * p.H * p.W * eb
+    w_bytes = p.K * p.C * p.R * p.S * eb
+    y_bytes = p.N * p.K * d.P * d.Q * eb
+    if stage == "contract":
+        a_bytes = x_bytes if info["lowering_elided"] else info["ws_lowered_bytes"]
+        b_bytes = info["ws_filter_bytes"] or w_bytes
+        return l["flops"], a_bytes + b_bytes + y_bytes + p.K * eb
+    if stage == "lower":
+        return 0, x_bytes + info["ws_lowered_bytes"]
+    return 0, w_bytes + info["ws_filter_bytes"]
+
+
+def kernel_symbol(l, stage):
+    d = l["desc"]
+    return {"pack": "pack_filter_kernel", "contract": "igemm_kernel"}.get(
+        stage, "%s_%s_kernel" % (d.algo, d.layout))
+
+
+def cpu_baseline(wl, budget_s=10.0):
+    """The fp64 reference convolution, as it stands, on a bounded sample of the
+    workload's images (every layer, chained as the workload chains them)."""
+    import numpy as np
+    import torch
+    import oracle
+    spec = wl.spec
+    threads = oracle.default_threads()
+
+    def run(n_img):
+        flops = 0
+        t0 = time.perf_counter()
+        prev = None
+        for L in wl.layers:
+            x = (L.x[:n_img] if L.x is not None else prev)
+            y = oracle.conv2d(x, L.w, L.b, layout=spec.layout, stride=L.stride, padding=L.padding,
+                              dilation=L.dilation, nthreads=threads)
+            if spec.layout == "nchw":
+                _, K, P, Q = y.shape
+            else:
+                _, P, Q, K = y.shape
+            flops += 2 * n_img * K * P * Q * L.C * L.R * L.S
+            prev = torch.from_numpy(np.ascontiguousarray(y)).to(wl.dtype) if spec.chained else None
+        return flops, time.perf_counter() - t0
+
+    probe = max(1, min(spec.N, 4))
+    f, t = run(probe)
+    n = int(min(spec.N, max(probe, probe * budget_s / max(t, 1e-6))))
+    if n > probe:
+        f, t = run(n)
+    else:
+        n = probe
+    return {"value": f / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "%d of %d images of workload %s, all %d layers, fp64 seven-loop reference, %.1f s"
+                      % (n, spec.N, spec.name, len(wl.layers), t)}
+
+
+def load_traffic(kernel_key: str):
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(kernel_key)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha256_16") != source_digest():
+        return None      # counters were taken on a different kernel source
+    return rec.get("bytes_per_launch")
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c2", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--algo", default="im2win", choices=["im2win", "im2col"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of reference work to time")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print("bench.py: this build measures one GPU; --gpus %d is not supported (the path shards over "
+              "images with no exchange, see the design notes)" % args.gpus, file=sys.stderr)
+        return 2
+
+    import torch
+    import cnn_convolution_lowering_amd as cl
+    from cnn_convolution_lowering_amd.workloads import make_workload
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    cl.load_library()
+    dev = torch.device("cuda:0")
+    wl = make_workload(args.workload)
+    spec = wl.spec
+    print("bench: workload %s, algo %s, building inputs" % (spec.name, args.algo), file=sys.stderr, flush=True)
+    layers, ws = build_layers(wl, dev, args.algo)
+    stream = torch.cuda.current_stream(dev)
+    step_flops = sum(l["flops"] for l in layers)
+
+    # Per-kernel durations (outside the timed region) pick the dominant kernel.
+    for _ in range(2):
+        for l in layers:
+            for st in STAGES:
+                run_stage(l, st, ws, stream)
+    torch.cuda.synchronize()
+    brk = kernel_breakdown(layers, ws, stream)
+    dom = max(brk, key=brk.get)
+    dom_layer, dom_stage = dom
+
+    def step(rec=None):
+        for i, l in enumerate(layers):
+            for st in STAGES:
+                if rec is not None and (i, st) == dom:
+                    rec[0].record(stream)
+                    run_stage(l, st, ws, stream)
+                    rec[1].record(stream)
+                else:
+                    run_stage(l, st, ws, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print("bench: timing %d steps" % args.steps, file=sys.stderr, flush=True)
+    recs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    h0 = time.perf_counter()
+    t_start.record(stream)
+    for k in range(args.steps):
+        step(recs[k])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    h1 = time.perf_counter()
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    dom_ms = sum(a.elapsed_time(b) for a, b in recs) / args.steps
+    tflops = step_flops / (ms_step * 1e-3) / 1e12
+
+    # roofline of the dominant kernel
+    dl = layers[dom_layer]
+    flops, nbytes = kernel_work(dl, dom_stage)
+    peak_f = PEAK_TFLOPS[spec.dtype]
+    compute_bound = flops > 0 and flops / (peak_f * 1e12) >= nbytes / (PEAK_HBM_GBS * 1e9)
+    kernel_key = "%s/%s/layer%d/%s" % (spec.name, args.algo, dom_layer, dom_stage)
+    traffic = load_traffic(kernel_key)
+    if compute_bound:
+        achieved = flops / (dom_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": peak_f, "unit": "TFLOP/s", "frac": achieved / peak_f}
+    else:
+        achieved = nbytes / (dom_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS}
+    roof.update({"traffic": traffic, "kernel": kernel_symbol(dl, dom_stage), "kernel_key": kernel_key,
+                 "layer": dl["spec"].label, "avg_launch_ms": dom_ms, "algorithmic_flops": flops,
+                 "algorithmic_bytes": nbytes})
+
+    per_layer = []
+    for i, l in enumerate(layers):
+        info = l["desc"].info
+        lay_ms = sum(v for (j, _), v in brk.items() if j == i)
+        per_layer.append({
+            "layer": l["spec"].label, "gflop": l["flops"] / 1e9,
+            "kernels_ms": {st: round(brk[(i, st)], 5) for st in STAGES if (i, st) in brk},
+            "tflops_isolated": l["flops"] / (lay_ms * 1e-3) / 1e12 if lay_ms else None,
+            "ws_lowered_bytes": info["ws_lowered_bytes"], "im2col_bytes": info["im2col_bytes"],
+            "ws_vs_im2col": info["ws_lowered_bytes"] / info["im2col_bytes"],
+            "tile": [info["tile_m"], info["tile_n"], info["tile_k"]]})
+
+    out = {
+        "metric": METRIC, "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": spec.dtype, "data": "synthetic",
+        "config": {"workload": "%s: %s" % (spec.name, WORKLOAD_TEXT[spec.name]), "algo": args.algo,
+                   "batch": spec.N, "layers": len(layers), "layout": spec.layout},
+        "pct_of_mfma_peak": 100.0 * tflops / peak_f,
+        "host_ms_per_step": (h1 - h0) * 1e3 / args.steps,
+        "roofline": roof,
+        "workspace": {"bytes": max(l["desc"].workspace_bytes for l in layers),
+                      "lowered_max_bytes": max(p["ws_lowered_bytes"] for p in per_layer),
+                      "im2col_max_bytes": max(p["im2col_bytes"] for p in per_layer),
+                      "ratio_max_over_layers": max(p["ws_vs_im2col"] for p in per_layer)},
+        "layers": per_layer,
+    }
+    if not args.no_cpu_baseline:
+        print("bench: timing the fp64 reference on the host", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,45 @@
+// Device-side types and helpers shared by the lowering and contraction kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace convlower {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Elements per 16-byte vector: every global load and store of the lowering
+// and contraction kernels moves whole 16-byte vectors where the layout allows.
+template <typename T>
+struct Vec {
+    static constexpr int n = 16 / sizeof(T);
+};
+
+__device__ __forceinline__ u32x4 zero4() { return u32x4{0u, 0u, 0u, 0u}; }
+
+__device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+__device__ __forceinline__ void store16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+// Pack VEC elements into one 16-byte vector (used where a vector is gathered
+// element by element).
+template <typename T>
+struct Pack16 {
+    union {
+        u32x4 v;
+        T e[Vec<T>::n];
+    };
+};
+
+template <typename T>
+__device__ __forceinline__ float to_f32(T v) { return static_cast<float>(v); }
+
+// fp32 -> storage type, round to nearest even (the hardware default mode).
+template <typename T>
+__device__ __forceinline__ T from_f32(float v) { return static_cast<T>(v); }
+
+}  // namespace convlower

@@ -1,0 +1,287 @@
+// Lowering kernels: window strips (im2win), explicit im2col rows, filter pack.
+//
+// Both lowered layouts order one contraction row as (s, r, c): for kernel
+// column s, the R*C values x[h_r][w_s][c] of one padded input column, padded
+// with zeros to RCp = R*C rounded up to a whole 16-byte vector.
+//
+//  im2win  Win[n][p][j][t], t < RCp: input column w = j - pw of the R input
+//          rows h = p*sh - ph + r*dh, for the W_used columns j the windows of
+//          output row p touch.  A contraction row (n, p, q) is the S strip
+//          columns j = q*sw + s*dw, so overlapping windows share storage and
+//          (for dw = 1) a row is one contiguous run -- the window layout of
+//          "Enabling Memory-efficient Im2win Convolution with Multi-precision
+//          Support on GPU CUDA and Tensor Cores" (abstract).
+//  im2col  Col[m = (n,p,q)][s*RCp + t]: one materialised row per output pixel,
+//          the explicit matrix of overlapping windows of "GPU-Accelerating
+//          MSCRED with CUDA, im2col, GEMM, and a Custom PyTorch Extension",
+//          section "Transforming Conv2D into im2col and GEMM".
+//
+// Zero padding of the convolution is written into the lowered buffer, so the
+// contraction never tests bounds on the input.
+#pragma once
+
+#include "device_common.hpp"
+
+namespace convlower {
+
+struct LowerArgs {
+    const void* x;
+    void* out;
+    int32_t N, C, H, W;
+    int32_t P, Q, R, S;
+    int32_t sh, sw, ph, pw, dh, dw;
+    int32_t W_used;   // strip columns per (n, p)
+    int32_t RCp;      // R*C padded to whole vectors
+    int32_t Kl;       // S*RCp
+    int32_t chunk;    // strip columns (im2win NCHW) or output columns (im2col NCHW) per block
+    int32_t lds_ld;   // LDS row pitch (elements) of the NCHW staging tile
+};
+
+// x element (n, c, h, w) in either layout, zero outside the image.
+template <typename T, bool NHWC>
+__device__ __forceinline__ T x_at(const LowerArgs& a, const T* __restrict__ x, int n, int c, int h, int w) {
+    if (h < 0 || h >= a.H || w < 0 || w >= a.W) return T(0);
+    int64_t off = NHWC ? ((int64_t(n) * a.H + h) * a.W + w) * a.C + c
+                       : ((int64_t(n) * a.C + c) * a.H + h) * a.W + w;
+    return x[off];
+}
+
+// ---------------------------------------------------------------------------
+// im2win, NHWC input: one thread per 16-byte vector of the strip.  When C is a
+// whole number of vectors, a vector of the strip is a vector of one x row, so
+// the copy is 16-byte load -> 16-byte store; otherwise it gathers elements.
+// grid.x = N*P strips, grid.y = ceil(W_used*RCp/VEC / 256).
+template <typename T, bool C_VEC>
+__global__ void __launch_bounds__(256) im2win_nhwc_kernel(LowerArgs a) {
+    constexpr int VEC = Vec<T>::n;
+    const int strip = blockIdx.x;
+    const int cpv = a.RCp / VEC;                 // vectors per strip column
+    const int v = blockIdx.y * 256 + threadIdx.x;
+    if (v >= a.W_used * cpv) return;
+    const int n = strip / a.P, p = strip - (strip / a.P) * a.P;
+    const int j = v / cpv;
+    const int t0 = (v - j * cpv) * VEC;
+    const int wcol = j - a.pw;
+    const T* __restrict__ x = static_cast<const T*>(a.x);
+    T* out = static_cast<T*>(a.out) + (int64_t(strip) * a.W_used * a.RCp + int64_t(v) * VEC);
+    if (C_VEC) {
+        const int r = t0 / a.C, c0 = t0 - (t0 / a.C) * a.C;
+        const int h = p * a.sh - a.ph + r * a.dh;
+        u32x4 val = zero4();
+        if (h >= 0 && h < a.H && wcol >= 0 && wcol < a.W)
+            val = load16(x + ((int64_t(n) * a.H + h) * a.W + wcol) * a.C + c0);
+        store16(out, val);
+    } else {
+        Pack16<T> pk;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            const int t = t0 + e;
+            T val = T(0);
+            if (t < a.R * a.C) {
+                const int r = t / a.C, c = t - (t / a.C) * a.C;
+                val = x_at<T, true>(a, x, n, c, p * a.sh - a.ph + r * a.dh, wcol);
+            }
+            pk.e[e] = val;
+        }
+        store16(out, pk.v);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// NCHW input: x rows are contiguous along w, the strip is contiguous along
+// (r, c) inside a column, so stage through LDS: read coalesced along w into a
+// [column][r*C + c] tile, then write whole 16-byte strip vectors.
+// Tile rows [j0, j0 + ncols) of strip (n, p); LDS pitch a.lds_ld elements.
+template <typename T>
+__device__ __forceinline__ void stage_strip_nchw(const LowerArgs& a, T* tile, int n, int p, int j0, int ncols) {
+    const T* __restrict__ x = static_cast<const T*>(a.x);
+    const int RC = a.R * a.C;
+    const int total = ncols * RC;
+    for (int idx = threadIdx.x; idx < total; idx += blockDim.x) {
+        const int jj = idx % ncols;
+        const int rc = idx / ncols;
+        const int c = rc % a.C, r = rc / a.C;
+        const int h = p * a.sh - a.ph + r * a.dh;
+        tile[jj * a.lds_ld + rc] = x_at<T, false>(a, x, n, c, h, j0 + jj - a.pw);
+    }
+}
+
+// grid.x = N*P strips, grid.y = ceil(W_used / chunk); dynamic LDS = chunk*lds_ld elements.
+template <typename T>
+__global__ void __launch_bounds__(256) im2win_nchw_kernel(LowerArgs a) {
+    constexpr int VEC = Vec<T>::n;
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
+    T* tile = reinterpret_cast<T*>(lds_raw);
+    const int strip = blockIdx.x;
+    const int n = strip / a.P, p = strip - (strip / a.P) * a.P;
+    const int j0 = blockIdx.y * a.chunk;
+    const int ncols = min(a.chunk, a.W_used - j0);
+    stage_strip_nchw<T>(a, tile, n, p, j0, ncols);
+    __syncthreads();
+    const int RC = a.R * a.C;
+    const int cpv = a.RCp / VEC;
+    T* out = static_cast<T*>(a.out) + (int64_t(strip) * a.W_used + j0) * a.RCp;
+    for (int idx = threadIdx.x; idx < ncols * cpv; idx += blockDim.x) {
+        const int jj = idx / cpv, tv = idx - (idx / cpv) * cpv;
+        Pack16<T> pk;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            const int t = tv * VEC + e;
+            pk.e[e] = t < RC ? tile[jj * a.lds_ld + t] : T(0);
+        }
+        store16(out + int64_t(jj) * a.RCp + tv * VEC, pk.v);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// im2col, NHWC input: one thread per 16-byte vector of Col; grid-stride over
+// M*Kl/VEC vectors (checked on the host to fit 32 bits).
+template <typename T, bool C_VEC>
+__global__ void __launch_bounds__(256) im2col_nhwc_kernel(LowerArgs a, uint32_t total_vec) {
+    constexpr int VEC = Vec<T>::n;
+    const T* __restrict__ x = static_cast<const T*>(a.x);
+    const uint32_t vpr = a.Kl / VEC;   // vectors per Col row
+    const uint32_t cpv = a.RCp / VEC;
+    const uint32_t PQ = uint32_t(a.P) * a.Q;
+    for (uint32_t v = blockIdx.x * 256u + threadIdx.x; v < total_vec; v += gridDim.x * 256u) {
+        const uint32_t m = v / vpr, kv = v - (v / vpr) * vpr;
+        const uint32_t s = kv / cpv;
+        const int t0 = int(kv - s * cpv) * VEC;
+        const uint32_t n = m / PQ, pq = m - (m / PQ) * PQ;
+        const int p = int(pq / a.Q), q = int(pq - (pq / a.Q) * a.Q);
+        const int wcol = q * a.sw - a.pw + int(s) * a.dw;
+        T* out = static_cast<T*>(a.out) + int64_t(v) * VEC;
+        if (C_VEC) {
+            const int r = t0 / a.C, c0 = t0 - (t0 / a.C) * a.C;
+            const int h = p * a.sh - a.ph + r * a.dh;
+            u32x4 val = zero4();
+            if (h >= 0 && h < a.H && wcol >= 0 && wcol < a.W)
+                val = load16(x + ((int64_t(n) * a.H + h) * a.W + wcol) * a.C + c0);
+            store16(out, val);
+        } else {
+            Pack16<T> pk;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                const int t = t0 + e;
+                T val = T(0);
+                if (t < a.R * a.C) {
+                    const int r = t / a.C, c = t - (t / a.C) * a.C;
+                    val = x_at<T, true>(a, x, int(n), c, p * a.sh - a.ph + r * a.dh, wcol);
+                }
+                pk.e[e] = val;
+            }
+            store16(out, pk.v);
+        }
+    }
+}
+
+// im2col, NCHW input: a block stages the strip columns its output columns
+// [q0, q0 + chunk) need for one (n, p), then writes those Col rows.
+// grid.x = N*P, grid.y = ceil(Q / chunk); dynamic LDS = cols*lds_ld elements
+// with cols = (chunk-1)*sw + (S-1)*dw + 1.
+template <typename T>
+__global__ void __launch_bounds__(256) im2col_nchw_kernel(LowerArgs a) {
+    constexpr int VEC = Vec<T>::n;
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
+    T* tile = reinterpret_cast<T*>(lds_raw);
+    const int strip = blockIdx.x;
+    const int n = strip / a.P, p = strip - (strip / a.P) * a.P;
+    const int q0 = blockIdx.y * a.chunk;
+    const int nq = min(a.chunk, a.Q - q0);
+    const int j0 = q0 * a.sw;
+    const int ncols = (nq - 1) * a.sw + (a.S - 1) * a.dw + 1;
+    stage_strip_nchw<T>(a, tile, n, p, j0, ncols);
+    __syncthreads();
+    const int RC = a.R * a.C;
+    const int cpv = a.RCp / VEC;
+    const int vpr = a.Kl / VEC;
+    T* out = static_cast<T*>(a.out) + (int64_t(strip) * a.Q + q0) * a.Kl;
+    for (int idx = threadIdx.x; idx < nq * vpr; idx += blockDim.x) {
+        const int qq = idx / vpr, kv = idx - (idx / vpr) * vpr;
+        const int s = kv / cpv, tv = kv - (kv / cpv) * cpv;
+        const int jj = qq * a.sw + s * a.dw;
+        Pack16<T> pk;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            const int t = tv * VEC + e;
+            pk.e[e] = t < RC ? tile[jj * a.lds_ld + t] : T(0);
+        }
+        store16(out + int64_t(qq) * a.Kl + kv * VEC, pk.v);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Generic element-wise lowering for shapes whose NCHW staging tile would not
+// fit in LDS: one thread per 16-byte output vector, elements gathered one by one.
+template <typename T, bool NHWC, bool COL>
+__global__ void __launch_bounds__(256) lower_generic_kernel(LowerArgs a, uint32_t total_vec) {
+    constexpr int VEC = Vec<T>::n;
+    const T* __restrict__ x = static_cast<const T*>(a.x);
+    const uint32_t cpv = a.RCp / VEC;
+    for (uint32_t v = blockIdx.x * 256u + threadIdx.x; v < total_vec; v += gridDim.x * 256u) {
+        int n, p, wcol;
+        int t0;
+        if (COL) {
+            const uint32_t vpr = a.Kl / VEC;
+            const uint32_t m = v / vpr, kv = v - (v / vpr) * vpr;
+            const uint32_t s = kv / cpv;
+            t0 = int(kv - s * cpv) * VEC;
+            const uint32_t PQ = uint32_t(a.P) * a.Q;
+            n = int(m / PQ);
+            const uint32_t pq = m - uint32_t(n) * PQ;
+            p = int(pq / a.Q);
+            const int q = int(pq - uint32_t(p) * a.Q);
+            wcol = q * a.sw - a.pw + int(s) * a.dw;
+        } else {
+            const uint32_t vps = uint32_t(a.W_used) * cpv;
+            const uint32_t strip = v / vps, rem = v - (v / vps) * vps;
+            n = int(strip / a.P);
+            p = int(strip - uint32_t(n) * a.P);
+            const int j = int(rem / cpv);
+            t0 = int(rem - uint32_t(j) * cpv) * VEC;
+            wcol = j - a.pw;
+        }
+        Pack16<T> pk;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            const int t = t0 + e;
+            T val = T(0);
+            if (t < a.R * a.C) {
+                const int r = t / a.C, c = t - (t / a.C) * a.C;
+                val = x_at<T, NHWC>(a, x, n, c, p * a.sh - a.ph + r * a.dh, wcol);
+            }
+            pk.e[e] = val;
+        }
+        store16(static_cast<T*>(a.out) + int64_t(v) * VEC, pk.v);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Filter pack: Bp[k][s*RCp + r*C + c] = w[k, c, r, s] (zeros in the padding),
+// the filter matrix reshaped to the lowered row order.
+struct PackArgs {
+    const void* w;
+    void* out;
+    int32_t K, C, R, S, RCp, Kl;
+};
+
+template <typename T, bool NHWC>
+__global__ void __launch_bounds__(256) pack_filter_kernel(PackArgs a) {
+    const T* __restrict__ w = static_cast<const T*>(a.w);
+    T* out = static_cast<T*>(a.out);
+    const int total = a.K * a.Kl;
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < total; i += gridDim.x * 256) {
+        const int k = i / a.Kl, kk = i - (i / a.Kl) * a.Kl;
+        const int s = kk / a.RCp, t = kk - (kk / a.RCp) * a.RCp;
+        T val = T(0);
+        if (t < a.R * a.C) {
+            const int r = t / a.C, c = t - (t / a.C) * a.C;
+            const int64_t src = NHWC ? ((int64_t(k) * a.R + r) * a.S + s) * a.C + c
+                                     : ((int64_t(k) * a.C + c) * a.R + r) * a.S + s;
+            val = w[src];
+        }
+        out[i] = val;
+    }
+}
+
+}  // namespace convlower

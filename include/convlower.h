@@ -1,0 +1,168 @@
+/*
+ * convlower.h -- forward 2-D convolution lowered to a dense contraction on
+ * AMD Instinct MI355X (gfx950): im2win window strips or explicit im2col
+ * columns, then an LDS-staged MFMA contraction with a fused bias epilogue.
+ *
+ * The operation (cross-correlation, zero padding):
+ *
+ *   y[n,k,p,q] = b[k] + sum_{c<C, r<R, s<S}
+ *                x[n, c, p*sh - ph + r*dh, q*sw - pw + s*dw] * w[k, c, r, s]
+ *   P = floor((H + 2 ph - dh (R-1) - 1) / sh) + 1,  Q likewise,
+ *
+ * as described in "GPU-Accelerating MSCRED with CUDA, im2col, GEMM, and a
+ * Custom PyTorch Extension" (section "Transforming Conv2D into im2col and
+ * GEMM": the output matrix is the reshaped filter matrix times the im2col
+ * matrix of overlapping input windows), with the window-strip layout of
+ * "Enabling Memory-efficient Im2win Convolution with Multi-precision Support
+ * on GPU CUDA and Tensor Cores" (abstract: contiguous memory access for every
+ * kernel size, lower memory than explicit im2col).
+ *
+ * Conventions shared by every entry point
+ *  - All tensors are dense and packed (no strides).  layout CONV_NCHW means
+ *    x is NCHW, w is KCRS and y is NKPQ; CONV_NHWC means x NHWC, w KRSC,
+ *    y NPQK.  x, w, bias and y share one storage type; products are formed
+ *    from the stored values and accumulated in fp32; y is rounded to the
+ *    storage type once, round-to-nearest-even, after the bias is added.
+ *  - x, w, bias, y and ws are DEVICE pointers owned by the caller.  x, w, y
+ *    and ws must be 16-byte aligned; bias must be aligned to its element.
+ *    y must not overlap x, w, bias or ws.
+ *  - The library never allocates device memory, never copies between host
+ *    and device and never synchronises.  Work is enqueued on `stream` (a
+ *    hipStream_t; NULL = the default stream) and runs asynchronously; errors
+ *    found on the host are returned before anything is enqueued, launch
+ *    failures come back as CONV_ERR_HIP, and faults inside a kernel surface
+ *    at the caller's next synchronisation.
+ *  - There is no fallback: a case the kernels do not cover returns
+ *    CONV_ERR_UNSUPPORTED and nothing runs.
+ *  - A descriptor is immutable after creation; one descriptor may be used
+ *    from several threads and streams at once if each call has its own ws.
+ */
+#ifndef CONVLOWER_H
+#define CONVLOWER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    CONV_OK = 0,
+    CONV_ERR_INVALID_ARG = -1,     /* sizes, strides, enum values out of range */
+    CONV_ERR_UNSUPPORTED = -2,     /* valid convolution the kernels do not cover */
+    CONV_ERR_NULL_PTR = -3,        /* a required pointer is NULL */
+    CONV_ERR_NOT_DEVICE_PTR = -4,  /* a tensor pointer is not device memory */
+    CONV_ERR_MISALIGNED = -5,      /* a tensor pointer breaks the alignment rule */
+    CONV_ERR_HIP = -6,             /* the HIP runtime reported an error */
+    CONV_ERR_OOM = -7              /* host allocation of a descriptor failed */
+} conv_status_t;
+
+typedef enum { CONV_NCHW = 0, CONV_NHWC = 1 } conv_layout_t;
+typedef enum { CONV_F32 = 0, CONV_F16 = 1, CONV_BF16 = 2 } conv_dtype_t;
+
+/* How the input is lowered before the contraction.
+ *  CONV_ALGO_IM2WIN  for each (image n, output row p) one contiguous window
+ *                    strip Win[n][p][j][r*C + c] over the W_used padded input
+ *                    columns j the row's windows touch; a GEMM row (n,p,q) is
+ *                    then the run of S strip columns starting at q*sw
+ *                    (every dw-th column), so overlapping windows share
+ *                    storage (the im2win layout).
+ *  CONV_ALGO_IM2COL  explicit im2col: one materialised row per output pixel,
+ *                    Col[(n,p,q)][s][r*C + c] (the baseline the im2win
+ *                    workspace is compared against).
+ * For 1x1 kernels on NHWC input with no padding, both algorithms read x in
+ * place and use no lowering workspace. */
+typedef enum { CONV_ALGO_IM2WIN = 0, CONV_ALGO_IM2COL = 1 } conv_algo_t;
+
+typedef struct {
+    int64_t N, C, H, W;        /* input: batch, channels, height, width */
+    int64_t K, R, S;           /* filter: output channels, kernel height, kernel width */
+    int32_t stride_h, stride_w;
+    int32_t pad_h, pad_w;      /* symmetric zero padding per dimension */
+    int32_t dil_h, dil_w;
+    conv_layout_t layout;
+    conv_dtype_t dtype;
+    conv_algo_t algo;
+} conv_params_t;
+
+typedef struct conv_desc* conv_desc_t;   /* opaque; owned by the library */
+
+/* What a descriptor decided: extents, GEMM shape, workspace layout, tiling.
+ * Filled by conv_plan_info; for reporting and for tests of the layouts. */
+typedef struct {
+    int64_t P, Q;              /* output extents */
+    int64_t M;                 /* GEMM rows = N*P*Q */
+    int64_t Kg;                /* contraction length of the definition = C*R*S */
+    int64_t W_used;            /* padded input columns one output row's windows touch */
+    int64_t RCp;               /* R*C rounded up to a 16-byte multiple of elements */
+    int64_t Kl;                /* lowered contraction length = S*RCp (zeros in the padding) */
+    uint64_t ws_bytes;         /* total workspace the caller must pass */
+    uint64_t ws_filter_offset, ws_filter_bytes;    /* packed filter Bp[K][Kl] */
+    uint64_t ws_lowered_offset, ws_lowered_bytes;  /* window strips or im2col rows */
+    uint64_t im2win_bytes;     /* N*P*W_used*RCp*elem: im2win strip bytes for this shape */
+    uint64_t im2col_bytes;     /* N*P*Q*C*R*S*elem: the plain explicit im2col matrix */
+    int32_t lowering_elided;   /* 1: x is read in place (1x1 NHWC, no padding) */
+    int32_t tile_m, tile_n, tile_k;  /* contraction tile chosen for this shape */
+    int32_t elem_bytes;
+} conv_plan_info_t;
+
+/* Validate *p and build a descriptor.  Host only: no HIP call is made, so it
+ * works without a GPU.  Errors: CONV_ERR_NULL_PTR (p or out NULL),
+ * CONV_ERR_INVALID_ARG (N < 0, C/H/W/K/R/S <= 0, stride or dilation <= 0,
+ * padding < 0, bad enum, or a kernel that does not fit the padded input, i.e.
+ * P or Q <= 0), CONV_ERR_UNSUPPORTED (sizes beyond the 32-bit index ranges the
+ * kernels use), CONV_ERR_OOM.  On success *out owns a descriptor the caller
+ * must release with conv_destroy_desc. */
+conv_status_t conv_create_desc(const conv_params_t* p, conv_desc_t* out);
+
+/* Release a descriptor (NULL is accepted and ignored). */
+conv_status_t conv_destroy_desc(conv_desc_t d);
+
+/* Bytes of device workspace conv2d_fwd needs for this descriptor (may be 0).
+ * Host only. */
+conv_status_t conv_workspace_size(conv_desc_t d, size_t* bytes);
+
+/* Output extents P, Q (floor formula above).  Host only. */
+conv_status_t conv_output_dims(conv_desc_t d, int64_t* P, int64_t* Q);
+
+/* The descriptor's plan (see conv_plan_info_t).  Host only. */
+conv_status_t conv_plan_info(conv_desc_t d, conv_plan_info_t* info);
+
+/* The whole forward convolution: conv_pack_filter, conv_lower_input and
+ * conv_contract enqueued in that order on `stream`.
+ *   x     input, N*C*H*W elements in the descriptor's layout
+ *   w     filter, K*C*R*S elements (KCRS or KRSC)
+ *   bias  K elements, or NULL for no bias
+ *   y     output, N*K*P*Q elements (NKPQ or NPQK); fully overwritten
+ *   ws    at least conv_workspace_size bytes (NULL iff that size is 0); its
+ *         contents on entry are ignored and on return are unspecified
+ * N == 0 is accepted and enqueues nothing. */
+conv_status_t conv2d_fwd(conv_desc_t d, const void* x, const void* w, const void* bias, void* y,
+                         void* ws, void* stream);
+
+/* Stage 1 of conv2d_fwd: reorder w into the packed contraction operand
+ * Bp[k][s*RCp + r*C + c] in ws (zeros in the RCp padding).  A no-op when the
+ * filter is already in that order (NHWC with R == 1 or S == 1 and C a
+ * multiple of the 16-byte vector). */
+conv_status_t conv_pack_filter(conv_desc_t d, const void* w, void* ws, void* stream);
+
+/* Stage 2: lower x into ws -- im2win strips or im2col rows, per the
+ * descriptor's algorithm.  A no-op when the lowering is elided. */
+conv_status_t conv_lower_input(conv_desc_t d, const void* x, void* ws, void* stream);
+
+/* Stage 3: the MFMA contraction over the lowered operand and packed filter
+ * with the fused epilogue y = round(acc + bias[k]).  Reads ws written by
+ * stages 1 and 2; reads x in place when the lowering is elided and w in place
+ * when the pack is a no-op. */
+conv_status_t conv_contract(conv_desc_t d, const void* x, const void* w, const void* bias, void* y,
+                            const void* ws, void* stream);
+
+/* Static English text for a status code. */
+const char* conv_status_string(conv_status_t s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CONVLOWER_H */

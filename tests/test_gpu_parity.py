@@ -1,0 +1,308 @@
+"""GPU parity: the HIP path (called through the C ABI) against the fp64
+reference convolution, on seeded inputs.
+
+Covers: a fuzz over shapes, strides, padding, dilation, layouts, storage types
+and both lowerings (several tiles and ragged tails in every GEMM dimension);
+integer-valued inputs, where fp32 accumulation is exact and the result must
+equal the reference rounded to the storage type bit for bit; delta kernels
+(y == x bit for bit); the lowered buffers and packed filter byte for byte;
+determinism; the staged entry points; error paths; and the five workloads at
+their full sizes in the launch configuration the benchmark times.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import cnn_convolution_lowering_amd as cl
+import oracle
+from parity import (TORCH_DT, assert_parity, expected_im2col, expected_im2win, expected_packed_filter,
+                    gather, sample_points, to_f64, to_nkpq)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    cl.load_library()          # raises if the HIP library is not built: there is no other path
+    return torch.device("cuda:0")
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _perm_x(x_nchw, layout):
+    return x_nchw.permute(0, 2, 3, 1).contiguous() if layout == "nhwc" else x_nchw.contiguous()
+
+
+def _run(dev, x, w, b, layout, stride, pad, dil, algo):
+    d = cl.descriptor(tuple(x.shape), tuple(w.shape), stride=stride, padding=pad, dilation=dil, layout=layout,
+                      dtype={torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}[x.dtype],
+                      algo=algo)
+    xd, wd = x.to(dev), w.to(dev)
+    bd = None if b is None else b.to(dev)
+    y = d.forward(xd, wd, bd)
+    torch.cuda.synchronize()
+    return y.cpu()
+
+
+def _check_full(dev, x, w, b, layout, stride, pad, dil, algo, dtype, what):
+    _say("case %s" % what)
+    y = _run(dev, x, w, b, layout, stride, pad, dil, algo)
+    ref, yabs = oracle.conv2d(x, w, b, layout=layout, stride=stride, padding=pad, dilation=dil, with_abs=True)
+    return assert_parity(to_f64(y), ref, yabs, dtype, what)
+
+
+# ---------------------------------------------------------------- fuzz
+
+def _fuzz_cases():
+    rng = np.random.default_rng(2024)
+    cases = []
+    combos = [(dt, lay, algo) for dt in ("f32", "f16", "bf16") for lay in ("nchw", "nhwc")
+              for algo in ("im2win", "im2col")]
+    for i in range(72):
+        dt, lay, algo = combos[i % len(combos)]
+        R, S = int(rng.integers(1, 6)), int(rng.integers(1, 6))
+        st = (int(rng.integers(1, 4)), int(rng.integers(1, 4)))
+        dl = (int(rng.integers(1, 3)), int(rng.integers(1, 3))) if i % 3 == 0 else (1, 1)
+        pd = (int(rng.integers(0, 4)), int(rng.integers(0, 4)))
+        C = int(rng.choice([1, 3, 5, 8, 16, 19, 32, 40, 64]))
+        K = int(rng.choice([1, 7, 16, 31, 32, 33, 64, 65, 100, 128, 150]))
+        N = int(rng.integers(1, 4))
+        H = int(rng.integers(max(1, dl[0] * (R - 1) + 1 - 2 * pd[0]), 24))
+        W = int(rng.integers(max(1, dl[1] * (S - 1) + 1 - 2 * pd[1]), 24))
+        cases.append((i, dt, lay, algo, N, C, H, W, K, R, S, st, pd, dl))
+    return cases
+
+
+@pytest.mark.parametrize("case", _fuzz_cases(), ids=lambda c: "%d-%s-%s-%s-N%dC%dH%dW%dK%dR%dS%d-s%s-p%s-d%s" % c)
+def test_fuzz_parity(dev, case):
+    i, dt, lay, algo, N, C, H, W, K, R, S, st, pd, dl = case
+    g = torch.Generator().manual_seed(1000 + i)
+    x = (torch.rand(N, C, H, W, generator=g) * 2 - 1).to(TORCH_DT[dt])
+    w = (torch.randn(K, C, R, S, generator=g) / np.sqrt(C * R * S)).to(TORCH_DT[dt])
+    b = (torch.randn(K, generator=g) * 0.1).to(TORCH_DT[dt]) if i % 4 != 3 else None
+    _check_full(dev, _perm_x(x, lay), _perm_x(w, lay), b, lay, st, pd, dl, algo, dt, "fuzz %d" % i)
+
+
+# ---------------------------------------------------------------- exactness
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("lay", ["nchw", "nhwc"])
+@pytest.mark.parametrize("algo", ["im2win", "im2col"])
+def test_integer_inputs_bit_exact(dev, dt, lay, algo):
+    """Integer x, w, b: fp32 accumulation is exact (|partial sums| < 2^24), so y
+    must be the reference rounded once to the storage type (RNE), bit for bit."""
+    g = torch.Generator().manual_seed(7)
+    for (N, C, H, W, K, R, S, st, pd) in [(2, 24, 11, 9, 70, 3, 3, (1, 1), (1, 1)),
+                                          (1, 3, 20, 17, 33, 5, 4, (2, 1), (2, 0)),
+                                          (3, 64, 6, 6, 130, 1, 1, (1, 1), (0, 0)),
+                                          (2, 40, 8, 8, 48, 2, 2, (2, 2), (0, 0))]:
+        x = torch.randint(-2, 3, (N, C, H, W), generator=g).to(TORCH_DT[dt])
+        w = torch.randint(-2, 3, (K, C, R, S), generator=g).to(TORCH_DT[dt])
+        b = torch.randint(-4, 5, (K,), generator=g).to(TORCH_DT[dt])
+        xl, wl = _perm_x(x, lay), _perm_x(w, lay)
+        _say("int case C%d K%d R%d %s %s %s" % (C, K, R, dt, lay, algo))
+        y = _run(dev, xl, wl, b, lay, st, pd, (1, 1), algo)
+        ref = oracle.conv2d(xl, wl, b, layout=lay, stride=st, padding=pd)
+        assert np.all(np.abs(ref) < 2 ** 24)
+        want = torch.from_numpy(ref).to(torch.float32).to(TORCH_DT[dt])
+        assert torch.equal(y.view(torch.int16 if dt != "f32" else torch.int32),
+                           want.view(torch.int16 if dt != "f32" else torch.int32)), "%s %s %s" % (dt, lay, algo)
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("lay", ["nchw", "nhwc"])
+def test_delta_kernel_reproduces_input(dev, dt, lay):
+    g = torch.Generator().manual_seed(8)
+    for R in (1, 3, 5):
+        C = 24
+        x = (torch.rand(2, C, 13, 10, generator=g) * 8 - 4).to(TORCH_DT[dt])
+        w = torch.zeros(C, C, R, R)
+        for k in range(C):
+            w[k, k, R // 2, R // 2] = 1
+        w = w.to(TORCH_DT[dt])
+        for algo in ("im2win", "im2col"):
+            _say("delta R%d %s %s %s" % (R, dt, lay, algo))
+            y = _run(dev, _perm_x(x, lay), _perm_x(w, lay), None, lay, 1, R // 2, 1, algo)
+            assert torch.equal(y, _perm_x(x, lay)), (R, algo)
+
+
+# ---------------------------------------------------------------- lowered buffers byte for byte
+
+def _bits(t):
+    return t.view(torch.int16 if t.element_size() == 2 else torch.int32).numpy()
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("lay", ["nchw", "nhwc"])
+@pytest.mark.parametrize("shape", [(2, 3, 9, 11, 8, 3, 3, (1, 1), (1, 1), (1, 1)),
+                                   (1, 16, 7, 12, 5, 3, 2, (2, 3), (2, 1), (1, 2)),
+                                   (2, 8, 10, 10, 4, 2, 5, (1, 2), (0, 2), (2, 1))])
+def test_lowered_layouts_exact(dev, dt, lay, shape):
+    N, C, H, W, K, R, S, st, pd, dl = shape
+    g = torch.Generator().manual_seed(9)
+    x = (torch.rand(N, C, H, W, generator=g) * 2 - 1).to(TORCH_DT[dt])
+    w = torch.randn(K, C, R, S, generator=g).to(TORCH_DT[dt])
+    for algo in ("im2win", "im2col"):
+        d = cl.Conv2d(N, C, H, W, K, R, S, stride=st, padding=pd, dilation=dl, layout=lay, dtype=dt, algo=algo)
+        info = d.info
+        ws = torch.zeros(max(1, d.workspace_bytes), dtype=torch.uint8, device=dev)
+        _say("layout %s %s %s %s" % (shape, dt, lay, algo))
+        d.pack_filter(_perm_x(w, lay).to(dev), ws)
+        d.lower_input(_perm_x(x, lay).to(dev), ws)
+        torch.cuda.synchronize()
+        wsc = ws.cpu()
+        elem = info["elem_bytes"]
+        RCp, Kl, P, Q = info["RCp"], info["Kl"], info["P"], info["Q"]
+        xb, wb = _bits(x), _bits(w)
+        if info["ws_filter_bytes"]:
+            o = info["ws_filter_offset"]
+            got = wsc[o:o + info["ws_filter_bytes"]].view(x.dtype)
+            np.testing.assert_array_equal(_bits(got).reshape(K, Kl), expected_packed_filter(wb, RCp))
+        o = info["ws_lowered_offset"]
+        got = _bits(wsc[o:o + info["ws_lowered_bytes"]].view(x.dtype))
+        win = expected_im2win(xb, R, S, P, Q, st, pd, dl, RCp)
+        if algo == "im2win":
+            np.testing.assert_array_equal(got.reshape(win.shape), win)
+        else:
+            np.testing.assert_array_equal(got.reshape(N * P * Q, Kl), expected_im2col(win, Q, S, st[1], dl[1], RCp))
+
+
+# ---------------------------------------------------------------- properties of the path
+
+def test_deterministic_and_staged_equals_fused(dev):
+    g = torch.Generator().manual_seed(10)
+    for dt, lay in (("f16", "nhwc"), ("f32", "nchw"), ("bf16", "nchw")):
+        x = _perm_x((torch.rand(4, 32, 15, 15, generator=g) * 2 - 1).to(TORCH_DT[dt]), lay).to(dev)
+        w = _perm_x(torch.randn(96, 32, 3, 3, generator=g).to(TORCH_DT[dt]), lay).to(dev)
+        b = torch.randn(96, generator=g).to(TORCH_DT[dt]).to(dev)
+        d = cl.descriptor(tuple(x.shape), tuple(w.shape), padding=1, layout=lay, dtype=dt)
+        y1 = d.forward(x, w, b)
+        y2 = d.forward(x, w, b)
+        ws = d.new_workspace(dev)
+        y3 = d.new_output(dev)
+        d.pack_filter(w, ws)
+        d.lower_input(x, ws)
+        d.contract(x, w, b, y3, ws)
+        s = torch.cuda.Stream()
+        with torch.cuda.stream(s):
+            y4 = d.forward(x, w, b, stream=s)
+        torch.cuda.synchronize()
+        assert torch.equal(y1, y2) and torch.equal(y1, y3) and torch.equal(y1, y4)
+
+
+def test_empty_batch(dev):
+    d = cl.Conv2d(0, 8, 5, 5, 4, 3, 3, padding=1, layout="nhwc", dtype="f16")
+    x = torch.empty(0, 5, 5, 8, dtype=torch.float16, device=dev)
+    w = torch.randn(4, 3, 3, 8, device=dev).half()
+    y = d.forward(x, w)
+    torch.cuda.synchronize()
+    assert tuple(y.shape) == (0, 5, 5, 4)
+
+
+def test_error_paths(dev):
+    d = cl.Conv2d(1, 8, 6, 6, 8, 3, 3, padding=1, layout="nhwc", dtype="f16")
+    x = torch.randn(1, 6, 6, 8, device=dev).half()
+    w = torch.randn(8, 3, 3, 8, device=dev).half()
+    with pytest.raises(cl.ConvError) as e:                       # host memory is not accepted
+        d.forward(x.cpu(), w)
+    assert e.value.status == -4
+    big = torch.randn(1 * 6 * 6 * 8 + 8, device=dev).half()
+    xm = big[1:1 + 288].view(1, 6, 6, 8)                       # 2-byte offset: misaligned
+    with pytest.raises(cl.ConvError) as e:
+        d.forward(xm, w)
+    assert e.value.status == -5
+
+
+@pytest.mark.parametrize("lay", ["nchw", "nhwc"])
+def test_edge_shapes(dev, lay):
+    g = torch.Generator().manual_seed(11)
+    cases = [  # N, C, H, W, K, R, S, stride, pad, dil
+        (1, 1, 1, 1, 1, 1, 1, (1, 1), (0, 0), (1, 1)),
+        (1, 1, 5, 5, 1, 1, 1, (1, 1), (2, 2), (1, 1)),      # padding wider than the kernel: border = bias
+        (3, 8, 9, 9, 5, 1, 1, (2, 3), (0, 0), (1, 1)),      # 1x1 strided (read in place for NHWC)
+        (2, 5, 4, 30, 9, 1, 7, (1, 4), (0, 3), (1, 1)),     # wide kernel, large stride
+        (2, 6, 30, 4, 9, 7, 1, (4, 1), (3, 0), (1, 1)),     # tall kernel
+        (1, 8, 12, 12, 3, 3, 3, (5, 5), (0, 0), (1, 1)),    # stride larger than the kernel
+        (2, 4, 16, 16, 300, 3, 3, (1, 1), (1, 1), (3, 3)),  # K spans three tiles, dilation 3
+        (1, 136, 5, 5, 8, 3, 3, (1, 1), (1, 1), (1, 1)),    # long contraction, ragged K-tile tail
+    ]
+    for i, (N, C, H, W, K, R, S, st, pd, dl) in enumerate(cases):
+        for dt in ("f32", "f16", "bf16"):
+            x = (torch.rand(N, C, H, W, generator=g) * 2 - 1).to(TORCH_DT[dt])
+            w = (torch.randn(K, C, R, S, generator=g) / np.sqrt(C * R * S)).to(TORCH_DT[dt])
+            b = (torch.randn(K, generator=g) * 0.1).to(TORCH_DT[dt])
+            for algo in ("im2win", "im2col"):
+                _check_full(dev, _perm_x(x, lay), _perm_x(w, lay), b, lay, st, pd, dl, algo, dt,
+                            "edge %d %s %s %s" % (i, dt, lay, algo))
+
+
+# ---------------------------------------------------------------- the five workloads
+
+def _workload_check(dev, name, batch=None, points=4000, full_limit=3e9, algo="im2win"):
+    from cnn_convolution_lowering_amd.workloads import make_workload
+    wl = make_workload(name, batch)
+    spec = wl.spec
+    rng = np.random.default_rng(99)
+    x_prev = None
+    errs = []
+    for i, L in enumerate(wl.layers):
+        x = L.x.to(dev) if L.x is not None else x_prev
+        w = L.w.to(dev)
+        b = L.b.to(dev)
+        d = cl.descriptor(tuple(x.shape), tuple(w.shape), stride=L.stride, padding=L.padding,
+                          dilation=L.dilation, layout=spec.layout, dtype=spec.dtype, algo=algo)
+        _say("workload %s N=%d layer %d (%s) %s" % (name, spec.N, i, L.label, algo))
+        y = d.forward(x, w, b)
+        torch.cuda.synchronize()
+        xc, yc = x.cpu(), y.cpu()
+        macs = spec.N * L.K * d.P * d.Q * L.C * L.R * L.S
+        if macs <= full_limit:
+            ref, yabs = oracle.conv2d(xc, L.w, L.b, layout=spec.layout, stride=L.stride, padding=L.padding,
+                                      dilation=L.dilation, with_abs=True)
+            errs.append(assert_parity(to_f64(yc), ref, yabs, spec.dtype, "%s layer %d full" % (name, i)))
+        else:
+            pts = sample_points(spec.N, L.K, d.P, d.Q, points, rng)
+            ref, yabs = oracle.conv2d_points(xc, L.w, L.b, pts, layout=spec.layout, stride=L.stride,
+                                             padding=L.padding, dilation=L.dilation)
+            got = gather(to_nkpq(to_f64(yc), spec.layout), pts)
+            errs.append(assert_parity(got, ref, yabs, spec.dtype, "%s layer %d sampled" % (name, i)))
+        x_prev = y
+    return errs
+
+
+@pytest.mark.parametrize("algo", ["im2win", "im2col"])
+def test_workload_c1(dev, algo):
+    _workload_check(dev, "c1", algo=algo)
+
+
+@pytest.mark.parametrize("algo", ["im2win", "im2col"])
+def test_workload_c2_full_size(dev, algo):
+    _workload_check(dev, "c2", algo=algo, full_limit=2.5e9)
+
+
+def test_workload_c3_full_size(dev):
+    _workload_check(dev, "c3", full_limit=1e10)
+
+
+@pytest.mark.parametrize("algo", ["im2win", "im2col"])
+def test_workload_c4_full_size(dev, algo):
+    _workload_check(dev, "c4", algo=algo, full_limit=0)
+
+
+@pytest.mark.parametrize("algo", ["im2win", "im2col"])
+def test_workload_c5_full_size(dev, algo):
+    _workload_check(dev, "c5", algo=algo, full_limit=0, points=3000)
+
+
+@pytest.mark.parametrize("name,batch", [("c2", 6), ("c4", 1), ("c5", 1)])
+def test_workloads_reduced_batch_full_output(dev, name, batch):
+    _workload_check(dev, name, batch=batch, full_limit=1e12)
