@@ -65,10 +65,12 @@ struct Mfma<__bf16> {
 template <>
 struct Mfma<float> {
     static __device__ __forceinline__ f32x4 run(u32x4 a, u32x4 b, f32x4 c) {
+        // Reinterpret the whole vector, then index it: a bit-cast of one
+        // vector element (a[j]) was compiled to element 0 for every j.
+        const f32x4 af = __builtin_bit_cast(f32x4, a);
+        const f32x4 bf = __builtin_bit_cast(f32x4, b);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            c = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, a[j]), __builtin_bit_cast(float, b[j]),
-                                                     c, 0, 0, 0);
+        for (int j = 0; j < 4; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(af[j], bf[j], c, 0, 0, 0);
         return c;
     }
 };
@@ -227,8 +229,8 @@ __global__ void __launch_bounds__(256) igemm_kernel(GemmArgs g) {
                 T* dst = y + m * g.K + k;
                 if (k + 3 < g.K && (g.K & 3) == 0) {
                     if (sizeof(T) == 4) {
-                        store16(dst, u32x4{__builtin_bit_cast(uint32_t, v[0]), __builtin_bit_cast(uint32_t, v[1]),
-                                           __builtin_bit_cast(uint32_t, v[2]), __builtin_bit_cast(uint32_t, v[3])});
+                        store16(dst, u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]),
+                                           __float_as_uint(v[2]), __float_as_uint(v[3])});
                     } else {
                         union {
                             u32x2 u;

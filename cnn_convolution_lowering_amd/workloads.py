@@ -75,6 +75,12 @@ class LayerInputs:
     w: torch.Tensor
     b: torch.Tensor
 
+    def __getattr__(self, name):
+        # shape fields (C, K, R, S, stride, padding, dilation, label) come from the spec
+        if name != "spec" and "spec" in self.__dict__:
+            return getattr(self.spec, name)
+        raise AttributeError(name)
+
 
 @dataclass
 class Workload:
