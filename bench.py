@@ -207,6 +207,9 @@ def main(argv=None):
     ap.add_argument("--algo", default="im2win", choices=["im2win", "im2col"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of reference work to time")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB (5 times), to scale "
+                         "the HBM byte counters of a profiler against a transfer of known size")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -223,6 +226,15 @@ def main(argv=None):
         return 1
     cl.load_library()
     dev = torch.device("cuda:0")
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_launch": n, "launches": 5}))
+        return 0
     wl = make_workload(args.workload)
     spec = wl.spec
     print("bench: workload %s, algo %s, building inputs" % (spec.name, args.algo), file=sys.stderr, flush=True)
