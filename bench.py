@@ -204,7 +204,7 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c2", choices=sorted(WORKLOAD_TEXT))
-    ap.add_argument("--algo", default="im2win", choices=["im2win", "im2col"])
+    ap.add_argument("--algo", default="im2win", choices=["im2win", "im2col", "implicit"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of reference work to time")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,

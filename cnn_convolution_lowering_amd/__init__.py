@@ -25,7 +25,7 @@ STATUS = {0: "CONV_OK", -1: "CONV_ERR_INVALID_ARG", -2: "CONV_ERR_UNSUPPORTED", 
           -4: "CONV_ERR_NOT_DEVICE_PTR", -5: "CONV_ERR_MISALIGNED", -6: "CONV_ERR_HIP", -7: "CONV_ERR_OOM"}
 LAYOUTS = {"nchw": 0, "nhwc": 1}
 DTYPES = {"f32": 0, "f16": 1, "bf16": 2}
-ALGOS = {"im2win": 0, "im2col": 1}
+ALGOS = {"im2win": 0, "im2col": 1, "implicit": 2}
 
 
 class ConvError(RuntimeError):

@@ -37,7 +37,7 @@ struct conv_desc {
     conv_params_t p;
     int64_t P, Q, M, Kg, W_used, RCp, Kl;
     int32_t elem, vec;
-    bool elided;        // x read in place (1x1 NHWC, no padding)
+    bool elided;        // no lowering launch: the contraction reads x (implicit, or 1x1 NHWC unpadded)
     bool pack;          // filter needs packing into ws
     uint64_t off_filter, bytes_filter, off_low, bytes_low, ws_bytes;
     uint64_t im2win_bytes, im2col_bytes;
@@ -63,7 +63,8 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d) {
         return CONV_ERR_INVALID_ARG;
     if (p.layout != CONV_NCHW && p.layout != CONV_NHWC) return CONV_ERR_INVALID_ARG;
     if (p.dtype != CONV_F32 && p.dtype != CONV_F16 && p.dtype != CONV_BF16) return CONV_ERR_INVALID_ARG;
-    if (p.algo != CONV_ALGO_IM2WIN && p.algo != CONV_ALGO_IM2COL) return CONV_ERR_INVALID_ARG;
+    if (p.algo != CONV_ALGO_IM2WIN && p.algo != CONV_ALGO_IM2COL && p.algo != CONV_ALGO_IMPLICIT)
+        return CONV_ERR_INVALID_ARG;
     const int64_t lim = (int64_t(1) << 31) - 1;
     if (p.N > lim || p.C > lim || p.H > lim || p.W > lim || p.K > lim || p.R > lim || p.S > lim)
         return CONV_ERR_UNSUPPORTED;
@@ -85,12 +86,14 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d) {
 
     const bool nhwc = p.layout == CONV_NHWC;
     const bool c_vec = p.C % d.vec == 0;
-    d.elided = nhwc && p.R == 1 && p.S == 1 && p.pad_h == 0 && p.pad_w == 0 && c_vec;
-    // KRSC with R == 1 or S == 1 is already the (s, r, c) order when C fills whole vectors.
-    d.pack = !(nhwc && c_vec && (p.R == 1 || p.S == 1));
+    const bool implicit = p.algo == CONV_ALGO_IMPLICIT;
+    d.elided = implicit || (nhwc && p.R == 1 && p.S == 1 && p.pad_h == 0 && p.pad_w == 0 && c_vec);
+    // KRSC with R == 1 or S == 1 is already the (s, r, c) order when C fills whole vectors;
+    // the implicit contraction reads the filter in its own order.
+    d.pack = !implicit && !(nhwc && c_vec && (p.R == 1 || p.S == 1));
 
     // 32-bit index ranges used inside the kernels.
-    if (d.M > lim || d.Kl > lim || p.K * d.Kl > lim || d.P * d.Q > lim) return CONV_ERR_UNSUPPORTED;
+    if (d.M > lim || d.Kl > lim || p.K * d.Kl > lim || d.P * d.Q > lim || p.K * d.Kg > lim) return CONV_ERR_UNSUPPORTED;
     if (p.N * d.P > lim || d.W_used * d.RCp > lim) return CONV_ERR_UNSUPPORTED;
 
     const uint64_t e = uint64_t(d.elem);
@@ -239,15 +242,47 @@ void launch_lower(const conv_desc& d, const void* x, void* out, hipStream_t st) 
     }
 }
 
-template <typename T, int BM, int BN, int BK, int WGM, int WGN>
-void launch_gemm_tile(const conv_desc& d, GemmArgs g, hipStream_t st) {
+template <typename T, int BM, int BN, int BK, int WGM, int WGN, bool NHWC_OUT, class ALoad, class BLoad>
+void launch_core(const conv_desc& d, GemmArgs g, hipStream_t st) {
     g.tiles_n = int32_t((d.p.K + BN - 1) / BN);
     const uint64_t tiles_m = (uint64_t(d.M) + BM - 1) / BM;
     const uint32_t blocks = uint32_t(tiles_m * g.tiles_n);
-    if (d.p.layout == CONV_NHWC)
-        igemm_kernel<T, BM, BN, BK, WGM, WGN, true><<<blocks, 256, 0, st>>>(g);
-    else
-        igemm_kernel<T, BM, BN, BK, WGM, WGN, false><<<blocks, 256, 0, st>>>(g);
+    conv_gemm_kernel<T, BM, BN, BK, WGM, WGN, NHWC_OUT, ALoad, BLoad><<<blocks, 256, 0, st>>>(g);
+}
+
+// Pick the loaders for the descriptor and launch one tile shape.
+template <typename T, int BM, int BN, int BK, int WGM, int WGN>
+void launch_gemm_tile(const conv_desc& d, const GemmArgs& g, hipStream_t st) {
+    constexpr int VEC = Vec<T>::n;
+    using BRows = StridedRows<T, BN, BK, false, false>;
+    using BRowsElem = StridedRows<T, BN, BK, false, true>;
+    const bool nhwc = d.p.layout == CONV_NHWC;
+    if (d.p.algo != CONV_ALGO_IMPLICIT) {
+        // lowered buffer (im2win strips / im2col rows) or 1x1 NHWC input in place
+        const bool seg = !d.elided && d.p.algo == CONV_ALGO_IM2WIN;
+        if (seg) {
+            using A = StridedRows<T, BM, BK, true, false>;
+            if (nhwc) launch_core<T, BM, BN, BK, WGM, WGN, true, A, BRows>(d, g, st);
+            else launch_core<T, BM, BN, BK, WGM, WGN, false, A, BRows>(d, g, st);
+        } else {
+            using A = StridedRows<T, BM, BK, false, false>;
+            if (nhwc) launch_core<T, BM, BN, BK, WGM, WGN, true, A, BRows>(d, g, st);
+            else launch_core<T, BM, BN, BK, WGM, WGN, false, A, BRows>(d, g, st);
+        }
+        return;
+    }
+    const bool b_vec = d.Kg % VEC == 0;
+    if (nhwc && d.p.C % VEC == 0) {
+        launch_core<T, BM, BN, BK, WGM, WGN, true, WindowVecNHWC<T, BM, BK>, BRows>(d, g, st);
+    } else if (nhwc) {
+        using A = WindowElem<T, BM, BK, true>;
+        if (b_vec) launch_core<T, BM, BN, BK, WGM, WGN, true, A, BRows>(d, g, st);
+        else launch_core<T, BM, BN, BK, WGM, WGN, true, A, BRowsElem>(d, g, st);
+    } else {
+        using A = WindowElem<T, BM, BK, false>;
+        if (b_vec) launch_core<T, BM, BN, BK, WGM, WGN, false, A, BRows>(d, g, st);
+        else launch_core<T, BM, BN, BK, WGM, WGN, false, A, BRowsElem>(d, g, st);
+    }
 }
 
 template <typename T>
@@ -255,19 +290,35 @@ void launch_gemm(const conv_desc& d, const void* x, const void* w, const void* b
                  hipStream_t st) {
     constexpr int BK = sizeof(T) == 4 ? 16 : 32;
     const char* wsb = static_cast<const char*>(ws);
-    GemmArgs g;
+    GemmArgs g{};
     g.b = d.pack ? static_cast<const void*>(wsb + d.off_filter) : w;
     g.bias = bias;
     g.y = y;
     g.M = d.M;
     g.K = int32_t(d.p.K);
-    g.Kl = int32_t(d.Kl);
     g.PQ = int32_t(d.P * d.Q);
     g.Q = int32_t(d.Q);
-    g.ldb = int32_t(d.Kl);
-    if (d.elided) {
+    g.C = int32_t(d.p.C);
+    g.H = int32_t(d.p.H);
+    g.W = int32_t(d.p.W);
+    g.R = int32_t(d.p.R);
+    g.S = int32_t(d.p.S);
+    g.sh = d.p.stride_h;
+    g.sw = d.p.stride_w;
+    g.ph = d.p.pad_h;
+    g.pw = d.p.pad_w;
+    g.dh = d.p.dil_h;
+    g.dw = d.p.dil_w;
+    if (d.p.algo == CONV_ALGO_IMPLICIT) {
+        // windows gathered from x; filter rows in their own order
+        g.a = x;
+        g.Kc = int32_t(d.Kg);
+        g.ldb = int32_t(d.Kg);
+    } else if (d.elided) {
         // 1x1, no padding, NHWC: row (n, p, q) is x[n][p*sh][q*sw][0..C)
         g.a = x;
+        g.Kc = int32_t(d.Kl);
+        g.ldb = int32_t(d.Kl);
         g.sN = d.p.H * d.p.W * d.p.C;
         g.sP = int64_t(d.p.stride_h) * d.p.W * d.p.C;
         g.sQ = int64_t(d.p.stride_w) * d.p.C;
@@ -275,6 +326,8 @@ void launch_gemm(const conv_desc& d, const void* x, const void* w, const void* b
         g.sS = 0;
     } else if (d.p.algo == CONV_ALGO_IM2WIN) {
         g.a = wsb + d.off_low;
+        g.Kc = int32_t(d.Kl);
+        g.ldb = int32_t(d.Kl);
         g.sP = d.W_used * d.RCp;
         g.sN = d.P * g.sP;
         g.sQ = int64_t(d.p.stride_w) * d.RCp;
@@ -282,6 +335,8 @@ void launch_gemm(const conv_desc& d, const void* x, const void* w, const void* b
         g.sS = int32_t(int64_t(d.p.dil_w) * d.RCp);
     } else {
         g.a = wsb + d.off_low;
+        g.Kc = int32_t(d.Kl);
+        g.ldb = int32_t(d.Kl);
         g.sQ = d.Kl;
         g.sP = d.Q * d.Kl;
         g.sN = d.P * g.sP;

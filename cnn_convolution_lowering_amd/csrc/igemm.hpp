@@ -1,20 +1,27 @@
-// The contraction Y[M x K] = A[M x Kl] * Bp[K x Kl]^T on gfx950 MFMA, with
+// The contraction Y[M x K] = A[M x Kc] * B[K x Kc]^T on gfx950 MFMA, with
 // the bias add, rounding and NCHW / NHWC store fused into its epilogue.
 //
 // "GPU-Accelerating MSCRED with CUDA, im2col, GEMM, and a Custom PyTorch
 // Extension", section "Transforming Conv2D into im2col and GEMM": output
 // matrix = filter matrix x lowered input; section "Global Memory and Shared
 // Memory": reusable tiles are staged in on-chip memory and reused by the
-// threads of a block.  Here a 256-thread workgroup owns a BM x BN output tile;
-// its A (lowered input) and B (packed filter) tiles are staged through LDS in
-// two buffers, so the 16-byte global loads of tile k+1 are in flight while
-// the MFMAs consume tile k; LDS rows are padded by one 16-byte vector so the
-// fragment reads of 16 consecutive rows fall in distinct banks.
+// threads of a block.  A 256-thread workgroup owns a BM x BN output tile; its
+// A (input windows) and B (filter) tiles are staged through LDS in two
+// buffers, so the global loads of tile k+1 are in flight while the MFMAs
+// consume tile k.  LDS rows are padded by one 16-byte vector so the fragment
+// reads of 16 consecutive rows fall in distinct banks.
 //
-// A row m = (n, p, q) starts at n*sN + p*sP + q*sQ and its element kk sits at
-// (kk / RCp)*sS + kk % RCp past that, which covers the im2win strips
-// (sQ = sw*RCp, sS = dw*RCp), explicit im2col rows (sQ = Kl, one segment) and
-// a 1x1 NHWC input read in place (sQ = sw*C).
+// Where the A tile comes from is a loader policy:
+//  - StridedRows: rows of a lowered buffer -- im2win strips (a row (n,p,q)
+//    starts at n*sN + p*sP + q*sQ; element kk sits (kk / RCp)*sS + kk % RCp
+//    past it), explicit im2col rows, or a 1x1 NHWC input read in place;
+//  - WindowVecNHWC / WindowElem: the window of output pixel (n,p,q) gathered
+//    straight from x, zero outside the image, in the filter's natural
+//    contraction order ((r,s,c) for NHWC / KRSC, (c,r,s) for NCHW / KCRS), so
+//    no lowered buffer is written at all: the window tile exists only in LDS
+//    ("Enabling Memory-efficient Im2win Convolution with Multi-precision
+//    Support on GPU CUDA and Tensor Cores", abstract: asynchronous data
+//    movement, reduced memory).
 //
 // MFMA: v_mfma_f32_16x16x32_{f16,bf16} for 16-bit storage, four
 // v_mfma_f32_16x16x4_f32 per 16-deep step for fp32 (full fp32 products, no
@@ -29,18 +36,21 @@
 namespace convlower {
 
 struct GemmArgs {
-    const void* a;
-    const void* b;
+    const void* a;      // lowered buffer, or x for the window loaders
+    const void* b;      // filter rows [K][ldb]
     const void* bias;   // NULL: no bias
     void* y;
     int64_t M;          // output pixels N*P*Q
     int32_t K;          // output channels
-    int32_t Kl;         // lowered contraction length (multiple of VEC)
+    int32_t Kc;         // contraction length (lowered Kl, or C*R*S for the window loaders)
     int32_t PQ, Q;      // decode m -> (n, p, q)
-    int64_t sN, sP, sQ; // A row offset (elements)
-    int32_t RCp, sS;    // A column offset
-    int32_t ldb;        // Bp row pitch (elements)
+    int64_t sN, sP, sQ; // StridedRows: row offset (elements)
+    int32_t RCp, sS;    // StridedRows: column offset
+    int32_t ldb;        // filter row pitch (elements)
     int32_t tiles_n;    // ceil(K / BN)
+    // window loaders: the convolution itself
+    int32_t C, H, W, R, S;
+    int32_t sh, sw, ph, pw, dh, dw;
 };
 
 template <typename T>
@@ -75,22 +85,265 @@ struct Mfma<float> {
     }
 };
 
+// Output pixel m -> (n, p, q); M < 2^31 is checked on the host.
+__device__ __forceinline__ void decode_m(const GemmArgs& g, int32_t m, int32_t& n, int32_t& p, int32_t& q) {
+    n = m / g.PQ;
+    const int32_t pq = m - n * g.PQ;
+    p = pq / g.Q;
+    q = pq - p * g.Q;
+}
+
+// ---------------------------------------------------------------------------
+// Loaders.  Each holds NV 16-byte registers of the next tile: fetch() issues
+// the global loads for the current contraction position, next() moves it by
+// BK, put() writes the registers into an LDS tile [ROWS][LDK].
+
+// Rows of a strided matrix, 16-byte vectors along the contraction (k-fast
+// mapping: consecutive threads take consecutive vectors of a row).  Rows are
+// output pixels for the A side (PIXELS) or filter rows for the B side.  With
+// SEGMENTED the column offset is (kk / RCp)*sS + kk % RCp (im2win strips);
+// otherwise it is kk.  ELEM gathers a vector element by element, for row
+// pitches that are not whole vectors.
+template <typename T, int ROWS, int BK, bool SEGMENTED, bool ELEM>
+struct StridedRows {
+    static constexpr int VEC = Vec<T>::n;
+    static constexpr int KV = BK / VEC;
+    static constexpr int NV = (ROWS * KV + 255) / 256;
+    static_assert(256 % KV == 0, "tile depth");
+    u32x4 r[NV];
+    int64_t off[NV];
+    bool ok[NV];
+    int kv, kk, t;
+    int64_t seg;
+
+    template <bool PIXELS>
+    __device__ __forceinline__ void init(const GemmArgs& g, int64_t row0, int tid) {
+        kv = tid % KV;
+        kk = kv * VEC;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int v = tid + i * 256;
+            const int64_t row = row0 + v / KV;
+            if (PIXELS) {
+                ok[i] = (v < ROWS * KV) && (row < g.M);
+                int32_t n, p, q;
+                decode_m(g, ok[i] ? int32_t(row) : 0, n, p, q);
+                off[i] = int64_t(n) * g.sN + int64_t(p) * g.sP + int64_t(q) * g.sQ;
+            } else {
+                ok[i] = (v < ROWS * KV) && (row < g.K);
+                off[i] = (ok[i] ? row : 0) * int64_t(g.ldb);
+            }
+        }
+        if (SEGMENTED) {
+            t = kk % g.RCp;
+            seg = int64_t(kk / g.RCp) * g.sS;
+        } else {
+            t = kk;
+            seg = 0;
+        }
+    }
+    __device__ __forceinline__ void fetch(const GemmArgs& g, const T* __restrict__ base) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            if (!ELEM) {
+                r[i] = (ok[i] && kk < g.Kc) ? load16(base + off[i] + seg + t) : zero4();
+            } else {
+                Pack16<T> pk;
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) pk.e[e] = (ok[i] && kk + e < g.Kc) ? base[off[i] + seg + t + e] : T(0);
+                r[i] = pk.v;
+            }
+        }
+    }
+    __device__ __forceinline__ void next(const GemmArgs& g) {
+        kk += BK;
+        t += BK;
+        if (SEGMENTED) {
+            while (t >= g.RCp) {
+                t -= g.RCp;
+                seg += g.sS;
+            }
+        }
+    }
+    __device__ __forceinline__ void put(T* lds, int tid, int LDK) const {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int v = tid + i * 256;
+            if (v < ROWS * KV) store16(lds + (v / KV) * LDK + kv * VEC, r[i]);
+        }
+    }
+};
+
+// Window of each output pixel gathered from NHWC x, 16-byte vectors of
+// channels (C a whole number of vectors), contraction order (r, s, c).
+template <typename T, int ROWS, int BK>
+struct WindowVecNHWC {
+    static constexpr int VEC = Vec<T>::n;
+    static constexpr int KV = BK / VEC;
+    static constexpr int NV = (ROWS * KV + 255) / 256;
+    static_assert(256 % KV == 0, "tile depth");
+    u32x4 r[NV];
+    int64_t nbase[NV];
+    int32_t h0[NV], w0[NV];
+    bool ok[NV];
+    int kv, kk, c0, s, rr;
+
+    template <bool PIXELS>
+    __device__ __forceinline__ void init(const GemmArgs& g, int64_t row0, int tid) {
+        static_assert(PIXELS, "window loaders feed the pixel side");
+        kv = tid % KV;
+        kk = kv * VEC;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int v = tid + i * 256;
+            const int64_t m = row0 + v / KV;
+            ok[i] = (v < ROWS * KV) && (m < g.M);
+            int32_t n, p, q;
+            decode_m(g, ok[i] ? int32_t(m) : 0, n, p, q);
+            nbase[i] = int64_t(n) * g.H * g.W * g.C;
+            h0[i] = p * g.sh - g.ph;
+            w0[i] = q * g.sw - g.pw;
+        }
+        c0 = kk % g.C;
+        const int rs = kk / g.C;
+        s = rs % g.S;
+        rr = rs / g.S;
+    }
+    __device__ __forceinline__ void fetch(const GemmArgs& g, const T* __restrict__ x) {
+        const int dh = rr * g.dh, dw = s * g.dw;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int h = h0[i] + dh, w = w0[i] + dw;
+            const bool in = ok[i] && kk < g.Kc && unsigned(h) < unsigned(g.H) && unsigned(w) < unsigned(g.W);
+            r[i] = in ? load16(x + nbase[i] + (int64_t(h) * g.W + w) * g.C + c0) : zero4();
+        }
+    }
+    __device__ __forceinline__ void next(const GemmArgs& g) {
+        kk += BK;
+        c0 += BK;
+        while (c0 >= g.C) {
+            c0 -= g.C;
+            if (++s == g.S) {
+                s = 0;
+                ++rr;
+            }
+        }
+    }
+    __device__ __forceinline__ void put(T* lds, int tid, int LDK) const {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int v = tid + i * 256;
+            if (v < ROWS * KV) store16(lds + (v / KV) * LDK + kv * VEC, r[i]);
+        }
+    }
+};
+
+// Window of each output pixel gathered element by element (NCHW input, or
+// NHWC with C not a whole number of vectors).  Pixel-fast mapping: the
+// threads of a wave take consecutive output pixels, so for one contraction
+// element their loads walk along an input row; each thread takes EPT
+// consecutive contraction elements of its pixel.  Order (c, r, s) for NCHW,
+// (r, s, c) for NHWC -- the filter's own order.
+template <typename T, int ROWS, int BK, bool NHWC>
+struct WindowElem {
+    static constexpr int VEC = Vec<T>::n;
+    static constexpr int TPR = 256 / ROWS;        // threads per pixel row
+    static constexpr int EPT = BK / TPR;          // elements per thread
+    static constexpr int NV = EPT / VEC;
+    static_assert(256 % ROWS == 0 && BK % TPR == 0 && EPT % VEC == 0, "window tile shape");
+    u32x4 r[NV];
+    int64_t nbase;
+    int32_t h0, w0;
+    bool ok;
+    int row, kq, kk;       // kk: first contraction element of this thread
+    int c, rr, s;          // its decoded position
+
+    __device__ __forceinline__ void decode(const GemmArgs& g) {
+        if (NHWC) {
+            c = kk % g.C;
+            const int rs = kk / g.C;
+            s = rs % g.S;
+            rr = rs / g.S;
+        } else {
+            const int RS = g.R * g.S;
+            c = kk / RS;
+            const int rs = kk - c * RS;
+            rr = rs / g.S;
+            s = rs - rr * g.S;
+        }
+    }
+    template <bool PIXELS>
+    __device__ __forceinline__ void init(const GemmArgs& g, int64_t row0, int tid) {
+        static_assert(PIXELS, "window loaders feed the pixel side");
+        row = tid % ROWS;
+        kq = tid / ROWS;
+        const int64_t m = row0 + row;
+        ok = m < g.M;
+        int32_t n, p, q;
+        decode_m(g, ok ? int32_t(m) : 0, n, p, q);
+        nbase = int64_t(n) * g.C * g.H * g.W;
+        h0 = p * g.sh - g.ph;
+        w0 = q * g.sw - g.pw;
+        kk = kq * EPT;
+        decode(g);
+    }
+    __device__ __forceinline__ void fetch(const GemmArgs& g, const T* __restrict__ x) {
+        int cc = c, r2 = rr, s2 = s;
+        Pack16<T> pk[NV];
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+            const int h = h0 + r2 * g.dh, w = w0 + s2 * g.dw;
+            T val = T(0);
+            if (ok && kk + e < g.Kc && unsigned(h) < unsigned(g.H) && unsigned(w) < unsigned(g.W)) {
+                const int64_t o = NHWC ? (int64_t(h) * g.W + w) * g.C + cc : (int64_t(cc) * g.H + h) * g.W + w;
+                val = x[nbase + o];
+            }
+            pk[e / VEC].e[e % VEC] = val;
+            if (NHWC) {
+                if (++cc == g.C) {
+                    cc = 0;
+                    if (++s2 == g.S) {
+                        s2 = 0;
+                        ++r2;
+                    }
+                }
+            } else {
+                if (++s2 == g.S) {
+                    s2 = 0;
+                    if (++r2 == g.R) {
+                        r2 = 0;
+                        ++cc;
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < NV; ++j) r[j] = pk[j].v;
+    }
+    __device__ __forceinline__ void next(const GemmArgs& g) {
+        kk += BK;
+        decode(g);
+    }
+    __device__ __forceinline__ void put(T* lds, int, int LDK) const {
+#pragma unroll
+        for (int j = 0; j < NV; ++j) store16(lds + row * LDK + kq * EPT + j * VEC, r[j]);
+    }
+};
+
+// ---------------------------------------------------------------------------
 // BM x BN output tile, BK-deep LDS stages, WGM x WGN waves (4 in all).
 // NHWC_OUT: the MFMA is fed (filter, pixel) so a lane ends with 4 consecutive
 // output channels of one pixel (contiguous in NPQK); otherwise (pixel, filter)
 // so a lane ends with 4 consecutive pixels of one channel (contiguous in NKPQ).
-template <typename T, int BM, int BN, int BK, int WGM, int WGN, bool NHWC_OUT>
-__global__ void __launch_bounds__(256) igemm_kernel(GemmArgs g) {
+template <typename T, int BM, int BN, int BK, int WGM, int WGN, bool NHWC_OUT, class ALoad, class BLoad>
+__global__ void __launch_bounds__(256) conv_gemm_kernel(GemmArgs g) {
     constexpr int VEC = Vec<T>::n;
-    constexpr int KV = BK / VEC;      // 16-byte vectors per tile row
     constexpr int LDK = BK + VEC;     // LDS row pitch (elements), one vector of padding
     constexpr int WM = BM / WGM, WN = BN / WGN;
     constexpr int TM = WM / 16, TN = WN / 16;
     constexpr int KB = 4 * VEC;       // contraction depth of one fragment step
-    constexpr int A_LD = (BM * KV + 255) / 256;
-    constexpr int B_LD = (BN * KV + 255) / 256;
     static_assert(WGM * WGN == 4, "four waves per workgroup");
-    static_assert(BK % KB == 0 && 256 % KV == 0, "tile depth");
+    static_assert(BK % KB == 0, "tile depth");
     static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile");
 
     __shared__ __attribute__((aligned(16))) T sA[2][BM * LDK];
@@ -107,69 +360,10 @@ __global__ void __launch_bounds__(256) igemm_kernel(GemmArgs g) {
     const T* __restrict__ A = static_cast<const T*>(g.a);
     const T* __restrict__ B = static_cast<const T*>(g.b);
 
-    // Load slots: vector v = tid + i*256 of a tile is row v / KV, column
-    // (v % KV)*VEC; since 256 % KV == 0 the column is the same for every slot.
-    const int kv = tid % KV;
-    int64_t a_off[A_LD];
-    bool a_ok[A_LD];
-#pragma unroll
-    for (int i = 0; i < A_LD; ++i) {
-        const int v = tid + i * 256;
-        const int row = v / KV;
-        const int64_t m = m0 + row;
-        a_ok[i] = (v < BM * KV) && (m < g.M);
-        const int32_t mm = a_ok[i] ? int32_t(m) : 0;   // M < 2^31 (checked on the host)
-        const int32_t n = mm / g.PQ;
-        const int32_t pq = mm - n * g.PQ;
-        const int32_t p = pq / g.Q, q = pq - (pq / g.Q) * g.Q;
-        a_off[i] = int64_t(n) * g.sN + int64_t(p) * g.sP + int64_t(q) * g.sQ;
-    }
-    int64_t b_off[B_LD];
-    bool b_ok[B_LD];
-#pragma unroll
-    for (int i = 0; i < B_LD; ++i) {
-        const int v = tid + i * 256;
-        const int k = n0 + v / KV;
-        b_ok[i] = (v < BN * KV) && (k < g.K);
-        b_off[i] = int64_t(b_ok[i] ? k : 0) * g.ldb;
-    }
-
-    // Column state of this thread's vector: absolute lowered column kk, and
-    // its split into segment offset a_seg = (kk / RCp)*sS and remainder a_t.
-    int kk = kv * VEC;
-    int a_t = kk % g.RCp;
-    int64_t a_seg = int64_t(kk / g.RCp) * g.sS;
-
-    u32x4 ra[A_LD], rb[B_LD];
-    auto gload = [&]() {
-        const bool kin = kk < g.Kl;
-#pragma unroll
-        for (int i = 0; i < A_LD; ++i)
-            ra[i] = (a_ok[i] && kin) ? load16(A + a_off[i] + a_seg + a_t) : zero4();
-#pragma unroll
-        for (int i = 0; i < B_LD; ++i)
-            rb[i] = (b_ok[i] && kin) ? load16(B + b_off[i] + kk) : zero4();
-    };
-    auto advance = [&]() {
-        kk += BK;
-        a_t += BK;
-        while (a_t >= g.RCp) {
-            a_t -= g.RCp;
-            a_seg += g.sS;
-        }
-    };
-    auto sstore = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < A_LD; ++i) {
-            const int v = tid + i * 256;
-            if (v < BM * KV) store16(&sA[buf][(v / KV) * LDK + kv * VEC], ra[i]);
-        }
-#pragma unroll
-        for (int i = 0; i < B_LD; ++i) {
-            const int v = tid + i * 256;
-            if (v < BN * KV) store16(&sB[buf][(v / KV) * LDK + kv * VEC], rb[i]);
-        }
-    };
+    ALoad la;
+    BLoad lb;
+    la.template init<true>(g, m0, tid);
+    lb.template init<false>(g, n0, tid);
 
     f32x4 acc[TM][TN];
 #pragma unroll
@@ -177,9 +371,11 @@ __global__ void __launch_bounds__(256) igemm_kernel(GemmArgs g) {
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int nkt = (g.Kl + BK - 1) / BK;
-    gload();
-    sstore(0);
+    const int nkt = (g.Kc + BK - 1) / BK;
+    la.fetch(g, A);
+    lb.fetch(g, B);
+    la.put(sA[0], tid, LDK);
+    lb.put(sB[0], tid, LDK);
     __syncthreads();
 
     const int frag_row = lane & 15;
@@ -188,8 +384,10 @@ __global__ void __launch_bounds__(256) igemm_kernel(GemmArgs g) {
         const int cur = kt & 1;
         const bool more = kt + 1 < nkt;
         if (more) {
-            advance();
-            gload();
+            la.next(g);
+            lb.next(g);
+            la.fetch(g, A);
+            lb.fetch(g, B);
         }
 #pragma unroll
         for (int kb = 0; kb < BK / KB; ++kb) {
@@ -206,7 +404,10 @@ __global__ void __launch_bounds__(256) igemm_kernel(GemmArgs g) {
                 for (int j = 0; j < TN; ++j)
                     acc[i][j] = NHWC_OUT ? Mfma<T>::run(fb[j], fa[i], acc[i][j]) : Mfma<T>::run(fa[i], fb[j], acc[i][j]);
         }
-        if (more) sstore(cur ^ 1);
+        if (more) {
+            la.put(sA[cur ^ 1], tid, LDK);
+            lb.put(sB[cur ^ 1], tid, LDK);
+        }
         __syncthreads();
     }
 
@@ -229,8 +430,8 @@ __global__ void __launch_bounds__(256) igemm_kernel(GemmArgs g) {
                 T* dst = y + m * g.K + k;
                 if (k + 3 < g.K && (g.K & 3) == 0) {
                     if (sizeof(T) == 4) {
-                        store16(dst, u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]),
-                                           __float_as_uint(v[2]), __float_as_uint(v[3])});
+                        store16(dst, u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                                           __float_as_uint(v[3])});
                     } else {
                         union {
                             u32x2 u;

@@ -71,9 +71,15 @@ typedef enum { CONV_F32 = 0, CONV_F16 = 1, CONV_BF16 = 2 } conv_dtype_t;
  *  CONV_ALGO_IM2COL  explicit im2col: one materialised row per output pixel,
  *                    Col[(n,p,q)][s][r*C + c] (the baseline the im2win
  *                    workspace is compared against).
- * For 1x1 kernels on NHWC input with no padding, both algorithms read x in
+ *  CONV_ALGO_IMPLICIT the contraction gathers each output pixel's window
+ *                    straight from x into its LDS tile (zero outside the
+ *                    image), in the filter's own order -- (c, r, s) for KCRS,
+ *                    (r, s, c) for KRSC -- so neither a lowered buffer nor a
+ *                    packed filter is written: the workspace is 0 bytes and a
+ *                    call is one kernel launch.
+ * For 1x1 kernels on NHWC input with no padding, IM2WIN and IM2COL read x in
  * place and use no lowering workspace. */
-typedef enum { CONV_ALGO_IM2WIN = 0, CONV_ALGO_IM2COL = 1 } conv_algo_t;
+typedef enum { CONV_ALGO_IM2WIN = 0, CONV_ALGO_IM2COL = 1, CONV_ALGO_IMPLICIT = 2 } conv_algo_t;
 
 typedef struct {
     int64_t N, C, H, W;        /* input: batch, channels, height, width */
@@ -142,13 +148,14 @@ conv_status_t conv2d_fwd(conv_desc_t d, const void* x, const void* w, const void
                          void* ws, void* stream);
 
 /* Stage 1 of conv2d_fwd: reorder w into the packed contraction operand
- * Bp[k][s*RCp + r*C + c] in ws (zeros in the RCp padding).  A no-op when the
- * filter is already in that order (NHWC with R == 1 or S == 1 and C a
- * multiple of the 16-byte vector). */
+ * Bp[k][s*RCp + r*C + c] in ws (zeros in the RCp padding).  A no-op for
+ * CONV_ALGO_IMPLICIT and when the filter is already in that order (NHWC with
+ * R == 1 or S == 1 and C a multiple of the 16-byte vector). */
 conv_status_t conv_pack_filter(conv_desc_t d, const void* w, void* ws, void* stream);
 
 /* Stage 2: lower x into ws -- im2win strips or im2col rows, per the
- * descriptor's algorithm.  A no-op when the lowering is elided. */
+ * descriptor's algorithm.  A no-op when the lowering is elided and for
+ * CONV_ALGO_IMPLICIT. */
 conv_status_t conv_lower_input(conv_desc_t d, const void* x, void* ws, void* stream);
 
 /* Stage 3: the MFMA contraction over the lowered operand and packed filter

@@ -48,7 +48,7 @@ def test_struct_sizes_match_header():
 @pytest.mark.parametrize("field,value", [
     ("N", -1), ("C", 0), ("H", 0), ("W", -3), ("K", 0), ("R", 0), ("S", -1),
     ("stride_h", 0), ("stride_w", -1), ("dil_h", 0), ("dil_w", -2), ("pad_h", -1), ("pad_w", -1),
-    ("layout", 2), ("dtype", 3), ("algo", 7)])
+    ("layout", 2), ("dtype", 3), ("algo", 3)])
 def test_invalid_params(field, value):
     st, d = _create(**{field: value})
     assert st == -1 and not d.value
@@ -207,6 +207,16 @@ def test_workload_workspace_ratios():
             if spec.chained:
                 H, W = c.P, c.Q
         np.testing.assert_allclose(got, expect, rtol=1e-12, err_msg=name)
+
+
+@pytest.mark.parametrize("layout", ["nchw", "nhwc"])
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_implicit_needs_no_workspace(layout, dtype):
+    for (C, R, S, st, pd) in [(3, 7, 7, 2, 3), (32, 3, 3, 2, 0), (128, 1, 1, 1, 0), (5, 2, 3, 1, 1)]:
+        c = cl.Conv2d(4, C, 20, 20, 16, R, S, stride=st, padding=pd, layout=layout, dtype=dtype, algo="implicit")
+        assert c.workspace_bytes == 0
+        assert c.info["ws_filter_bytes"] == 0 and c.info["ws_lowered_bytes"] == 0
+        assert c.info["lowering_elided"] == 1
 
 
 def test_elided_layers_use_no_lowering_workspace():

@@ -66,8 +66,8 @@ def _fuzz_cases():
     rng = np.random.default_rng(2024)
     cases = []
     combos = [(dt, lay, algo) for dt in ("f32", "f16", "bf16") for lay in ("nchw", "nhwc")
-              for algo in ("im2win", "im2col")]
-    for i in range(72):
+              for algo in ("im2win", "im2col", "implicit")]
+    for i in range(90):
         dt, lay, algo = combos[i % len(combos)]
         R, S = int(rng.integers(1, 6)), int(rng.integers(1, 6))
         st = (int(rng.integers(1, 4)), int(rng.integers(1, 4)))
@@ -96,7 +96,7 @@ def test_fuzz_parity(dev, case):
 
 @pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("lay", ["nchw", "nhwc"])
-@pytest.mark.parametrize("algo", ["im2win", "im2col"])
+@pytest.mark.parametrize("algo", ["im2win", "im2col", "implicit"])
 def test_integer_inputs_bit_exact(dev, dt, lay, algo):
     """Integer x, w, b: fp32 accumulation is exact (|partial sums| < 2^24), so y
     must be the reference rounded once to the storage type (RNE), bit for bit."""
@@ -129,7 +129,7 @@ def test_delta_kernel_reproduces_input(dev, dt, lay):
         for k in range(C):
             w[k, k, R // 2, R // 2] = 1
         w = w.to(TORCH_DT[dt])
-        for algo in ("im2win", "im2col"):
+        for algo in ("im2win", "im2col", "implicit"):
             _say("delta R%d %s %s %s" % (R, dt, lay, algo))
             y = _run(dev, _perm_x(x, lay), _perm_x(w, lay), None, lay, 1, R // 2, 1, algo)
             assert torch.equal(y, _perm_x(x, lay)), (R, algo)
@@ -180,11 +180,12 @@ def test_lowered_layouts_exact(dev, dt, lay, shape):
 
 def test_deterministic_and_staged_equals_fused(dev):
     g = torch.Generator().manual_seed(10)
-    for dt, lay in (("f16", "nhwc"), ("f32", "nchw"), ("bf16", "nchw")):
+    for dt, lay, algo in (("f16", "nhwc", "im2win"), ("f32", "nchw", "im2win"), ("bf16", "nchw", "im2col"),
+                          ("f16", "nhwc", "implicit"), ("f32", "nchw", "implicit")):
         x = _perm_x((torch.rand(4, 32, 15, 15, generator=g) * 2 - 1).to(TORCH_DT[dt]), lay).to(dev)
         w = _perm_x(torch.randn(96, 32, 3, 3, generator=g).to(TORCH_DT[dt]), lay).to(dev)
         b = torch.randn(96, generator=g).to(TORCH_DT[dt]).to(dev)
-        d = cl.descriptor(tuple(x.shape), tuple(w.shape), padding=1, layout=lay, dtype=dt)
+        d = cl.descriptor(tuple(x.shape), tuple(w.shape), padding=1, layout=lay, dtype=dt, algo=algo)
         y1 = d.forward(x, w, b)
         y2 = d.forward(x, w, b)
         ws = d.new_workspace(dev)
@@ -240,7 +241,7 @@ def test_edge_shapes(dev, lay):
             x = (torch.rand(N, C, H, W, generator=g) * 2 - 1).to(TORCH_DT[dt])
             w = (torch.randn(K, C, R, S, generator=g) / np.sqrt(C * R * S)).to(TORCH_DT[dt])
             b = (torch.randn(K, generator=g) * 0.1).to(TORCH_DT[dt])
-            for algo in ("im2win", "im2col"):
+            for algo in ("im2win", "im2col", "implicit"):
                 _check_full(dev, _perm_x(x, lay), _perm_x(w, lay), b, lay, st, pd, dl, algo, dt,
                             "edge %d %s %s %s" % (i, dt, lay, algo))
 
@@ -279,30 +280,32 @@ def _workload_check(dev, name, batch=None, points=4000, full_limit=3e9, algo="im
     return errs
 
 
-@pytest.mark.parametrize("algo", ["im2win", "im2col"])
+@pytest.mark.parametrize("algo", ["im2win", "im2col", "implicit"])
 def test_workload_c1(dev, algo):
     _workload_check(dev, "c1", algo=algo)
 
 
-@pytest.mark.parametrize("algo", ["im2win", "im2col"])
+@pytest.mark.parametrize("algo", ["im2win", "im2col", "implicit"])
 def test_workload_c2_full_size(dev, algo):
     _workload_check(dev, "c2", algo=algo, full_limit=2.5e9)
 
 
-def test_workload_c3_full_size(dev):
-    _workload_check(dev, "c3", full_limit=1e10)
+@pytest.mark.parametrize("algo", ["im2win", "implicit"])
+def test_workload_c3_full_size(dev, algo):
+    _workload_check(dev, "c3", algo=algo, full_limit=1e10)
 
 
-@pytest.mark.parametrize("algo", ["im2win", "im2col"])
+@pytest.mark.parametrize("algo", ["im2win", "im2col", "implicit"])
 def test_workload_c4_full_size(dev, algo):
     _workload_check(dev, "c4", algo=algo, full_limit=0)
 
 
-@pytest.mark.parametrize("algo", ["im2win", "im2col"])
+@pytest.mark.parametrize("algo", ["im2win", "im2col", "implicit"])
 def test_workload_c5_full_size(dev, algo):
     _workload_check(dev, "c5", algo=algo, full_limit=0, points=3000)
 
 
 @pytest.mark.parametrize("name,batch", [("c2", 6), ("c4", 1), ("c5", 1)])
-def test_workloads_reduced_batch_full_output(dev, name, batch):
-    _workload_check(dev, name, batch=batch, full_limit=1e12)
+@pytest.mark.parametrize("algo", ["im2win", "implicit"])
+def test_workloads_reduced_batch_full_output(dev, name, batch, algo):
+    _workload_check(dev, name, batch=batch, full_limit=1e12, algo=algo)
