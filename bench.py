@@ -205,6 +205,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c2", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--algo", default="im2win", choices=["im2win", "im2col", "implicit"])
+    ap.add_argument("--layer", type=int, default=None,
+                    help="time only this layer of the workload (chained inputs are still computed once)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of reference work to time")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -240,6 +242,12 @@ def main(argv=None):
     print("bench: workload %s, algo %s, building inputs" % (spec.name, args.algo), file=sys.stderr, flush=True)
     layers, ws = build_layers(wl, dev, args.algo)
     stream = torch.cuda.current_stream(dev)
+    if args.layer is not None:
+        # inputs of a chained layer come from one pass of the layers before it
+        for l in layers[:args.layer]:
+            for st in STAGES:
+                run_stage(l, st, ws, stream)
+        layers = [layers[args.layer]]
     step_flops = sum(l["flops"] for l in layers)
 
     # Per-kernel durations (outside the timed region) pick the dominant kernel.

@@ -8,8 +8,9 @@
 // threads of a block.  A 256-thread workgroup owns a BM x BN output tile; its
 // A (input windows) and B (filter) tiles are staged through LDS in two
 // buffers, so the global loads of tile k+1 are in flight while the MFMAs
-// consume tile k.  LDS rows are padded by one 16-byte vector so the fragment
-// reads of 16 consecutive rows fall in distinct banks.
+// consume tile k.  LDS tiles are unpadded rows of BK elements whose 16-byte
+// chunks are XOR-swizzled by row (see swz_chunk), so that both the tile
+// writes and the MFMA fragment reads are free of bank conflicts.
 //
 // Where the A tile comes from is a loader policy:
 //  - StridedRows: rows of a lowered buffer -- im2win strips (a row (n,p,q)
@@ -93,10 +94,27 @@ __device__ __forceinline__ void decode_m(const GemmArgs& g, int32_t m, int32_t& 
     q = pq - p * g.Q;
 }
 
+// Position of 16-byte chunk `chunk` of LDS tile row `row` (CPR chunks per row).
+// Measured on gfx950: a ds_read_b128 is served 16 lanes per cycle over 64
+// four-byte banks, the lanes grouped by bits 3 and 5 of the lane id (lanes
+// 0-7 with 16-23, ...); a ds_write_b128 is served 8 consecutive lanes per
+// cycle over 32 banks.  A fragment read (lane l: row l%16, chunk l/16 of the
+// step) then puts rows r and r+4 (64-byte rows) or r and r+2 (128-byte rows)
+// on the same banks unless their chunks are moved apart; XOR-ing the chunk
+// index with ((row >> 1) & 3), scaled to keep chunk pairs together in
+// 128-byte rows, separates them, and keeps the row-major tile writes (8
+// lanes covering 128 contiguous bytes) conflict-free as well.
+template <int CPR>
+__device__ __forceinline__ int swz_chunk(int row, int chunk) {
+    static_assert(CPR == 4 || CPR == 8, "tile rows of 64 or 128 bytes");
+    return CPR == 4 ? (chunk ^ ((row >> 1) & 3)) : (chunk ^ (((row >> 1) & 3) << 1));
+}
+
 // ---------------------------------------------------------------------------
 // Loaders.  Each holds NV 16-byte registers of the next tile: fetch() issues
 // the global loads for the current contraction position, next() moves it by
-// BK, put() writes the registers into an LDS tile [ROWS][LDK].
+// BK, put() writes the registers into an LDS tile of ROWS rows of BK elements
+// (chunks placed by swz_chunk).
 
 // Rows of a strided matrix, 16-byte vectors along the contraction (k-fast
 // mapping: consecutive threads take consecutive vectors of a row).  Rows are
@@ -165,11 +183,12 @@ struct StridedRows {
             }
         }
     }
-    __device__ __forceinline__ void put(T* lds, int tid, int LDK) const {
+    __device__ __forceinline__ void put(T* lds, int tid) const {
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
             const int v = tid + i * 256;
-            if (v < ROWS * KV) store16(lds + (v / KV) * LDK + kv * VEC, r[i]);
+            const int row = v / KV;
+            if (v < ROWS * KV) store16(lds + row * BK + swz_chunk<KV>(row, kv) * VEC, r[i]);
         }
     }
 };
@@ -229,11 +248,12 @@ struct WindowVecNHWC {
             }
         }
     }
-    __device__ __forceinline__ void put(T* lds, int tid, int LDK) const {
+    __device__ __forceinline__ void put(T* lds, int tid) const {
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
             const int v = tid + i * 256;
-            if (v < ROWS * KV) store16(lds + (v / KV) * LDK + kv * VEC, r[i]);
+            const int row = v / KV;
+            if (v < ROWS * KV) store16(lds + row * BK + swz_chunk<KV>(row, kv) * VEC, r[i]);
         }
     }
 };
@@ -324,9 +344,9 @@ struct WindowElem {
         kk += BK;
         decode(g);
     }
-    __device__ __forceinline__ void put(T* lds, int, int LDK) const {
+    __device__ __forceinline__ void put(T* lds, int) const {
 #pragma unroll
-        for (int j = 0; j < NV; ++j) store16(lds + row * LDK + kq * EPT + j * VEC, r[j]);
+        for (int j = 0; j < NV; ++j) store16(lds + row * BK + swz_chunk<BK / VEC>(row, kq * NV + j) * VEC, r[j]);
     }
 };
 
@@ -338,7 +358,7 @@ struct WindowElem {
 template <typename T, int BM, int BN, int BK, int WGM, int WGN, bool NHWC_OUT, class ALoad, class BLoad>
 __global__ void __launch_bounds__(256) conv_gemm_kernel(GemmArgs g) {
     constexpr int VEC = Vec<T>::n;
-    constexpr int LDK = BK + VEC;     // LDS row pitch (elements), one vector of padding
+    constexpr int CPR = BK / VEC;     // 16-byte chunks per LDS tile row
     constexpr int WM = BM / WGM, WN = BN / WGN;
     constexpr int TM = WM / 16, TN = WN / 16;
     constexpr int KB = 4 * VEC;       // contraction depth of one fragment step
@@ -346,8 +366,8 @@ __global__ void __launch_bounds__(256) conv_gemm_kernel(GemmArgs g) {
     static_assert(BK % KB == 0, "tile depth");
     static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile");
 
-    __shared__ __attribute__((aligned(16))) T sA[2][BM * LDK];
-    __shared__ __attribute__((aligned(16))) T sB[2][BN * LDK];
+    __shared__ __attribute__((aligned(16))) T sA[2][BM * BK];
+    __shared__ __attribute__((aligned(16))) T sB[2][BN * BK];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -374,12 +394,12 @@ __global__ void __launch_bounds__(256) conv_gemm_kernel(GemmArgs g) {
     const int nkt = (g.Kc + BK - 1) / BK;
     la.fetch(g, A);
     lb.fetch(g, B);
-    la.put(sA[0], tid, LDK);
-    lb.put(sB[0], tid, LDK);
+    la.put(sA[0], tid);
+    lb.put(sB[0], tid);
     __syncthreads();
 
     const int frag_row = lane & 15;
-    const int frag_k = (lane >> 4) * VEC;
+    const int frag_chunk = lane >> 4;
     for (int kt = 0; kt < nkt; ++kt) {
         const int cur = kt & 1;
         const bool more = kt + 1 < nkt;
@@ -393,11 +413,15 @@ __global__ void __launch_bounds__(256) conv_gemm_kernel(GemmArgs g) {
         for (int kb = 0; kb < BK / KB; ++kb) {
             u32x4 fa[TM], fb[TN];
 #pragma unroll
-            for (int i = 0; i < TM; ++i)
-                fa[i] = load16(&sA[cur][(wm * WM + i * 16 + frag_row) * LDK + kb * KB + frag_k]);
+            for (int i = 0; i < TM; ++i) {
+                const int row = wm * WM + i * 16 + frag_row;
+                fa[i] = load16(&sA[cur][row * BK + swz_chunk<CPR>(row, kb * 4 + frag_chunk) * VEC]);
+            }
 #pragma unroll
-            for (int j = 0; j < TN; ++j)
-                fb[j] = load16(&sB[cur][(wn * WN + j * 16 + frag_row) * LDK + kb * KB + frag_k]);
+            for (int j = 0; j < TN; ++j) {
+                const int row = wn * WN + j * 16 + frag_row;
+                fb[j] = load16(&sB[cur][row * BK + swz_chunk<CPR>(row, kb * 4 + frag_chunk) * VEC]);
+            }
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -405,8 +429,8 @@ __global__ void __launch_bounds__(256) conv_gemm_kernel(GemmArgs g) {
                     acc[i][j] = NHWC_OUT ? Mfma<T>::run(fb[j], fa[i], acc[i][j]) : Mfma<T>::run(fa[i], fb[j], acc[i][j]);
         }
         if (more) {
-            la.put(sA[cur ^ 1], tid, LDK);
-            lb.put(sB[cur ^ 1], tid, LDK);
+            la.put(sA[cur ^ 1], tid);
+            lb.put(sB[cur ^ 1], tid);
         }
         __syncthreads();
     }
@@ -458,6 +482,27 @@ __global__ void __launch_bounds__(256) conv_gemm_kernel(GemmArgs g) {
 #pragma unroll
             for (int i = 0; i < TM; ++i) {
                 const int64_t mb = m0 + wm * WM + i * 16 + 4 * (lane >> 4);
+                if (mb >= g.M) continue;
+                if ((g.PQ & 3) == 0) {
+                    // mb % 4 == 0 and PQ % 4 == 0: the 4 pixels are in one image and
+                    // contiguous in NKPQ, so one 16-byte (fp32) or 8-byte store
+                    const int32_t n = int32_t(mb) / g.PQ;
+                    const int32_t pq = int32_t(mb) - n * g.PQ;
+                    T* dst = y + (int64_t(n) * g.K + k) * g.PQ + pq;
+                    if (sizeof(T) == 4) {
+                        store16(dst, u32x4{__float_as_uint(acc[i][j][0] + bk), __float_as_uint(acc[i][j][1] + bk),
+                                           __float_as_uint(acc[i][j][2] + bk), __float_as_uint(acc[i][j][3] + bk)});
+                    } else {
+                        union {
+                            u32x2 u;
+                            T e[4];
+                        } pk;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) pk.e[e] = from_f32<T>(acc[i][j][e] + bk);
+                        *reinterpret_cast<u32x2*>(dst) = pk.u;
+                    }
+                    continue;
+                }
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int64_t m = mb + e;
