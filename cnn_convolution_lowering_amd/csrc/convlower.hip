@@ -14,6 +14,7 @@
 
 #include "../../include/convlower.h"
 #include "igemm.hpp"
+#include "igemm_dma.hpp"
 #include "lowering.hpp"
 
 using namespace convlower;
@@ -28,6 +29,7 @@ enum TileId : int32_t {
     TILE_128x128 = 0,
     TILE_128x64 = 1,
     TILE_128x32 = 2,
+    TILE_256x128 = 3,   // pipelined (LDS-DMA) kernel only
 };
 
 }  // namespace
@@ -42,6 +44,7 @@ struct conv_desc {
     uint64_t off_filter, bytes_filter, off_low, bytes_low, ws_bytes;
     uint64_t im2win_bytes, im2col_bytes;
     int32_t tile;       // TileId
+    bool dma;           // pipelined LDS-DMA contraction kernel
     int32_t tile_m, tile_n, tile_k;
     // NCHW staging (0 = use the element-wise kernel)
     int32_t stage_chunk, stage_ld;
@@ -111,9 +114,19 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d) {
     d.ws_bytes = d.bytes_low ? d.off_low + d.bytes_low : d.bytes_filter;
     if (p.N == 0) d.ws_bytes = 0;
 
-    // Contraction tile: BN covers the output channels up to 128; BM = 128.
+    // Contraction kernel.  The pipelined kernel takes every A side made of
+    // whole 16-byte chunks (NHWC windows with C a multiple of the vector, or
+    // lowered / in-place rows) while its operand buffers fit 32-bit offsets.
+    const uint64_t x_bytes = uint64_t(p.N) * p.C * p.H * p.W * e;
+    const uint64_t a_bytes = d.elided ? x_bytes : d.bytes_low;
+    const uint64_t b_bytes = uint64_t(p.K) * (implicit ? d.Kg : d.Kl) * e;
+    const bool a_chunks = implicit ? (nhwc && c_vec) : true;
+    d.dma = a_chunks && a_bytes < (uint64_t(1) << 31) && b_bytes < (uint64_t(1) << 31);
+    // Tile: BN covers the output channels up to 128; BM = 256 where that still
+    // gives two workgroups per CU, else 128.
     d.tile = p.K <= 32 ? TILE_128x32 : (p.K <= 64 ? TILE_128x64 : TILE_128x128);
-    d.tile_m = 128;
+    if (d.dma && d.tile == TILE_128x128 && (d.M / 256) * ((p.K + 127) / 128) >= 512) d.tile = TILE_256x128;
+    d.tile_m = d.tile == TILE_256x128 ? 256 : 128;
     d.tile_n = d.tile == TILE_128x32 ? 32 : (d.tile == TILE_128x64 ? 64 : 128);
     d.tile_k = p.dtype == CONV_F32 ? 16 : 32;
 
@@ -285,6 +298,32 @@ void launch_gemm_tile(const conv_desc& d, const GemmArgs& g, hipStream_t st) {
     }
 }
 
+template <typename T, int BM, int BN, int BK, int WGM, int WGN, int STAGES, bool NHWC_OUT, class ASrc, class BSrc>
+void launch_dma_core(const conv_desc& d, GemmArgs g, hipStream_t st) {
+    g.tiles_n = int32_t((d.p.K + BN - 1) / BN);
+    const uint64_t tiles_m = (uint64_t(d.M) + BM - 1) / BM;
+    const uint32_t blocks = uint32_t(tiles_m * g.tiles_n);
+    conv_gemm_dma_kernel<T, BM, BN, BK, WGM, WGN, STAGES, NHWC_OUT, ASrc, BSrc><<<blocks, 256, 0, st>>>(g);
+}
+
+template <typename T, int BM, int BN, int BK, int WGM, int WGN, int STAGES>
+void launch_dma_tile(const conv_desc& d, const GemmArgs& g, hipStream_t st) {
+    using B = DmaRows<T, BN, BK, false, false>;
+    const bool nhwc = d.p.layout == CONV_NHWC;
+    if (d.p.algo == CONV_ALGO_IMPLICIT) {
+        // NHWC with C a whole number of vectors (checked when planning)
+        launch_dma_core<T, BM, BN, BK, WGM, WGN, STAGES, true, DmaWindowNHWC<T, BM, BK>, B>(d, g, st);
+    } else if (!d.elided && d.p.algo == CONV_ALGO_IM2WIN) {
+        using A = DmaRows<T, BM, BK, true, true>;
+        if (nhwc) launch_dma_core<T, BM, BN, BK, WGM, WGN, STAGES, true, A, B>(d, g, st);
+        else launch_dma_core<T, BM, BN, BK, WGM, WGN, STAGES, false, A, B>(d, g, st);
+    } else {
+        using A = DmaRows<T, BM, BK, true, false>;
+        if (nhwc) launch_dma_core<T, BM, BN, BK, WGM, WGN, STAGES, true, A, B>(d, g, st);
+        else launch_dma_core<T, BM, BN, BK, WGM, WGN, STAGES, false, A, B>(d, g, st);
+    }
+}
+
 template <typename T>
 void launch_gemm(const conv_desc& d, const void* x, const void* w, const void* bias, void* y, const void* ws,
                  hipStream_t st) {
@@ -342,6 +381,15 @@ void launch_gemm(const conv_desc& d, const void* x, const void* w, const void* b
         g.sN = d.P * g.sP;
         g.RCp = int32_t(d.Kl);
         g.sS = 0;
+    }
+    if (d.dma) {
+        switch (d.tile) {
+            case TILE_256x128: launch_dma_tile<T, 256, 128, BK, 2, 2, 3>(d, g, st); break;
+            case TILE_128x128: launch_dma_tile<T, 128, 128, BK, 2, 2, 4>(d, g, st); break;
+            case TILE_128x64: launch_dma_tile<T, 128, 64, BK, 2, 2, 4>(d, g, st); break;
+            default: launch_dma_tile<T, 128, 32, BK, 4, 1, 4>(d, g, st); break;
+        }
+        return;
     }
     switch (d.tile) {
         case TILE_128x128: launch_gemm_tile<T, 128, 128, BK, 2, 2>(d, g, st); break;

@@ -350,6 +350,104 @@ struct WindowElem {
     }
 };
 
+// Epilogue shared by the contraction kernels: y = round(acc + bias[k]),
+// stored in NPQK (NHWC_OUT) or NKPQ order.
+template <typename T, int BM, int BN, int WM, int WN, int TM, int TN, bool NHWC_OUT>
+__device__ __forceinline__ void store_tile(const GemmArgs& g, const f32x4 (&acc)[TM][TN], int64_t m0, int n0, int wm,
+                                           int wn, int lane) {
+    const T* __restrict__ bias = static_cast<const T*>(g.bias);
+    T* __restrict__ y = static_cast<T*>(g.y);
+    if (NHWC_OUT) {
+        // acc[i][j][e]: channel n0 + wn*WN + j*16 + 4*(lane>>4) + e, pixel m0 + wm*WM + i*16 + (lane&15)
+        float bv[TN][4];   // this lane's bias values, loaded once
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int k = n0 + wn * WN + j * 16 + 4 * (lane >> 4) + e;
+                bv[j][e] = (bias && k < g.K) ? to_f32(bias[k]) : 0.f;
+            }
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int64_t m = m0 + wm * WM + i * 16 + (lane & 15);
+            if (m >= g.M) continue;
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int k = n0 + wn * WN + j * 16 + 4 * (lane >> 4);
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = acc[i][j][e] + bv[j][e];
+                T* dst = y + m * g.K + k;
+                if (k + 3 < g.K && (g.K & 3) == 0) {
+                    if (sizeof(T) == 4) {
+                        store16(dst, u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                                           __float_as_uint(v[3])});
+                    } else {
+                        union {
+                            u32x2 u;
+                            T e[4];
+                        } pk;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) pk.e[e] = from_f32<T>(v[e]);
+                        *reinterpret_cast<u32x2*>(dst) = pk.u;
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (k + e < g.K) dst[e] = from_f32<T>(v[e]);
+                }
+            }
+        }
+    } else {
+        // acc[i][j][e]: pixel m0 + wm*WM + i*16 + 4*(lane>>4) + e, channel n0 + wn*WN + j*16 + (lane&15)
+        float bv[TN];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int k = n0 + wn * WN + j * 16 + (lane & 15);
+            bv[j] = (bias && k < g.K) ? to_f32(bias[k]) : 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int k = n0 + wn * WN + j * 16 + (lane & 15);
+            if (k >= g.K) continue;
+            const float bk = bv[j];
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                const int64_t mb = m0 + wm * WM + i * 16 + 4 * (lane >> 4);
+                if (mb >= g.M) continue;
+                if ((g.PQ & 3) == 0) {
+                    // mb % 4 == 0 and PQ % 4 == 0: the 4 pixels are in one image and
+                    // contiguous in NKPQ, so one 16-byte (fp32) or 8-byte store
+                    const int32_t n = int32_t(mb) / g.PQ;
+                    const int32_t pq = int32_t(mb) - n * g.PQ;
+                    T* dst = y + (int64_t(n) * g.K + k) * g.PQ + pq;
+                    if (sizeof(T) == 4) {
+                        store16(dst, u32x4{__float_as_uint(acc[i][j][0] + bk), __float_as_uint(acc[i][j][1] + bk),
+                                           __float_as_uint(acc[i][j][2] + bk), __float_as_uint(acc[i][j][3] + bk)});
+                    } else {
+                        union {
+                            u32x2 u;
+                            T e[4];
+                        } pk;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) pk.e[e] = from_f32<T>(acc[i][j][e] + bk);
+                        *reinterpret_cast<u32x2*>(dst) = pk.u;
+                    }
+                    continue;
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int64_t m = mb + e;
+                    if (m >= g.M) break;
+                    const int32_t n = int32_t(m) / g.PQ;
+                    const int32_t pq = int32_t(m) - n * g.PQ;
+                    y[(int64_t(n) * g.K + k) * g.PQ + pq] = from_f32<T>(acc[i][j][e] + bk);
+                }
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // BM x BN output tile, BK-deep LDS stages, WGM x WGN waves (4 in all).
 // NHWC_OUT: the MFMA is fed (filter, pixel) so a lane ends with 4 consecutive
@@ -435,85 +533,7 @@ __global__ void __launch_bounds__(256) conv_gemm_kernel(GemmArgs g) {
         __syncthreads();
     }
 
-    // Epilogue: y = round(acc + bias[k]).
-    const T* __restrict__ bias = static_cast<const T*>(g.bias);
-    T* __restrict__ y = static_cast<T*>(g.y);
-    if (NHWC_OUT) {
-        // acc[i][j][e]: channel n0 + wn*WN + j*16 + 4*(lane>>4) + e, pixel m0 + wm*WM + i*16 + (lane&15)
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            const int64_t m = m0 + wm * WM + i * 16 + (lane & 15);
-            if (m >= g.M) continue;
-#pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                const int k = n0 + wn * WN + j * 16 + 4 * (lane >> 4);
-                float v[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    v[e] = acc[i][j][e] + ((bias && k + e < g.K) ? to_f32(bias[k + e]) : 0.f);
-                T* dst = y + m * g.K + k;
-                if (k + 3 < g.K && (g.K & 3) == 0) {
-                    if (sizeof(T) == 4) {
-                        store16(dst, u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
-                                           __float_as_uint(v[3])});
-                    } else {
-                        union {
-                            u32x2 u;
-                            T e[4];
-                        } pk;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) pk.e[e] = from_f32<T>(v[e]);
-                        *reinterpret_cast<u32x2*>(dst) = pk.u;
-                    }
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (k + e < g.K) dst[e] = from_f32<T>(v[e]);
-                }
-            }
-        }
-    } else {
-        // acc[i][j][e]: pixel m0 + wm*WM + i*16 + 4*(lane>>4) + e, channel n0 + wn*WN + j*16 + (lane&15)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int k = n0 + wn * WN + j * 16 + (lane & 15);
-            if (k >= g.K) continue;
-            const float bk = bias ? to_f32(bias[k]) : 0.f;
-#pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                const int64_t mb = m0 + wm * WM + i * 16 + 4 * (lane >> 4);
-                if (mb >= g.M) continue;
-                if ((g.PQ & 3) == 0) {
-                    // mb % 4 == 0 and PQ % 4 == 0: the 4 pixels are in one image and
-                    // contiguous in NKPQ, so one 16-byte (fp32) or 8-byte store
-                    const int32_t n = int32_t(mb) / g.PQ;
-                    const int32_t pq = int32_t(mb) - n * g.PQ;
-                    T* dst = y + (int64_t(n) * g.K + k) * g.PQ + pq;
-                    if (sizeof(T) == 4) {
-                        store16(dst, u32x4{__float_as_uint(acc[i][j][0] + bk), __float_as_uint(acc[i][j][1] + bk),
-                                           __float_as_uint(acc[i][j][2] + bk), __float_as_uint(acc[i][j][3] + bk)});
-                    } else {
-                        union {
-                            u32x2 u;
-                            T e[4];
-                        } pk;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) pk.e[e] = from_f32<T>(acc[i][j][e] + bk);
-                        *reinterpret_cast<u32x2*>(dst) = pk.u;
-                    }
-                    continue;
-                }
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int64_t m = mb + e;
-                    if (m >= g.M) break;
-                    const int32_t n = int32_t(m) / g.PQ;
-                    const int32_t pq = int32_t(m) - n * g.PQ;
-                    y[(int64_t(n) * g.K + k) * g.PQ + pq] = from_f32<T>(acc[i][j][e] + bk);
-                }
-            }
-        }
-    }
+    store_tile<T, BM, BN, WM, WN, TM, TN, NHWC_OUT>(g, acc, m0, n0, wm, wn, lane);
 }
 
 }  // namespace convlower

@@ -1,0 +1,310 @@
+// Pipelined contraction: the same Y = A * B^T with fused bias epilogue as
+// conv_gemm_kernel, but the A and B tiles are copied from global memory
+// straight into LDS by buffer loads (buffer_load_dwordx4 ... lds), several
+// tiles ahead of the MFMAs, in a ring of STAGES LDS stages.
+//
+// "Enabling Memory-efficient Im2win Convolution with Multi-precision Support
+// on GPU CUDA and Tensor Cores" (abstract) names asynchronous data movement
+// as one of its optimisations; on gfx950 the asynchronous path is the LDS-DMA
+// form of the buffer load: a wave's 64 lanes each move 16 bytes into 1 KiB of
+// LDS at M0 + 16*lane without passing through registers, and a lane whose
+// offset lies outside the buffer writes zeros -- which is how the window
+// loader produces the convolution's zero padding.
+//
+// The loads are issued from inline assembly so the compiler does not track
+// them (its own tracking would wait for every outstanding LDS-DMA load before
+// each LDS read); the kernel waits for them itself with s_waitcnt vmcnt and
+// orders them with s_barrier:
+//   iteration kt:  wait until tile kt has landed (the tiles after it may
+//                  still be in flight) -> barrier (every wave's part of tile kt
+//                  is visible, and every wave has finished reading the stage
+//                  of tile kt-1) -> issue tile kt+STAGES-1 into that stage ->
+//                  MFMAs on tile kt.
+//
+// LDS tiles use the same row swizzle as conv_gemm_kernel (swz_chunk).  Since a
+// DMA writes LDS in lane order, the swizzle is applied on the global side:
+// the lane that fills LDS chunk slot `slot` of row `row` loads global chunk
+// swz_chunk(row, slot) (the XOR is its own inverse); for the tile shapes used
+// that chunk is the same for all of a thread's loads.
+#pragma once
+
+#include "device_common.hpp"
+#include "igemm.hpp"
+
+namespace convlower {
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource for raw (unformatted) 32-bit-offset access to [base, base+bytes).
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    i32x4 r;
+    r[0] = int32_t(uint32_t(a));
+    r[1] = int32_t(uint32_t(a >> 32) & 0xffff);   // stride 0
+    r[2] = int32_t(bytes);                          // num_records: offsets >= bytes read as 0
+    r[3] = 0x00020000;                              // raw buffer, 32-bit data
+    return r;
+}
+
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+    return uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)p));
+}
+
+constexpr uint32_t kOutOfRange = 0x80000000u;   // any offset >= num_records (< 2^31) reads as zero
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// 16 bytes from rsrc+voffset into LDS at m0 + 16*lane (m0 wave-uniform).
+__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voffset, uint32_t m0) {
+    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(voffset), "s"(rsrc), "s"(m0)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" : : : "memory"); }
+
+// Swizzle mask of a thread's rows: for CPR chunks per row, thread t fills
+// rows j*(256/CPR) + t/CPR, whose swizzle depends on t/CPR only.
+template <int CPR>
+__device__ __forceinline__ int dma_chunk(int tid) {
+    return swz_chunk<CPR>(tid / CPR, tid % CPR);
+}
+
+// ---------------------------------------------------------------------------
+// DMA sources.  init() fixes the thread's rows and its chunk, voff(j) is the
+// byte offset of the thread's j-th 16-byte load of the current tile (or
+// kOutOfRange), next() moves the contraction position by BK.
+
+// Window of each output pixel gathered from NHWC x (C a multiple of VEC),
+// contraction order (r, s, c).  Offsets are relative to the first image of
+// the tile, so only that image range needs 32-bit offsets.
+template <typename T, int ROWS, int BK>
+struct DmaWindowNHWC {
+    static constexpr int VEC = Vec<T>::n;
+    static constexpr int CPR = BK / VEC;
+    static constexpr int NL = ROWS * CPR / 256;     // loads per thread per tile
+    static constexpr int RSTEP = 256 / CPR;         // row distance between a thread's loads
+    static_assert(ROWS * CPR % 256 == 0, "whole wave loads");
+    uint32_t nbase[NL];   // byte offset of the row's image
+    int32_t h0[NL], w0[NL];
+    bool ok[NL];
+    int kk, c0, s, rr;
+    i32x4 rsrc;
+
+    __device__ __forceinline__ void init(const GemmArgs& g, int64_t row0, int tid) {
+        int32_t n_first, p_, q_;
+        decode_m(g, int32_t(row0 < g.M ? row0 : g.M - 1), n_first, p_, q_);
+        const int64_t img = int64_t(g.H) * g.W * g.C;
+        const T* base = static_cast<const T*>(g.a) + int64_t(n_first) * img;
+        const int64_t n_imgs = g.M / g.PQ;
+        rsrc = make_rsrc(base, uint32_t((n_imgs - n_first) * img * int64_t(sizeof(T)) < int64_t(0x7fffffff)
+                                            ? (n_imgs - n_first) * img * int64_t(sizeof(T))
+                                            : int64_t(0x7fffffff)));
+#pragma unroll
+        for (int j = 0; j < NL; ++j) {
+            const int64_t m = row0 + j * RSTEP + tid / CPR;
+            ok[j] = m < g.M;
+            int32_t n, p, q;
+            decode_m(g, ok[j] ? int32_t(m) : 0, n, p, q);
+            nbase[j] = uint32_t((n - n_first) * img * int64_t(sizeof(T)));
+            h0[j] = p * g.sh - g.ph;
+            w0[j] = q * g.sw - g.pw;
+        }
+        kk = dma_chunk<CPR>(tid) * VEC;
+        c0 = kk % g.C;
+        const int rs = kk / g.C;
+        s = rs % g.S;
+        rr = rs / g.S;
+    }
+    __device__ __forceinline__ uint32_t voff(const GemmArgs& g, int j) const {
+        const int h = h0[j] + rr * g.dh, w = w0[j] + s * g.dw;
+        const bool in = ok[j] && kk < g.Kc && unsigned(h) < unsigned(g.H) && unsigned(w) < unsigned(g.W);
+        return in ? nbase[j] + uint32_t(((h * g.W + w) * g.C + c0) * int(sizeof(T))) : kOutOfRange;
+    }
+    __device__ __forceinline__ void next(const GemmArgs& g) {
+        kk += BK;
+        c0 += BK;
+        while (c0 >= g.C) {
+            c0 -= g.C;
+            if (++s == g.S) {
+                s = 0;
+                ++rr;
+            }
+        }
+    }
+};
+
+// Rows of a strided matrix: lowered pixel rows (SEGMENTED for im2win strips)
+// or filter rows.  Offsets are relative to the tile's first row.
+template <typename T, int ROWS, int BK, bool PIXELS, bool SEGMENTED>
+struct DmaRows {
+    static constexpr int VEC = Vec<T>::n;
+    static constexpr int CPR = BK / VEC;
+    static constexpr int NL = (ROWS * CPR + 255) / 256;
+    static constexpr int RSTEP = 256 / CPR;
+    static_assert(ROWS * CPR % 256 == 0 || ROWS * CPR < 256, "whole wave loads");
+    uint32_t roff[NL];    // row start, bytes from the tile base
+    bool ok[NL];
+    int kk, t;
+    uint32_t seg;         // bytes
+    i32x4 rsrc;
+
+    __device__ __forceinline__ int64_t row_offset(const GemmArgs& g, int64_t row) const {
+        if (PIXELS) {
+            int32_t n, p, q;
+            decode_m(g, int32_t(row), n, p, q);
+            return int64_t(n) * g.sN + int64_t(p) * g.sP + int64_t(q) * g.sQ;
+        }
+        return row * int64_t(g.ldb);
+    }
+    __device__ __forceinline__ void init(const GemmArgs& g, int64_t row0, int tid) {
+        const int64_t nrows = PIXELS ? g.M : g.K;
+        const int64_t first = row0 < nrows ? row0 : nrows - 1;
+        const int64_t last = (row0 + ROWS - 1) < nrows ? row0 + ROWS - 1 : nrows - 1;
+        const int64_t off0 = row_offset(g, first);
+        // span of the tile: last row's start plus one full lowered row
+        const int64_t span = (row_offset(g, last) - off0 + g.Kc +
+                              (SEGMENTED ? int64_t(g.Kc / g.RCp) * (g.sS - g.RCp) : 0)) * int64_t(sizeof(T));
+        const T* base = static_cast<const T*>(PIXELS ? g.a : g.b) + off0;
+        rsrc = make_rsrc(base, uint32_t(span < int64_t(0x7fffffff) ? span : int64_t(0x7fffffff)));
+#pragma unroll
+        for (int j = 0; j < NL; ++j) {
+            const int64_t row = row0 + j * RSTEP + tid / CPR;
+            ok[j] = (j * RSTEP + tid / CPR < ROWS) && row < nrows;
+            roff[j] = uint32_t((row_offset(g, ok[j] ? row : first) - off0) * int64_t(sizeof(T)));
+        }
+        kk = dma_chunk<CPR>(tid) * VEC;
+        if (SEGMENTED) {
+            t = kk % g.RCp;
+            seg = uint32_t(int64_t(kk / g.RCp) * g.sS * int64_t(sizeof(T)));
+        } else {
+            t = kk;
+            seg = 0;
+        }
+    }
+    __device__ __forceinline__ uint32_t voff(const GemmArgs& g, int j) const {
+        return (ok[j] && kk < g.Kc) ? roff[j] + seg + uint32_t(t * int(sizeof(T))) : kOutOfRange;
+    }
+    __device__ __forceinline__ void next(const GemmArgs& g) {
+        kk += BK;
+        t += BK;
+        if (SEGMENTED) {
+            while (t >= g.RCp) {
+                t -= g.RCp;
+                seg += uint32_t(g.sS * int(sizeof(T)));
+            }
+        }
+    }
+};
+
+// ---------------------------------------------------------------------------
+template <typename T, int BM, int BN, int BK, int WGM, int WGN, int STAGES, bool NHWC_OUT, class ASrc, class BSrc>
+__global__ void __launch_bounds__(256) conv_gemm_dma_kernel(GemmArgs g) {
+    constexpr int VEC = Vec<T>::n;
+    constexpr int CPR = BK / VEC;
+    constexpr int WM = BM / WGM, WN = BN / WGN;
+    constexpr int TM = WM / 16, TN = WN / 16;
+    constexpr int KB = 4 * VEC;
+    constexpr int STAGE_ELEMS = (BM + BN) * BK;
+    // DMA loads per thread per tile.  A narrow B tile (fewer than 256 chunks)
+    // is loaded by the first waves only, so the other waves issue fewer loads
+    // and must wait with their own count.
+    constexpr int B_WAVES = BN * CPR >= 256 ? 4 : (BN * CPR) / 64;
+    constexpr int NLOADS = ASrc::NL + BSrc::NL;
+    constexpr int NLOADS_NO_B = ASrc::NL;
+    static_assert(BN * CPR >= 256 || (BN * CPR) % 64 == 0, "B tile in whole wave loads");
+    static_assert(WGM * WGN == 4 && BK % KB == 0 && WM % 16 == 0 && WN % 16 == 0, "tile shape");
+    static_assert(STAGES >= 2, "at least double buffering");
+
+    __shared__ __attribute__((aligned(16))) T smem[STAGES * STAGE_ELEMS];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WGN, wn = wave - (wave / WGN) * WGN;
+    const int tile_m = blockIdx.x / g.tiles_n;
+    const int tile_n = blockIdx.x - tile_m * g.tiles_n;
+    const int64_t m0 = int64_t(tile_m) * BM;
+    const int n0 = tile_n * BN;
+
+    ASrc la;
+    BSrc lb;
+    la.init(g, m0, tid);
+    lb.init(g, n0, tid);
+
+    const uint32_t lds0 = lds_offset(smem);
+    // Issue one tile's loads into stage `st`: load j of wave w covers LDS chunk
+    // slots [j*256 + w*64, +64) of the A (then B) region.
+    auto issue = [&](int st) {
+        const uint32_t a_base = lds0 + uint32_t(st * STAGE_ELEMS * sizeof(T));
+        const uint32_t b_base = a_base + uint32_t(BM * BK * sizeof(T));
+#pragma unroll
+        for (int j = 0; j < ASrc::NL; ++j) dma16(la.rsrc, la.voff(g, j), a_base + uint32_t((j * 256 + wave * 64) * 16));
+#pragma unroll
+        for (int j = 0; j < BSrc::NL; ++j) {
+            if (wave < B_WAVES) dma16(lb.rsrc, lb.voff(g, j), b_base + uint32_t((j * 256 + wave * 64) * 16));
+        }
+        la.next(g);
+        lb.next(g);
+    };
+
+    f32x4 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int nkt = (g.Kc + BK - 1) / BK;
+#pragma unroll
+    for (int st = 0; st < STAGES - 1; ++st)
+        if (st < nkt) issue(st);
+
+    const int frag_row = lane & 15;
+    const int frag_chunk = lane >> 4;
+    for (int kt = 0; kt < nkt; ++kt) {
+        if (kt + STAGES - 2 < nkt) {
+            // the STAGES-2 tiles after kt may stay in flight
+            if (wave < B_WAVES)
+                wait_vmcnt<(STAGES - 2) * NLOADS>();
+            else
+                wait_vmcnt<(STAGES - 2) * NLOADS_NO_B>();
+        } else {
+            wait_vmcnt<0>();
+        }
+        lds_barrier();
+        if (kt + STAGES - 1 < nkt) issue((kt + STAGES - 1) % STAGES);
+        const T* sA = smem + (kt % STAGES) * STAGE_ELEMS;
+        const T* sB = sA + BM * BK;
+#pragma unroll
+        for (int kb = 0; kb < BK / KB; ++kb) {
+            u32x4 fa[TM], fb[TN];
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                const int row = wm * WM + i * 16 + frag_row;
+                fa[i] = load16(sA + row * BK + swz_chunk<CPR>(row, kb * 4 + frag_chunk) * VEC);
+            }
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int row = wn * WN + j * 16 + frag_row;
+                fb[j] = load16(sB + row * BK + swz_chunk<CPR>(row, kb * 4 + frag_chunk) * VEC);
+            }
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    acc[i][j] = NHWC_OUT ? Mfma<T>::run(fb[j], fa[i], acc[i][j]) : Mfma<T>::run(fa[i], fb[j], acc[i][j]);
+        }
+    }
+
+    store_tile<T, BM, BN, WM, WN, TM, TN, NHWC_OUT>(g, acc, m0, n0, wm, wn, lane);
+}
+
+}  // namespace convlower
