@@ -207,7 +207,7 @@ struct DmaRows {
 
 // ---------------------------------------------------------------------------
 template <typename T, int BM, int BN, int BK, int WGM, int WGN, int STAGES, bool NHWC_OUT, class ASrc, class BSrc>
-__global__ void __launch_bounds__(256) conv_gemm_dma_kernel(GemmArgs g) {
+__global__ void __launch_bounds__(256, 2) conv_gemm_dma_kernel(GemmArgs g) {
     constexpr int VEC = Vec<T>::n;
     constexpr int CPR = BK / VEC;
     constexpr int WM = BM / WGM, WN = BN / WGN;
