@@ -312,7 +312,10 @@ void launch_dma_tile(const conv_desc& d, const GemmArgs& g, hipStream_t st) {
     const bool nhwc = d.p.layout == CONV_NHWC;
     if (d.p.algo == CONV_ALGO_IMPLICIT) {
         // NHWC with C a whole number of vectors (checked when planning)
-        launch_dma_core<T, BM, BN, BK, WGM, WGN, STAGES, true, DmaWindowNHWC<T, BM, BK>, B>(d, g, st);
+        if (d.p.C % BK == 0)
+            launch_dma_core<T, BM, BN, BK, WGM, WGN, STAGES, true, DmaWindowNHWCBlocked<T, BM, BK>, B>(d, g, st);
+        else
+            launch_dma_core<T, BM, BN, BK, WGM, WGN, STAGES, true, DmaWindowNHWC<T, BM, BK>, B>(d, g, st);
     } else if (!d.elided && d.p.algo == CONV_ALGO_IM2WIN) {
         using A = DmaRows<T, BM, BK, true, true>;
         if (nhwc) launch_dma_core<T, BM, BN, BK, WGM, WGN, STAGES, true, A, B>(d, g, st);

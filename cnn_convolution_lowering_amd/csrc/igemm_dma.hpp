@@ -18,8 +18,8 @@
 //   iteration kt:  wait until tile kt has landed (the tiles after it may
 //                  still be in flight) -> barrier (every wave's part of tile kt
 //                  is visible, and every wave has finished reading the stage
-//                  of tile kt-1) -> issue tile kt+STAGES-1 into that stage ->
-//                  MFMAs on tile kt.
+//                  of tile kt-1) -> MFMAs on tile kt -> issue tile
+//                  kt+STAGES-1 into the stage of tile kt-1.
 //
 // LDS tiles use the same row swizzle as conv_gemm_kernel (swz_chunk).  Since a
 // DMA writes LDS in lane order, the swizzle is applied on the global side:
@@ -126,14 +126,76 @@ struct DmaWindowNHWC {
     }
     __device__ __forceinline__ uint32_t voff(const GemmArgs& g, int j) const {
         const int h = h0[j] + rr * g.dh, w = w0[j] + s * g.dw;
-        const bool in = ok[j] && kk < g.Kc && unsigned(h) < unsigned(g.H) && unsigned(w) < unsigned(g.W);
-        return in ? nbase[j] + uint32_t(((h * g.W + w) * g.C + c0) * int(sizeof(T))) : kOutOfRange;
+        const bool in = ok[j] & (kk < g.Kc) & (unsigned(h) < unsigned(g.H)) & (unsigned(w) < unsigned(g.W));
+        const uint32_t o = nbase[j] + uint32_t(((h * g.W + w) * g.C + c0) * int(sizeof(T)));
+        return in ? o : kOutOfRange;
     }
     __device__ __forceinline__ void next(const GemmArgs& g) {
         kk += BK;
         c0 += BK;
         while (c0 >= g.C) {
             c0 -= g.C;
+            if (++s == g.S) {
+                s = 0;
+                ++rr;
+            }
+        }
+    }
+};
+
+// As DmaWindowNHWC for C a multiple of BK: a tile then covers BK channels of
+// one kernel tap (r, s) for every lane, so the tap and channel block are
+// wave-uniform (scalar registers) and each load's offset is one add from a
+// per-row base, two range checks and a select.
+template <typename T, int ROWS, int BK>
+struct DmaWindowNHWCBlocked {
+    static constexpr int VEC = Vec<T>::n;
+    static constexpr int CPR = BK / VEC;
+    static constexpr int NL = ROWS * CPR / 256;
+    static constexpr int RSTEP = 256 / CPR;
+    static_assert(ROWS * CPR % 256 == 0, "whole wave loads");
+    int32_t rowbase[NL];  // bytes: image base + (h0*W + w0)*C, plus this lane's channel chunk
+    int32_t h0[NL], w0[NL];
+    int cb, s, rr, kk;    // uniform: channel block start, tap, contraction position
+    i32x4 rsrc;
+
+    __device__ __forceinline__ void init(const GemmArgs& g, int64_t row0, int tid) {
+        int32_t n_first, p_, q_;
+        decode_m(g, int32_t(row0 < g.M ? row0 : g.M - 1), n_first, p_, q_);
+        const int64_t img = int64_t(g.H) * g.W * g.C;
+        const T* base = static_cast<const T*>(g.a) + int64_t(n_first) * img;
+        const int64_t n_imgs = g.M / g.PQ;
+        const int64_t bytes = (n_imgs - n_first) * img * int64_t(sizeof(T));
+        rsrc = make_rsrc(base, uint32_t(bytes < int64_t(0x7fffffff) ? bytes : int64_t(0x7fffffff)));
+        const int chunk = dma_chunk<CPR>(tid);
+#pragma unroll
+        for (int j = 0; j < NL; ++j) {
+            const int64_t m = row0 + j * RSTEP + tid / CPR;
+            const bool ok = m < g.M;
+            int32_t n, p, q;
+            decode_m(g, ok ? int32_t(m) : 0, n, p, q);
+            const int hv = p * g.sh - g.ph;
+            w0[j] = q * g.sw - g.pw;
+            rowbase[j] = int32_t((n - n_first) * img * int64_t(sizeof(T))) +
+                         ((hv * g.W + w0[j]) * g.C + chunk * VEC) * int(sizeof(T));
+            h0[j] = ok ? hv : -(1 << 28);   // rows past M never pass the range check
+        }
+        cb = 0;
+        s = 0;
+        rr = 0;
+        kk = 0;
+    }
+    __device__ __forceinline__ uint32_t voff(const GemmArgs& g, int j) const {
+        const int dh = rr * g.dh, dw = s * g.dw;
+        const bool in = (unsigned(h0[j] + dh) < unsigned(g.H)) & (unsigned(w0[j] + dw) < unsigned(g.W)) & (kk < g.Kc);
+        const int32_t o = rowbase[j] + ((dh * g.W + dw) * g.C + cb) * int(sizeof(T));
+        return in ? uint32_t(o) : kOutOfRange;
+    }
+    __device__ __forceinline__ void next(const GemmArgs& g) {
+        kk += BK;
+        cb += BK;
+        if (cb == g.C) {
+            cb = 0;
             if (++s == g.S) {
                 s = 0;
                 ++rr;
@@ -280,7 +342,6 @@ __global__ void __launch_bounds__(256, 2) conv_gemm_dma_kernel(GemmArgs g) {
             wait_vmcnt<0>();
         }
         lds_barrier();
-        if (kt + STAGES - 1 < nkt) issue((kt + STAGES - 1) % STAGES);
         const T* sA = smem + (kt % STAGES) * STAGE_ELEMS;
         const T* sB = sA + BM * BK;
 #pragma unroll
@@ -302,6 +363,10 @@ __global__ void __launch_bounds__(256, 2) conv_gemm_dma_kernel(GemmArgs g) {
                 for (int j = 0; j < TN; ++j)
                     acc[i][j] = NHWC_OUT ? Mfma<T>::run(fb[j], fa[i], acc[i][j]) : Mfma<T>::run(fa[i], fb[j], acc[i][j]);
         }
+        // The next tile's loads go out after this tile's MFMAs are issued, so
+        // their address arithmetic overlaps the MFMAs in flight.  Their stage
+        // was last read in iteration kt-1, which every wave has left (barrier).
+        if (kt + STAGES - 1 < nkt) issue((kt + STAGES - 1) % STAGES);
     }
 
     store_tile<T, BM, BN, WM, WN, TM, TN, NHWC_OUT>(g, acc, m0, n0, wm, wn, lane);
