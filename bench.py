@@ -187,6 +187,39 @@ def cpu_baseline(wl, budget_s=10.0):
                       % (n, spec.N, spec.name, len(wl.layers), t)}
 
 
+def time_steps(wl, dev, algo, steps, warmup, layer=None):
+    """ms per step of the whole path with one lowering, HIP events on the
+    current stream; also the largest workspace of its layers."""
+    import torch
+    layers, ws = build_layers(wl, dev, algo)
+    stream = torch.cuda.current_stream(dev)
+    if layer is not None:
+        for l in layers[:layer]:
+            for st in STAGES:
+                run_stage(l, st, ws, stream)
+        layers = [layers[layer]]
+    for _ in range(warmup):
+        for l in layers:
+            for st in STAGES:
+                run_stage(l, st, ws, stream)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(steps):
+        for l in layers:
+            for st in STAGES:
+                run_stage(l, st, ws, stream)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    info = {"ms_per_step": ms,
+            "workspace_bytes": max(l["desc"].workspace_bytes for l in layers),
+            "lowered_bytes_max": max(l["desc"].info["ws_lowered_bytes"] for l in layers),
+            "im2col_bytes_max": max(l["desc"].info["im2col_bytes"] for l in layers)}
+    del layers, ws
+    return info
+
+
 def load_traffic(kernel_key: str):
     try:
         with open(TRAFFIC_FILE) as f:
@@ -204,7 +237,10 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c2", choices=sorted(WORKLOAD_TEXT))
-    ap.add_argument("--algo", default="im2win", choices=["im2win", "im2col", "implicit"])
+    ap.add_argument("--algo", default="implicit", choices=["im2win", "im2col", "implicit"],
+                    help="lowering timed for the headline value (the other two are timed as well, "
+                         "unless --only-algo)")
+    ap.add_argument("--only-algo", action="store_true", help="time only --algo")
     ap.add_argument("--layer", type=int, default=None,
                     help="time only this layer of the workload (chained inputs are still computed once)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -334,6 +370,15 @@ def main(argv=None):
                       "ratio_max_over_layers": max(p["ws_vs_im2col"] for p in per_layer)},
         "layers": per_layer,
     }
+    if not args.only_algo:
+        flops_total = step_flops
+        algos = {}
+        for algo in ("implicit", "im2win", "im2col"):
+            print("bench: timing the %s lowering" % algo, file=sys.stderr, flush=True)
+            r = time_steps(wl, dev, algo, max(5, args.steps // 2), max(2, args.warmup // 2), args.layer)
+            r["tflops"] = flops_total / (r["ms_per_step"] * 1e-3) / 1e12
+            algos[algo] = r
+        out["algorithms"] = algos
     if not args.no_cpu_baseline:
         print("bench: timing the fp64 reference on the host", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
