@@ -15,6 +15,7 @@
 #include "../../include/convlower.h"
 #include "igemm.hpp"
 #include "igemm_dma.hpp"
+#include "igemm_nchw.hpp"
 #include "lowering.hpp"
 
 using namespace convlower;
@@ -30,9 +31,23 @@ enum TileId : int32_t {
     TILE_128x64 = 1,
     TILE_128x32 = 2,
     TILE_256x128 = 3,   // pipelined (LDS-DMA) kernel only
+    TILE_64x128 = 4,    // fp32 NCHW pipelined kernel only
 };
 
 }  // namespace
+
+// Variants of the fp32 NCHW fused kernel (BM, BN, BK, STAGES).  The default
+// per shape (see plan) follows a sweep of all of them on the encoder layers;
+// CONVLOWER_NCHW_VARIANT=<index> forces one, for tuning.
+struct NchwVariant {
+    int bm, bn, bk, stages;
+};
+constexpr NchwVariant kNchwVariants[] = {
+    {128, 32, 32, 3}, {128, 64, 32, 3}, {128, 128, 32, 3}, {64, 128, 32, 3},
+    {128, 64, 16, 4}, {128, 64, 16, 6}, {64, 64, 32, 4},  {64, 64, 16, 6},
+    {128, 32, 16, 4},
+};
+constexpr int kNchwVariantCount = sizeof(kNchwVariants) / sizeof(kNchwVariants[0]);
 
 struct conv_desc {
     uint32_t magic;
@@ -45,6 +60,8 @@ struct conv_desc {
     uint64_t im2win_bytes, im2col_bytes;
     int32_t tile;       // TileId
     bool dma;           // pipelined LDS-DMA contraction kernel
+    bool nchw_dma;      // pipelined fp32 NCHW fused kernel
+    int32_t nchw_variant;   // index into kNchwVariants
     int32_t tile_m, tile_n, tile_k;
     // NCHW staging (0 = use the element-wise kernel)
     int32_t stage_chunk, stage_ld;
@@ -126,9 +143,31 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d) {
     // gives two workgroups per CU, else 128.
     d.tile = p.K <= 32 ? TILE_128x32 : (p.K <= 64 ? TILE_128x64 : TILE_128x128);
     if (d.dma && d.tile == TILE_128x128 && (d.M / 256) * ((p.K + 127) / 128) >= 512) d.tile = TILE_256x128;
-    d.tile_m = d.tile == TILE_256x128 ? 256 : 128;
+    // fp32 NCHW fused windows: the pipelined kernel with 4-byte window loads.
+    d.nchw_dma = implicit && !nhwc && p.dtype == CONV_F32 && x_bytes < (uint64_t(1) << 31) &&
+                 b_bytes < (uint64_t(1) << 31);
+    if (d.nchw_dma && d.tile == TILE_128x128 && (d.M / 128) * ((p.K + 127) / 128) < 512) d.tile = TILE_64x128;
+    d.tile_m = d.tile == TILE_256x128 ? 256 : (d.tile == TILE_64x128 ? 64 : 128);
     d.tile_n = d.tile == TILE_128x32 ? 32 : (d.tile == TILE_128x64 ? 64 : 128);
     d.tile_k = p.dtype == CONV_F32 ? 16 : 32;
+    // fp32 NCHW: narrow K -> 128-row tiles, 16-deep stages x4; wide K -> 64-row
+    // tiles, 64 or 128 channels wide depending on how many workgroups that gives.
+    if (p.K <= 32)
+        d.nchw_variant = 8;
+    else if (p.K <= 64)
+        d.nchw_variant = 4;
+    else
+        d.nchw_variant = (d.M / 64) * ((p.K + 127) / 128) >= 768 ? 3 : 7;
+    if (d.nchw_dma) {
+        // Tuning override: CONVLOWER_NCHW_VARIANT=<index> selects another compiled variant.
+        if (const char* v = std::getenv("CONVLOWER_NCHW_VARIANT")) {
+            const int i = std::atoi(v);
+            if (i >= 0 && i < kNchwVariantCount) d.nchw_variant = i;
+        }
+        d.tile_m = kNchwVariants[d.nchw_variant].bm;
+        d.tile_n = kNchwVariants[d.nchw_variant].bn;
+        d.tile_k = kNchwVariants[d.nchw_variant].bk;
+    }
 
     // NCHW staging tile: whole strip columns of R*C values per LDS row.
     d.stage_chunk = 0;
@@ -384,6 +423,42 @@ void launch_gemm(const conv_desc& d, const void* x, const void* w, const void* b
         g.sN = d.P * g.sP;
         g.RCp = int32_t(d.Kl);
         g.sS = 0;
+    }
+    if (d.nchw_dma) {
+        if constexpr (sizeof(T) == 4) {
+            auto launch = [&](auto kernel, int BM, int BN) {
+                GemmArgs h = g;
+                h.tiles_n = int32_t((d.p.K + BN - 1) / BN);
+                const uint32_t blocks = uint32_t(((uint64_t(d.M) + BM - 1) / BM) * h.tiles_n);
+                kernel<<<blocks, 256, 0, st>>>(h);
+            };
+            const bool mask = d.p.R * d.p.S <= 32;
+#define CONVLOWER_NCHW_CASE(I, BM, BN, BK, ST)                                                     \
+    case I:                                                                                        \
+        if (mask) launch(conv_nchw_f32_dma_kernel<BM, BN, BK, 2, 2, ST, true>, BM, BN);           \
+        else launch(conv_nchw_f32_dma_kernel<BM, BN, BK, 2, 2, ST, false>, BM, BN);               \
+        break;
+            switch (d.nchw_variant) {
+                case 0:
+                    if (mask) launch(conv_nchw_f32_dma_kernel<128, 32, 32, 4, 1, 3, true>, 128, 32);
+                    else launch(conv_nchw_f32_dma_kernel<128, 32, 32, 4, 1, 3, false>, 128, 32);
+                    break;
+                CONVLOWER_NCHW_CASE(1, 128, 64, 32, 3)
+                CONVLOWER_NCHW_CASE(2, 128, 128, 32, 3)
+                CONVLOWER_NCHW_CASE(3, 64, 128, 32, 3)
+                CONVLOWER_NCHW_CASE(4, 128, 64, 16, 4)
+                CONVLOWER_NCHW_CASE(5, 128, 64, 16, 6)
+                CONVLOWER_NCHW_CASE(6, 64, 64, 32, 4)
+                CONVLOWER_NCHW_CASE(7, 64, 64, 16, 6)
+                case 8:
+                    if (mask) launch(conv_nchw_f32_dma_kernel<128, 32, 16, 4, 1, 4, true>, 128, 32);
+                    else launch(conv_nchw_f32_dma_kernel<128, 32, 16, 4, 1, 4, false>, 128, 32);
+                    break;
+                default: break;
+            }
+#undef CONVLOWER_NCHW_CASE
+        }
+        return;
     }
     if (d.dma) {
         switch (d.tile) {

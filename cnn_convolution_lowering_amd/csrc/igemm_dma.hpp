@@ -344,6 +344,8 @@ __global__ void __launch_bounds__(256, 2) conv_gemm_dma_kernel(GemmArgs g) {
         lds_barrier();
         const T* sA = smem + (kt % STAGES) * STAGE_ELEMS;
         const T* sB = sA + BM * BK;
+        // All fragment reads of a step are issued ahead of its MFMAs
+        // (sched_barrier), so the LDS latency is paid once per step.
 #pragma unroll
         for (int kb = 0; kb < BK / KB; ++kb) {
             u32x4 fa[TM], fb[TN];
@@ -357,11 +359,13 @@ __global__ void __launch_bounds__(256, 2) conv_gemm_dma_kernel(GemmArgs g) {
                 const int row = wn * WN + j * 16 + frag_row;
                 fb[j] = load16(sB + row * BK + swz_chunk<CPR>(row, kb * 4 + frag_chunk) * VEC);
             }
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
                 for (int j = 0; j < TN; ++j)
                     acc[i][j] = NHWC_OUT ? Mfma<T>::run(fb[j], fa[i], acc[i][j]) : Mfma<T>::run(fa[i], fb[j], acc[i][j]);
+            __builtin_amdgcn_sched_barrier(0);
         }
         // The next tile's loads go out after this tile's MFMAs are issued, so
         // their address arithmetic overlaps the MFMAs in flight.  Their stage
