@@ -10,7 +10,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libconvlower.so")
-SOURCES = [os.path.join(CSRC, "convlower.hip")]
+SOURCES = [os.path.join(CSRC, f) for f in
+           ("convlower.hip", "contract_f32.hip", "contract_f16.hip", "contract_bf16.hip")]
 
 # Packed-fp32 instructions are kept out of every kernel: hipcc forms them from
 # plain float code on its own, and they are not needed here.
@@ -27,11 +28,28 @@ def hipcc() -> str:
 
 
 def build_library(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc()] + HIPCC_FLAGS + ["-I", INCLUDE] + SOURCES + ["-o", tmp]
+    """Compile each source to an object in parallel, then link the library."""
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    tag = "%d" % os.getpid()
+    compile_flags = [f for f in HIPCC_FLAGS if f != "-shared"]
+    jobs = []
+    for src in SOURCES:
+        obj = os.path.join(objdir, os.path.splitext(os.path.basename(src))[0] + "." + tag + ".o")
+        cmd = [hipcc()] + compile_flags + ["-I", INCLUDE, "-c", src, "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        jobs.append((subprocess.Popen(cmd), obj, cmd))
+    failed = [cmd for proc, _, cmd in jobs if proc.wait() != 0]
+    if failed:
+        raise subprocess.CalledProcessError(1, failed[0])
+    tmp = LIB + ".tmp" + tag
+    cmd = [hipcc()] + HIPCC_FLAGS + [obj for _, obj, _ in jobs] + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)
+    for _, obj, _ in jobs:
+        os.remove(obj)
     os.replace(tmp, LIB)
     return LIB
 

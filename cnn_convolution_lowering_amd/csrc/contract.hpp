@@ -1,0 +1,273 @@
+// Contraction launchers: pick the kernel, tile variant and operand loaders
+// recorded in the descriptor and enqueue the contraction with its fused
+// epilogue.  Included once per storage type (contract_f32.hip,
+// contract_f16.hip, contract_bf16.hip) so the kernels of the three types
+// compile in parallel.
+#pragma once
+
+#include "dispatch.hpp"
+#include "igemm.hpp"
+#include "igemm_dma.hpp"
+#include "igemm_nchw.hpp"
+#include "igemm_strip.hpp"
+#include "igemm_wide.hpp"
+
+namespace convlower {
+
+template <typename T, int BM, int BN, int BK, int WGM, int WGN, bool NHWC_OUT, class ALoad, class BLoad>
+void launch_core(const conv_desc& d, GemmArgs g, hipStream_t st) {
+    g.tiles_n = int32_t((d.p.K + BN - 1) / BN);
+    const uint64_t tiles_m = (uint64_t(d.M) + BM - 1) / BM;
+    const uint32_t blocks = uint32_t(tiles_m * g.tiles_n);
+    conv_gemm_kernel<T, BM, BN, BK, WGM, WGN, NHWC_OUT, ALoad, BLoad><<<blocks, 256, 0, st>>>(g);
+}
+
+// Pick the loaders for the descriptor and launch one tile shape.
+template <typename T, int BM, int BN, int BK, int WGM, int WGN>
+void launch_gemm_tile(const conv_desc& d, const GemmArgs& g, hipStream_t st) {
+    constexpr int VEC = Vec<T>::n;
+    using BRows = StridedRows<T, BN, BK, false, false>;
+    using BRowsElem = StridedRows<T, BN, BK, false, true>;
+    const bool nhwc = d.p.layout == CONV_NHWC;
+    if (d.p.algo != CONV_ALGO_IMPLICIT) {
+        // lowered buffer (im2win strips / im2col rows) or 1x1 NHWC input in place
+        const bool seg = !d.elided && d.p.algo == CONV_ALGO_IM2WIN;
+        if (seg) {
+            using A = StridedRows<T, BM, BK, true, false>;
+            if (nhwc) launch_core<T, BM, BN, BK, WGM, WGN, true, A, BRows>(d, g, st);
+            else launch_core<T, BM, BN, BK, WGM, WGN, false, A, BRows>(d, g, st);
+        } else {
+            using A = StridedRows<T, BM, BK, false, false>;
+            if (nhwc) launch_core<T, BM, BN, BK, WGM, WGN, true, A, BRows>(d, g, st);
+            else launch_core<T, BM, BN, BK, WGM, WGN, false, A, BRows>(d, g, st);
+        }
+        return;
+    }
+    const bool b_vec = d.Kg % VEC == 0;
+    if (nhwc && d.p.C % VEC == 0) {
+        launch_core<T, BM, BN, BK, WGM, WGN, true, WindowVecNHWC<T, BM, BK>, BRows>(d, g, st);
+    } else if (nhwc) {
+        using A = WindowElem<T, BM, BK, true>;
+        if (b_vec) launch_core<T, BM, BN, BK, WGM, WGN, true, A, BRows>(d, g, st);
+        else launch_core<T, BM, BN, BK, WGM, WGN, true, A, BRowsElem>(d, g, st);
+    } else {
+        using A = WindowElem<T, BM, BK, false>;
+        if (b_vec) launch_core<T, BM, BN, BK, WGM, WGN, false, A, BRows>(d, g, st);
+        else launch_core<T, BM, BN, BK, WGM, WGN, false, A, BRowsElem>(d, g, st);
+    }
+}
+
+template <typename T, int BM, int BN, int BK, int WGM, int WGN, int STAGES, bool WIDE, bool NHWC_OUT, class ASrc,
+          class BSrc>
+void launch_dma_core(const conv_desc& d, GemmArgs g, hipStream_t st) {
+    g.tiles_n = int32_t((d.p.K + BN - 1) / BN);
+    const uint64_t tiles_m = (uint64_t(d.M) + BM - 1) / BM;
+    const uint32_t blocks = uint32_t(tiles_m * g.tiles_n);
+    constexpr int NT = 64 * WGM * WGN;
+    if constexpr (WIDE)
+        conv_gemm_wide_kernel<T, BM, BN, BK, WGM, WGN, STAGES, ASrc, BSrc><<<blocks, NT, 0, st>>>(g);
+    else
+        conv_gemm_dma_kernel<T, BM, BN, BK, WGM, WGN, STAGES, NHWC_OUT, ASrc, BSrc><<<blocks, NT, 0, st>>>(g);
+}
+
+template <typename T, int BM, int BN, int WGM, int WGN, int STRIP, int BST>
+void launch_strip(const conv_desc& d, GemmArgs g, hipStream_t st) {
+    g.tiles_n = int32_t((d.p.K + BN - 1) / BN);
+    const uint64_t tiles_m = (uint64_t(d.M) + BM - 1) / BM;
+    const uint32_t blocks = uint32_t(tiles_m * g.tiles_n);
+    conv_strip_kernel<T, BM, BN, WGM, WGN, STRIP, BST><<<blocks, 64 * WGM * WGN, 0, st>>>(g);
+}
+
+// Pick the DMA sources for the descriptor and launch one tile shape of the
+// pipelined kernel (WIDE: the one-wave-per-SIMD schedule, implicit NHWC
+// windows with C a multiple of BK only -- checked when planning).
+template <typename T, int BM, int BN, int BK, int WGM, int WGN, int STAGES, bool WIDE>
+void launch_dma_tile(const conv_desc& d, const GemmArgs& g, hipStream_t st) {
+    constexpr int NT = 64 * WGM * WGN;
+    using B = DmaRows<T, BN, BK, false, false, NT>;
+    const bool nhwc = d.p.layout == CONV_NHWC;
+    if constexpr (WIDE) {
+        using BW = DmaRows<T, BN, BK, false, false, NT, 1>;
+        launch_dma_core<T, BM, BN, BK, WGM, WGN, STAGES, true, true, DmaWindowNHWCBlocked<T, BM, BK, NT, 1>, BW>(d, g,
+                                                                                                              st);
+    } else if (d.p.algo == CONV_ALGO_IMPLICIT) {
+        // NHWC with C a whole number of vectors (checked when planning)
+        if (d.p.C % BK == 0)
+            launch_dma_core<T, BM, BN, BK, WGM, WGN, STAGES, false, true, DmaWindowNHWCBlocked<T, BM, BK, NT>, B>(
+                d, g, st);
+        else
+            launch_dma_core<T, BM, BN, BK, WGM, WGN, STAGES, false, true, DmaWindowNHWC<T, BM, BK, NT>, B>(d, g, st);
+    } else if (!d.elided && d.p.algo == CONV_ALGO_IM2WIN) {
+        using A = DmaRows<T, BM, BK, true, true, NT>;
+        if (nhwc) launch_dma_core<T, BM, BN, BK, WGM, WGN, STAGES, false, true, A, B>(d, g, st);
+        else launch_dma_core<T, BM, BN, BK, WGM, WGN, STAGES, false, false, A, B>(d, g, st);
+    } else {
+        using A = DmaRows<T, BM, BK, true, false, NT>;
+        if (nhwc) launch_dma_core<T, BM, BN, BK, WGM, WGN, STAGES, false, true, A, B>(d, g, st);
+        else launch_dma_core<T, BM, BN, BK, WGM, WGN, STAGES, false, false, A, B>(d, g, st);
+    }
+}
+
+template <typename T>
+void launch_gemm(const conv_desc& d, const void* x, const void* w, const void* bias, void* y, const void* ws,
+                 hipStream_t st) {
+    const char* wsb = static_cast<const char*>(ws);
+    GemmArgs g{};
+    g.b = d.pack ? static_cast<const void*>(wsb + d.off_filter) : w;
+    g.bias = bias;
+    g.y = y;
+    g.M = d.M;
+    g.K = int32_t(d.p.K);
+    g.PQ = int32_t(d.P * d.Q);
+    g.Q = int32_t(d.Q);
+    g.C = int32_t(d.p.C);
+    g.H = int32_t(d.p.H);
+    g.W = int32_t(d.p.W);
+    g.R = int32_t(d.p.R);
+    g.S = int32_t(d.p.S);
+    g.sh = d.p.stride_h;
+    g.sw = d.p.stride_w;
+    g.ph = d.p.pad_h;
+    g.pw = d.p.pad_w;
+    g.dh = d.p.dil_h;
+    g.dw = d.p.dil_w;
+    if (d.p.algo == CONV_ALGO_IMPLICIT) {
+        // windows gathered from x; filter rows in their own order
+        g.a = x;
+        g.Kc = int32_t(d.Kg);
+        g.ldb = int32_t(d.Kg);
+    } else if (d.elided) {
+        // 1x1, no padding, NHWC: row (n, p, q) is x[n][p*sh][q*sw][0..C)
+        g.a = x;
+        g.Kc = int32_t(d.Kl);
+        g.ldb = int32_t(d.Kl);
+        g.sN = d.p.H * d.p.W * d.p.C;
+        g.sP = int64_t(d.p.stride_h) * d.p.W * d.p.C;
+        g.sQ = int64_t(d.p.stride_w) * d.p.C;
+        g.RCp = int32_t(d.Kl);
+        g.sS = 0;
+    } else if (d.p.algo == CONV_ALGO_IM2WIN) {
+        g.a = wsb + d.off_low;
+        g.Kc = int32_t(d.Kl);
+        g.ldb = int32_t(d.Kl);
+        g.sP = d.W_used * d.RCp;
+        g.sN = d.P * g.sP;
+        g.sQ = int64_t(d.p.stride_w) * d.RCp;
+        g.RCp = int32_t(d.RCp);
+        g.sS = int32_t(int64_t(d.p.dil_w) * d.RCp);
+    } else {
+        g.a = wsb + d.off_low;
+        g.Kc = int32_t(d.Kl);
+        g.ldb = int32_t(d.Kl);
+        g.sQ = d.Kl;
+        g.sP = d.Q * d.Kl;
+        g.sN = d.P * g.sP;
+        g.RCp = int32_t(d.Kl);
+        g.sS = 0;
+    }
+    if (d.kernel == KERN_NCHW) {
+        if constexpr (sizeof(T) == 4) {
+            auto launch = [&](auto kernel, int BM, int BN) {
+                GemmArgs h = g;
+                h.tiles_n = int32_t((d.p.K + BN - 1) / BN);
+                const uint32_t blocks = uint32_t(((uint64_t(d.M) + BM - 1) / BM) * h.tiles_n);
+                kernel<<<blocks, 256, 0, st>>>(h);
+            };
+            const bool mask = d.p.R * d.p.S <= 32;
+#define CONVLOWER_NCHW_CASE(I)                                                                                 \
+    case I: {                                                                                                  \
+        constexpr TileVariant v = kNchwVariants[I];                                                            \
+        if (mask) launch(conv_nchw_f32_dma_kernel<v.bm, v.bn, v.bk, v.wgm, v.wgn, v.stages, true>, v.bm, v.bn); \
+        else launch(conv_nchw_f32_dma_kernel<v.bm, v.bn, v.bk, v.wgm, v.wgn, v.stages, false>, v.bm, v.bn);    \
+        break;                                                                                                 \
+    }
+            switch (d.variant) {
+                CONVLOWER_NCHW_CASE(0)
+                CONVLOWER_NCHW_CASE(1)
+                CONVLOWER_NCHW_CASE(2)
+                CONVLOWER_NCHW_CASE(3)
+                CONVLOWER_NCHW_CASE(4)
+                CONVLOWER_NCHW_CASE(5)
+                CONVLOWER_NCHW_CASE(6)
+                CONVLOWER_NCHW_CASE(7)
+                CONVLOWER_NCHW_CASE(8)
+                default: break;
+            }
+#undef CONVLOWER_NCHW_CASE
+        }
+        return;
+    }
+    // BK of a variant is given for 16-bit storage; fp32 rows of the same bytes hold half as many elements.
+    constexpr int DIV = sizeof(T) == 4 ? 2 : 1;
+    if (d.kernel == KERN_DMA) {
+#define CONVLOWER_DMA_CASE(I)                                                                     \
+    case I: {                                                                                     \
+        constexpr TileVariant v = kDmaVariants[I];                                                \
+        launch_dma_tile<T, v.bm, v.bn, v.bk / DIV, v.wgm, v.wgn, v.stages, false>(d, g, st); \
+        break;                                                                                    \
+    }
+        switch (d.variant) {
+            CONVLOWER_DMA_CASE(0)
+            CONVLOWER_DMA_CASE(1)
+            CONVLOWER_DMA_CASE(2)
+            CONVLOWER_DMA_CASE(3)
+            CONVLOWER_DMA_CASE(4)
+            CONVLOWER_DMA_CASE(5)
+            CONVLOWER_DMA_CASE(6)
+            default: break;
+        }
+#undef CONVLOWER_DMA_CASE
+        return;
+    }
+    if (d.kernel == KERN_STRIP) {
+        if constexpr (sizeof(T) == 2) {
+#define CONVLOWER_STRIP_CASE(I)                                                          \
+    case I: {                                                                            \
+        constexpr StripVariant v = kStripVariants[I];                                    \
+        launch_strip<T, v.bm, v.bn, v.wgm, v.wgn, v.strip, v.bst>(d, g, st); \
+        break;                                                                           \
+    }
+            switch (d.variant) {
+                CONVLOWER_STRIP_CASE(0)
+                CONVLOWER_STRIP_CASE(1)
+                CONVLOWER_STRIP_CASE(2)
+                CONVLOWER_STRIP_CASE(3)
+                CONVLOWER_STRIP_CASE(4)
+                default: break;
+            }
+#undef CONVLOWER_STRIP_CASE
+        }
+        return;
+    }
+    if (d.kernel == KERN_WIDE) {
+        if constexpr (sizeof(T) == 2) {
+#define CONVLOWER_WIDE_CASE(I)                                                           \
+    case I: {                                                                            \
+        constexpr TileVariant v = kWideVariants[I];                                      \
+        launch_dma_tile<T, v.bm, v.bn, v.bk, v.wgm, v.wgn, v.stages, true>(d, g, st); \
+        break;                                                                           \
+    }
+            switch (d.variant) {
+                CONVLOWER_WIDE_CASE(0)
+                CONVLOWER_WIDE_CASE(1)
+                CONVLOWER_WIDE_CASE(2)
+                CONVLOWER_WIDE_CASE(3)
+                CONVLOWER_WIDE_CASE(4)
+                CONVLOWER_WIDE_CASE(5)
+                CONVLOWER_WIDE_CASE(6)
+                CONVLOWER_WIDE_CASE(7)
+                CONVLOWER_WIDE_CASE(8)
+                default: break;
+            }
+#undef CONVLOWER_WIDE_CASE
+        }
+        return;
+    }
+    switch (d.variant) {
+        case 0: launch_gemm_tile<T, 128, 128, 32 / DIV, 2, 2>(d, g, st); break;
+        case 1: launch_gemm_tile<T, 128, 64, 32 / DIV, 2, 2>(d, g, st); break;
+        default: launch_gemm_tile<T, 128, 32, 32 / DIV, 4, 1>(d, g, st); break;
+    }
+}
+
+}  // namespace convlower

@@ -1,0 +1,7 @@
+// Contraction kernels for bf16 storage.
+#include "contract.hpp"
+
+namespace convlower {
+template void launch_gemm<__bf16>(const conv_desc&, const void*, const void*, const void*, void*, const void*,
+                              hipStream_t);
+}  // namespace convlower

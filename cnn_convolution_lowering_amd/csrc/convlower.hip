@@ -10,12 +10,12 @@
 
 #include <cstdint>
 #include <cstdlib>
+#include <cstring>
 #include <new>
+#include <string>
 
 #include "../../include/convlower.h"
-#include "igemm.hpp"
-#include "igemm_dma.hpp"
-#include "igemm_nchw.hpp"
+#include "dispatch.hpp"
 #include "lowering.hpp"
 
 using namespace convlower;
@@ -26,46 +26,7 @@ constexpr uint32_t kDescMagic = 0x636f6e76u;   // marks a live descriptor
 constexpr uint64_t kWsAlign = 256;             // workspace sub-buffer alignment (bytes)
 constexpr int kStageLdsBytes = 32 * 1024;      // NCHW staging tile budget per block
 
-enum TileId : int32_t {
-    TILE_128x128 = 0,
-    TILE_128x64 = 1,
-    TILE_128x32 = 2,
-    TILE_256x128 = 3,   // pipelined (LDS-DMA) kernel only
-    TILE_64x128 = 4,    // fp32 NCHW pipelined kernel only
-};
-
 }  // namespace
-
-// Variants of the fp32 NCHW fused kernel (BM, BN, BK, STAGES).  The default
-// per shape (see plan) follows a sweep of all of them on the encoder layers;
-// CONVLOWER_NCHW_VARIANT=<index> forces one, for tuning.
-struct NchwVariant {
-    int bm, bn, bk, stages;
-};
-constexpr NchwVariant kNchwVariants[] = {
-    {128, 32, 32, 3}, {128, 64, 32, 3}, {128, 128, 32, 3}, {64, 128, 32, 3},
-    {128, 64, 16, 4}, {128, 64, 16, 6}, {64, 64, 32, 4},  {64, 64, 16, 6},
-    {128, 32, 16, 4},
-};
-constexpr int kNchwVariantCount = sizeof(kNchwVariants) / sizeof(kNchwVariants[0]);
-
-struct conv_desc {
-    uint32_t magic;
-    conv_params_t p;
-    int64_t P, Q, M, Kg, W_used, RCp, Kl;
-    int32_t elem, vec;
-    bool elided;        // no lowering launch: the contraction reads x (implicit, or 1x1 NHWC unpadded)
-    bool pack;          // filter needs packing into ws
-    uint64_t off_filter, bytes_filter, off_low, bytes_low, ws_bytes;
-    uint64_t im2win_bytes, im2col_bytes;
-    int32_t tile;       // TileId
-    bool dma;           // pipelined LDS-DMA contraction kernel
-    bool nchw_dma;      // pipelined fp32 NCHW fused kernel
-    int32_t nchw_variant;   // index into kNchwVariants
-    int32_t tile_m, tile_n, tile_k;
-    // NCHW staging (0 = use the element-wise kernel)
-    int32_t stage_chunk, stage_ld;
-};
 
 namespace {
 
@@ -138,35 +99,78 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d) {
     const uint64_t a_bytes = d.elided ? x_bytes : d.bytes_low;
     const uint64_t b_bytes = uint64_t(p.K) * (implicit ? d.Kg : d.Kl) * e;
     const bool a_chunks = implicit ? (nhwc && c_vec) : true;
-    d.dma = a_chunks && a_bytes < (uint64_t(1) << 31) && b_bytes < (uint64_t(1) << 31);
-    // Tile: BN covers the output channels up to 128; BM = 256 where that still
-    // gives two workgroups per CU, else 128.
-    d.tile = p.K <= 32 ? TILE_128x32 : (p.K <= 64 ? TILE_128x64 : TILE_128x128);
-    if (d.dma && d.tile == TILE_128x128 && (d.M / 256) * ((p.K + 127) / 128) >= 512) d.tile = TILE_256x128;
+    const bool dma_ok = a_chunks && a_bytes < (uint64_t(1) << 31) && b_bytes < (uint64_t(1) << 31);
     // fp32 NCHW fused windows: the pipelined kernel with 4-byte window loads.
-    d.nchw_dma = implicit && !nhwc && p.dtype == CONV_F32 && x_bytes < (uint64_t(1) << 31) &&
-                 b_bytes < (uint64_t(1) << 31);
-    if (d.nchw_dma && d.tile == TILE_128x128 && (d.M / 128) * ((p.K + 127) / 128) < 512) d.tile = TILE_64x128;
-    d.tile_m = d.tile == TILE_256x128 ? 256 : (d.tile == TILE_64x128 ? 64 : 128);
-    d.tile_n = d.tile == TILE_128x32 ? 32 : (d.tile == TILE_128x64 ? 64 : 128);
-    d.tile_k = p.dtype == CONV_F32 ? 16 : 32;
-    // fp32 NCHW: narrow K -> 128-row tiles, 16-deep stages x4; wide K -> 64-row
-    // tiles, 64 or 128 channels wide depending on how many workgroups that gives.
-    if (p.K <= 32)
-        d.nchw_variant = 8;
-    else if (p.K <= 64)
-        d.nchw_variant = 4;
-    else
-        d.nchw_variant = (d.M / 64) * ((p.K + 127) / 128) >= 768 ? 3 : 7;
-    if (d.nchw_dma) {
-        // Tuning override: CONVLOWER_NCHW_VARIANT=<index> selects another compiled variant.
-        if (const char* v = std::getenv("CONVLOWER_NCHW_VARIANT")) {
-            const int i = std::atoi(v);
-            if (i >= 0 && i < kNchwVariantCount) d.nchw_variant = i;
+    const bool nchw_ok = implicit && !nhwc && p.dtype == CONV_F32 && x_bytes < (uint64_t(1) << 31) &&
+                         b_bytes < (uint64_t(1) << 31);
+    // 16-bit NHWC windows whose channels fill whole 32-element tile rows: the
+    // one-wave-per-SIMD wide-tile kernel.
+    const bool wide_ok = dma_ok && implicit && nhwc && p.dtype != CONV_F32 && p.C % 32 == 0;
+    // The strip kernel: the same operands, a filter at least two taps wide,
+    // and the input rows under a tile's pixels fitting its strip buffer.
+    auto strip_fits = [&](const StripVariant& v) {
+        const int64_t rows = (v.bm - 1) / d.Q + 2;
+        return wide_ok && p.S >= 2 && rows * d.W_used * 4 <= v.strip;
+    };
+    if (nchw_ok) {
+        // fp32 NCHW: narrow K -> 128-row tiles, 16-deep stages x4; wide K ->
+        // 64-row tiles, 64 or 128 channels wide depending on how many
+        // workgroups that gives.
+        d.kernel = KERN_NCHW;
+        if (p.K <= 32)
+            d.variant = 8;
+        else if (p.K <= 64)
+            d.variant = 4;
+        else
+            d.variant = (d.M / 64) * ((p.K + 127) / 128) >= 768 ? 3 : 7;
+    } else if (dma_ok) {
+        // BN covers the output channels up to 128; BM = 256 where that still
+        // gives two workgroups per CU, else 128.
+        d.kernel = KERN_DMA;
+        d.variant = p.K <= 32 ? 0 : (p.K <= 64 ? 1 : 2);
+        if (d.variant == 2 && (d.M / 256) * ((p.K + 127) / 128) >= 512) d.variant = 3;
+    } else {
+        d.kernel = KERN_REG;
+        d.variant = p.K <= 32 ? 2 : (p.K <= 64 ? 1 : 0);
+    }
+    // Tuning override: CONVLOWER_KERNEL="<kernel>:<variant>" with kernel one
+    // of reg, dma, wide, nchw, where that kernel takes this convolution.
+    if (const char* v = std::getenv("CONVLOWER_KERNEL")) {
+        const char* colon = std::strchr(v, ':');
+        if (colon) {
+            const std::string name(v, colon - v);
+            const int i = std::atoi(colon + 1);
+            if (name == "reg" && !nchw_ok && i >= 0 && i < count_of(kRegVariants)) {
+                d.kernel = KERN_REG;
+                d.variant = i;
+            } else if (name == "dma" && dma_ok && !nchw_ok && i >= 0 && i < count_of(kDmaVariants)) {
+                d.kernel = KERN_DMA;
+                d.variant = i;
+            } else if (name == "wide" && wide_ok && i >= 0 && i < count_of(kWideVariants) &&
+                       p.C % kWideVariants[i].bk == 0) {
+                d.kernel = KERN_WIDE;
+                d.variant = i;
+            } else if (name == "strip" && i >= 0 && i < count_of(kStripVariants) && strip_fits(kStripVariants[i])) {
+                d.kernel = KERN_STRIP;
+                d.variant = i;
+            } else if (name == "nchw" && nchw_ok && i >= 0 && i < count_of(kNchwVariants)) {
+                d.kernel = KERN_NCHW;
+                d.variant = i;
+            }
         }
-        d.tile_m = kNchwVariants[d.nchw_variant].bm;
-        d.tile_n = kNchwVariants[d.nchw_variant].bn;
-        d.tile_k = kNchwVariants[d.nchw_variant].bk;
+    }
+    if (d.kernel == KERN_STRIP) {
+        d.tile_m = kStripVariants[d.variant].bm;
+        d.tile_n = kStripVariants[d.variant].bn;
+        d.tile_k = 32;
+    } else {
+        const TileVariant& tv = d.kernel == KERN_NCHW ? kNchwVariants[d.variant]
+                                : d.kernel == KERN_WIDE ? kWideVariants[d.variant]
+                                : d.kernel == KERN_DMA  ? kDmaVariants[d.variant]
+                                                        : kRegVariants[d.variant];
+        d.tile_m = tv.bm;
+        d.tile_n = tv.bn;
+        d.tile_k = d.kernel == KERN_NCHW ? tv.bk : (p.dtype == CONV_F32 ? tv.bk / 2 : tv.bk);
     }
 
     // NCHW staging tile: whole strip columns of R*C values per LDS row.
@@ -294,187 +298,6 @@ void launch_lower(const conv_desc& d, const void* x, void* out, hipStream_t st) 
     }
 }
 
-template <typename T, int BM, int BN, int BK, int WGM, int WGN, bool NHWC_OUT, class ALoad, class BLoad>
-void launch_core(const conv_desc& d, GemmArgs g, hipStream_t st) {
-    g.tiles_n = int32_t((d.p.K + BN - 1) / BN);
-    const uint64_t tiles_m = (uint64_t(d.M) + BM - 1) / BM;
-    const uint32_t blocks = uint32_t(tiles_m * g.tiles_n);
-    conv_gemm_kernel<T, BM, BN, BK, WGM, WGN, NHWC_OUT, ALoad, BLoad><<<blocks, 256, 0, st>>>(g);
-}
-
-// Pick the loaders for the descriptor and launch one tile shape.
-template <typename T, int BM, int BN, int BK, int WGM, int WGN>
-void launch_gemm_tile(const conv_desc& d, const GemmArgs& g, hipStream_t st) {
-    constexpr int VEC = Vec<T>::n;
-    using BRows = StridedRows<T, BN, BK, false, false>;
-    using BRowsElem = StridedRows<T, BN, BK, false, true>;
-    const bool nhwc = d.p.layout == CONV_NHWC;
-    if (d.p.algo != CONV_ALGO_IMPLICIT) {
-        // lowered buffer (im2win strips / im2col rows) or 1x1 NHWC input in place
-        const bool seg = !d.elided && d.p.algo == CONV_ALGO_IM2WIN;
-        if (seg) {
-            using A = StridedRows<T, BM, BK, true, false>;
-            if (nhwc) launch_core<T, BM, BN, BK, WGM, WGN, true, A, BRows>(d, g, st);
-            else launch_core<T, BM, BN, BK, WGM, WGN, false, A, BRows>(d, g, st);
-        } else {
-            using A = StridedRows<T, BM, BK, false, false>;
-            if (nhwc) launch_core<T, BM, BN, BK, WGM, WGN, true, A, BRows>(d, g, st);
-            else launch_core<T, BM, BN, BK, WGM, WGN, false, A, BRows>(d, g, st);
-        }
-        return;
-    }
-    const bool b_vec = d.Kg % VEC == 0;
-    if (nhwc && d.p.C % VEC == 0) {
-        launch_core<T, BM, BN, BK, WGM, WGN, true, WindowVecNHWC<T, BM, BK>, BRows>(d, g, st);
-    } else if (nhwc) {
-        using A = WindowElem<T, BM, BK, true>;
-        if (b_vec) launch_core<T, BM, BN, BK, WGM, WGN, true, A, BRows>(d, g, st);
-        else launch_core<T, BM, BN, BK, WGM, WGN, true, A, BRowsElem>(d, g, st);
-    } else {
-        using A = WindowElem<T, BM, BK, false>;
-        if (b_vec) launch_core<T, BM, BN, BK, WGM, WGN, false, A, BRows>(d, g, st);
-        else launch_core<T, BM, BN, BK, WGM, WGN, false, A, BRowsElem>(d, g, st);
-    }
-}
-
-template <typename T, int BM, int BN, int BK, int WGM, int WGN, int STAGES, bool NHWC_OUT, class ASrc, class BSrc>
-void launch_dma_core(const conv_desc& d, GemmArgs g, hipStream_t st) {
-    g.tiles_n = int32_t((d.p.K + BN - 1) / BN);
-    const uint64_t tiles_m = (uint64_t(d.M) + BM - 1) / BM;
-    const uint32_t blocks = uint32_t(tiles_m * g.tiles_n);
-    conv_gemm_dma_kernel<T, BM, BN, BK, WGM, WGN, STAGES, NHWC_OUT, ASrc, BSrc><<<blocks, 256, 0, st>>>(g);
-}
-
-template <typename T, int BM, int BN, int BK, int WGM, int WGN, int STAGES>
-void launch_dma_tile(const conv_desc& d, const GemmArgs& g, hipStream_t st) {
-    using B = DmaRows<T, BN, BK, false, false>;
-    const bool nhwc = d.p.layout == CONV_NHWC;
-    if (d.p.algo == CONV_ALGO_IMPLICIT) {
-        // NHWC with C a whole number of vectors (checked when planning)
-        if (d.p.C % BK == 0)
-            launch_dma_core<T, BM, BN, BK, WGM, WGN, STAGES, true, DmaWindowNHWCBlocked<T, BM, BK>, B>(d, g, st);
-        else
-            launch_dma_core<T, BM, BN, BK, WGM, WGN, STAGES, true, DmaWindowNHWC<T, BM, BK>, B>(d, g, st);
-    } else if (!d.elided && d.p.algo == CONV_ALGO_IM2WIN) {
-        using A = DmaRows<T, BM, BK, true, true>;
-        if (nhwc) launch_dma_core<T, BM, BN, BK, WGM, WGN, STAGES, true, A, B>(d, g, st);
-        else launch_dma_core<T, BM, BN, BK, WGM, WGN, STAGES, false, A, B>(d, g, st);
-    } else {
-        using A = DmaRows<T, BM, BK, true, false>;
-        if (nhwc) launch_dma_core<T, BM, BN, BK, WGM, WGN, STAGES, true, A, B>(d, g, st);
-        else launch_dma_core<T, BM, BN, BK, WGM, WGN, STAGES, false, A, B>(d, g, st);
-    }
-}
-
-template <typename T>
-void launch_gemm(const conv_desc& d, const void* x, const void* w, const void* bias, void* y, const void* ws,
-                 hipStream_t st) {
-    constexpr int BK = sizeof(T) == 4 ? 16 : 32;
-    const char* wsb = static_cast<const char*>(ws);
-    GemmArgs g{};
-    g.b = d.pack ? static_cast<const void*>(wsb + d.off_filter) : w;
-    g.bias = bias;
-    g.y = y;
-    g.M = d.M;
-    g.K = int32_t(d.p.K);
-    g.PQ = int32_t(d.P * d.Q);
-    g.Q = int32_t(d.Q);
-    g.C = int32_t(d.p.C);
-    g.H = int32_t(d.p.H);
-    g.W = int32_t(d.p.W);
-    g.R = int32_t(d.p.R);
-    g.S = int32_t(d.p.S);
-    g.sh = d.p.stride_h;
-    g.sw = d.p.stride_w;
-    g.ph = d.p.pad_h;
-    g.pw = d.p.pad_w;
-    g.dh = d.p.dil_h;
-    g.dw = d.p.dil_w;
-    if (d.p.algo == CONV_ALGO_IMPLICIT) {
-        // windows gathered from x; filter rows in their own order
-        g.a = x;
-        g.Kc = int32_t(d.Kg);
-        g.ldb = int32_t(d.Kg);
-    } else if (d.elided) {
-        // 1x1, no padding, NHWC: row (n, p, q) is x[n][p*sh][q*sw][0..C)
-        g.a = x;
-        g.Kc = int32_t(d.Kl);
-        g.ldb = int32_t(d.Kl);
-        g.sN = d.p.H * d.p.W * d.p.C;
-        g.sP = int64_t(d.p.stride_h) * d.p.W * d.p.C;
-        g.sQ = int64_t(d.p.stride_w) * d.p.C;
-        g.RCp = int32_t(d.Kl);
-        g.sS = 0;
-    } else if (d.p.algo == CONV_ALGO_IM2WIN) {
-        g.a = wsb + d.off_low;
-        g.Kc = int32_t(d.Kl);
-        g.ldb = int32_t(d.Kl);
-        g.sP = d.W_used * d.RCp;
-        g.sN = d.P * g.sP;
-        g.sQ = int64_t(d.p.stride_w) * d.RCp;
-        g.RCp = int32_t(d.RCp);
-        g.sS = int32_t(int64_t(d.p.dil_w) * d.RCp);
-    } else {
-        g.a = wsb + d.off_low;
-        g.Kc = int32_t(d.Kl);
-        g.ldb = int32_t(d.Kl);
-        g.sQ = d.Kl;
-        g.sP = d.Q * d.Kl;
-        g.sN = d.P * g.sP;
-        g.RCp = int32_t(d.Kl);
-        g.sS = 0;
-    }
-    if (d.nchw_dma) {
-        if constexpr (sizeof(T) == 4) {
-            auto launch = [&](auto kernel, int BM, int BN) {
-                GemmArgs h = g;
-                h.tiles_n = int32_t((d.p.K + BN - 1) / BN);
-                const uint32_t blocks = uint32_t(((uint64_t(d.M) + BM - 1) / BM) * h.tiles_n);
-                kernel<<<blocks, 256, 0, st>>>(h);
-            };
-            const bool mask = d.p.R * d.p.S <= 32;
-#define CONVLOWER_NCHW_CASE(I, BM, BN, BK, ST)                                                     \
-    case I:                                                                                        \
-        if (mask) launch(conv_nchw_f32_dma_kernel<BM, BN, BK, 2, 2, ST, true>, BM, BN);           \
-        else launch(conv_nchw_f32_dma_kernel<BM, BN, BK, 2, 2, ST, false>, BM, BN);               \
-        break;
-            switch (d.nchw_variant) {
-                case 0:
-                    if (mask) launch(conv_nchw_f32_dma_kernel<128, 32, 32, 4, 1, 3, true>, 128, 32);
-                    else launch(conv_nchw_f32_dma_kernel<128, 32, 32, 4, 1, 3, false>, 128, 32);
-                    break;
-                CONVLOWER_NCHW_CASE(1, 128, 64, 32, 3)
-                CONVLOWER_NCHW_CASE(2, 128, 128, 32, 3)
-                CONVLOWER_NCHW_CASE(3, 64, 128, 32, 3)
-                CONVLOWER_NCHW_CASE(4, 128, 64, 16, 4)
-                CONVLOWER_NCHW_CASE(5, 128, 64, 16, 6)
-                CONVLOWER_NCHW_CASE(6, 64, 64, 32, 4)
-                CONVLOWER_NCHW_CASE(7, 64, 64, 16, 6)
-                case 8:
-                    if (mask) launch(conv_nchw_f32_dma_kernel<128, 32, 16, 4, 1, 4, true>, 128, 32);
-                    else launch(conv_nchw_f32_dma_kernel<128, 32, 16, 4, 1, 4, false>, 128, 32);
-                    break;
-                default: break;
-            }
-#undef CONVLOWER_NCHW_CASE
-        }
-        return;
-    }
-    if (d.dma) {
-        switch (d.tile) {
-            case TILE_256x128: launch_dma_tile<T, 256, 128, BK, 2, 2, 3>(d, g, st); break;
-            case TILE_128x128: launch_dma_tile<T, 128, 128, BK, 2, 2, 4>(d, g, st); break;
-            case TILE_128x64: launch_dma_tile<T, 128, 64, BK, 2, 2, 4>(d, g, st); break;
-            default: launch_dma_tile<T, 128, 32, BK, 4, 1, 4>(d, g, st); break;
-        }
-        return;
-    }
-    switch (d.tile) {
-        case TILE_128x128: launch_gemm_tile<T, 128, 128, BK, 2, 2>(d, g, st); break;
-        case TILE_128x64: launch_gemm_tile<T, 128, 64, BK, 2, 2>(d, g, st); break;
-        default: launch_gemm_tile<T, 128, 32, BK, 4, 1>(d, g, st); break;
-    }
-}
 
 template <template <typename> class F, typename... Args>
 void by_dtype(conv_dtype_t dt, Args&&... args) {
@@ -594,6 +417,8 @@ conv_status_t conv_plan_info(conv_desc_t d, conv_plan_info_t* info) {
     i.tile_n = d->tile_n;
     i.tile_k = d->tile_k;
     i.elem_bytes = d->elem;
+    i.kernel = d->kernel;
+    i.kernel_variant = d->variant;
     *info = i;
     return CONV_OK;
 }

@@ -1,0 +1,91 @@
+// Library-internal descriptor and kernel tables, shared by the host planner
+// (convlower.hip) and the per-dtype contraction launchers (contract_*.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "../../include/convlower.h"
+
+// Contraction kernels.
+enum KernelId : int32_t {
+    KERN_REG = 0,    // register-staged, double-buffered LDS (any A side)
+    KERN_DMA = 1,    // LDS-DMA ring, two waves per SIMD (16-byte chunk A sides)
+    KERN_WIDE = 2,   // LDS-DMA ring, one wave per SIMD, wide register tiles (16-bit, NHWC windows)
+    KERN_NCHW = 3,   // fp32 NCHW windows by 4-byte LDS-DMA
+    KERN_STRIP = 4,  // input row strips staged in LDS once per filter row (16-bit, NHWC, C % 32 == 0, S >= 2)
+};
+
+// One compiled tile shape: BM x BN output tile, BK-deep LDS stages (in 16-bit
+// elements; fp32 uses BK/2, the same bytes per row), WGM x WGN waves, STAGES
+// LDS stages (0 for the register-staged kernel).
+struct TileVariant {
+    int bm, bn, bk, wgm, wgn, stages;
+};
+
+constexpr TileVariant kRegVariants[] = {
+    {128, 128, 32, 2, 2, 0}, {128, 64, 32, 2, 2, 0}, {128, 32, 32, 4, 1, 0},
+};
+constexpr TileVariant kDmaVariants[] = {
+    {128, 32, 32, 4, 1, 4}, {128, 64, 32, 2, 2, 4}, {128, 128, 32, 2, 2, 4}, {256, 128, 32, 2, 2, 3},
+    {256, 128, 32, 4, 2, 4}, {256, 256, 32, 4, 2, 3}, {128, 128, 64, 2, 2, 2},
+};
+constexpr TileVariant kWideVariants[] = {
+    {512, 128, 32, 4, 1, 4}, {512, 128, 32, 4, 1, 3}, {256, 256, 32, 2, 2, 3}, {256, 256, 32, 2, 2, 4},
+    {256, 128, 32, 2, 2, 4}, {128, 128, 32, 2, 2, 4}, {256, 128, 32, 2, 1, 3}, {256, 128, 64, 2, 2, 3},
+    {128, 256, 32, 2, 2, 4},
+};
+// fp32 NCHW kernel: BK in fp32 elements, 2 x 2 waves except where noted in
+// its launcher (BN = 32 uses 4 x 1).
+constexpr TileVariant kNchwVariants[] = {
+    {128, 32, 32, 4, 1, 3}, {128, 64, 32, 2, 2, 3}, {128, 128, 32, 2, 2, 3}, {64, 128, 32, 2, 2, 3},
+    {128, 64, 16, 2, 2, 4}, {128, 64, 16, 2, 2, 6}, {64, 64, 32, 2, 2, 4},  {64, 64, 16, 2, 2, 6},
+    {128, 32, 16, 4, 1, 4},
+};
+// Strip-staged kernel: BM x BN tile, WGM x WGN waves, STRIP 16-byte chunk
+// slots per strip buffer (bounds (ceil-ish BM/Q + 1) * W_used * 4), BST
+// filter stages.
+struct StripVariant {
+    int bm, bn, wgm, wgn, strip, bst;
+};
+constexpr StripVariant kStripVariants[] = {
+    {512, 128, 4, 1, 2816, 4}, {256, 128, 2, 2, 1536, 4}, {256, 256, 2, 2, 1536, 4},
+    {128, 128, 2, 2, 1024, 4}, {128, 256, 2, 2, 1024, 4},
+};
+template <class V, int N>
+constexpr int count_of(const V (&)[N]) {
+    return N;
+}
+
+struct conv_desc {
+    uint32_t magic;
+    conv_params_t p;
+    int64_t P, Q, M, Kg, W_used, RCp, Kl;
+    int32_t elem, vec;
+    bool elided;        // no lowering launch: the contraction reads x (implicit, or 1x1 NHWC unpadded)
+    bool pack;          // filter needs packing into ws
+    uint64_t off_filter, bytes_filter, off_low, bytes_low, ws_bytes;
+    uint64_t im2win_bytes, im2col_bytes;
+    int32_t kernel;     // KernelId
+    int32_t variant;    // index into that kernel's variant table
+    int32_t tile_m, tile_n, tile_k;
+    // NCHW staging (0 = use the element-wise kernel)
+    int32_t stage_chunk, stage_ld;
+};
+
+namespace convlower {
+
+// Enqueue the contraction (with its fused epilogue) for storage type T.
+template <typename T>
+void launch_gemm(const conv_desc& d, const void* x, const void* w, const void* bias, void* y, const void* ws,
+                 hipStream_t st);
+
+extern template void launch_gemm<float>(const conv_desc&, const void*, const void*, const void*, void*,
+                                        const void*, hipStream_t);
+extern template void launch_gemm<_Float16>(const conv_desc&, const void*, const void*, const void*, void*,
+                                           const void*, hipStream_t);
+extern template void launch_gemm<__bf16>(const conv_desc&, const void*, const void*, const void*, void*,
+                                         const void*, hipStream_t);
+
+}  // namespace convlower

@@ -104,10 +104,21 @@ __device__ __forceinline__ void decode_m(const GemmArgs& g, int32_t m, int32_t& 
 // index with ((row >> 1) & 3), scaled to keep chunk pairs together in
 // 128-byte rows, separates them, and keeps the row-major tile writes (8
 // lanes covering 128 contiguous bytes) conflict-free as well.
-template <int CPR>
+//
+// SWZ = 1 is the variant for 32 x 32 fragments (lane l: row l%32, chunk
+// l/32): one read cycle then covers rows 0-7 and 16-23 (or 8-15 and 24-31) of
+// a single chunk, so rows 16 apart must land on different banks as well as
+// rows 4 (64-byte rows) or 2 (128-byte rows) apart; the XOR takes bits 2 and
+// 4 of the row (64-byte rows) or bits 1, 2 and 4 (128-byte rows).  It depends
+// on row bits 0-4 only, like SWZ = 0.
+template <int CPR, int SWZ = 0>
 __device__ __forceinline__ int swz_chunk(int row, int chunk) {
     static_assert(CPR == 4 || CPR == 8, "tile rows of 64 or 128 bytes");
-    return CPR == 4 ? (chunk ^ ((row >> 1) & 3)) : (chunk ^ (((row >> 1) & 3) << 1));
+    if constexpr (SWZ == 0)
+        return CPR == 4 ? (chunk ^ ((row >> 1) & 3)) : (chunk ^ (((row >> 1) & 3) << 1));
+    else
+        return CPR == 4 ? (chunk ^ (((row >> 2) & 1) | (((row >> 4) & 1) << 1)))
+                        : (chunk ^ (((row >> 1) & 3) | (((row >> 4) & 1) << 2)));
 }
 
 // ---------------------------------------------------------------------------

@@ -71,11 +71,12 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" : : : "memory"); }
 
-// Swizzle mask of a thread's rows: for CPR chunks per row, thread t fills
-// rows j*(256/CPR) + t/CPR, whose swizzle depends on t/CPR only.
-template <int CPR>
+// Swizzle mask of a thread's rows: for CPR chunks per row and NT threads,
+// thread t fills rows j*(NT/CPR) + t/CPR, whose swizzle depends on t/CPR only
+// (NT/CPR is a multiple of 8).
+template <int CPR, int SWZ>
 __device__ __forceinline__ int dma_chunk(int tid) {
-    return swz_chunk<CPR>(tid / CPR, tid % CPR);
+    return swz_chunk<CPR, SWZ>(tid / CPR, tid % CPR);
 }
 
 // ---------------------------------------------------------------------------
@@ -86,13 +87,13 @@ __device__ __forceinline__ int dma_chunk(int tid) {
 // Window of each output pixel gathered from NHWC x (C a multiple of VEC),
 // contraction order (r, s, c).  Offsets are relative to the first image of
 // the tile, so only that image range needs 32-bit offsets.
-template <typename T, int ROWS, int BK>
+template <typename T, int ROWS, int BK, int NT, int SWZ = 0>
 struct DmaWindowNHWC {
     static constexpr int VEC = Vec<T>::n;
     static constexpr int CPR = BK / VEC;
-    static constexpr int NL = ROWS * CPR / 256;     // loads per thread per tile
-    static constexpr int RSTEP = 256 / CPR;         // row distance between a thread's loads
-    static_assert(ROWS * CPR % 256 == 0, "whole wave loads");
+    static constexpr int NL = ROWS * CPR / NT;      // loads per thread per tile
+    static constexpr int RSTEP = NT / CPR;          // row distance between a thread's loads
+    static_assert(ROWS * CPR % NT == 0, "whole wave loads");
     uint32_t nbase[NL];   // byte offset of the row's image
     int32_t h0[NL], w0[NL];
     bool ok[NL];
@@ -118,7 +119,7 @@ struct DmaWindowNHWC {
             h0[j] = p * g.sh - g.ph;
             w0[j] = q * g.sw - g.pw;
         }
-        kk = dma_chunk<CPR>(tid) * VEC;
+        kk = dma_chunk<CPR, SWZ>(tid) * VEC;
         c0 = kk % g.C;
         const int rs = kk / g.C;
         s = rs % g.S;
@@ -147,13 +148,13 @@ struct DmaWindowNHWC {
 // one kernel tap (r, s) for every lane, so the tap and channel block are
 // wave-uniform (scalar registers) and each load's offset is one add from a
 // per-row base, two range checks and a select.
-template <typename T, int ROWS, int BK>
+template <typename T, int ROWS, int BK, int NT, int SWZ = 0>
 struct DmaWindowNHWCBlocked {
     static constexpr int VEC = Vec<T>::n;
     static constexpr int CPR = BK / VEC;
-    static constexpr int NL = ROWS * CPR / 256;
-    static constexpr int RSTEP = 256 / CPR;
-    static_assert(ROWS * CPR % 256 == 0, "whole wave loads");
+    static constexpr int NL = ROWS * CPR / NT;
+    static constexpr int RSTEP = NT / CPR;
+    static_assert(ROWS * CPR % NT == 0, "whole wave loads");
     int32_t rowbase[NL];  // bytes: image base + (h0*W + w0)*C, plus this lane's channel chunk
     int32_t h0[NL], w0[NL];
     int cb, s, rr, kk;    // uniform: channel block start, tap, contraction position
@@ -167,7 +168,7 @@ struct DmaWindowNHWCBlocked {
         const int64_t n_imgs = g.M / g.PQ;
         const int64_t bytes = (n_imgs - n_first) * img * int64_t(sizeof(T));
         rsrc = make_rsrc(base, uint32_t(bytes < int64_t(0x7fffffff) ? bytes : int64_t(0x7fffffff)));
-        const int chunk = dma_chunk<CPR>(tid);
+        const int chunk = dma_chunk<CPR, SWZ>(tid);
 #pragma unroll
         for (int j = 0; j < NL; ++j) {
             const int64_t m = row0 + j * RSTEP + tid / CPR;
@@ -206,13 +207,13 @@ struct DmaWindowNHWCBlocked {
 
 // Rows of a strided matrix: lowered pixel rows (SEGMENTED for im2win strips)
 // or filter rows.  Offsets are relative to the tile's first row.
-template <typename T, int ROWS, int BK, bool PIXELS, bool SEGMENTED>
+template <typename T, int ROWS, int BK, bool PIXELS, bool SEGMENTED, int NT, int SWZ = 0>
 struct DmaRows {
     static constexpr int VEC = Vec<T>::n;
     static constexpr int CPR = BK / VEC;
-    static constexpr int NL = (ROWS * CPR + 255) / 256;
-    static constexpr int RSTEP = 256 / CPR;
-    static_assert(ROWS * CPR % 256 == 0 || ROWS * CPR < 256, "whole wave loads");
+    static constexpr int NL = (ROWS * CPR + NT - 1) / NT;
+    static constexpr int RSTEP = NT / CPR;
+    static_assert(ROWS * CPR % NT == 0 || ROWS * CPR < NT, "whole wave loads");
     uint32_t roff[NL];    // row start, bytes from the tile base
     bool ok[NL];
     int kk, t;
@@ -243,7 +244,7 @@ struct DmaRows {
             ok[j] = (j * RSTEP + tid / CPR < ROWS) && row < nrows;
             roff[j] = uint32_t((row_offset(g, ok[j] ? row : first) - off0) * int64_t(sizeof(T)));
         }
-        kk = dma_chunk<CPR>(tid) * VEC;
+        kk = dma_chunk<CPR, SWZ>(tid) * VEC;
         if (SEGMENTED) {
             t = kk % g.RCp;
             seg = uint32_t(int64_t(kk / g.RCp) * g.sS * int64_t(sizeof(T)));
@@ -268,22 +269,27 @@ struct DmaRows {
 };
 
 // ---------------------------------------------------------------------------
+// NT = 64*WGM*WGN threads (4 or 8 waves); two waves per SIMD either way
+// (two 4-wave or one 8-wave workgroup per CU).
 template <typename T, int BM, int BN, int BK, int WGM, int WGN, int STAGES, bool NHWC_OUT, class ASrc, class BSrc>
-__global__ void __launch_bounds__(256, 2) conv_gemm_dma_kernel(GemmArgs g) {
+__global__ void __launch_bounds__(64 * WGM * WGN, 8 / (WGM * WGN)) conv_gemm_dma_kernel(GemmArgs g) {
+    constexpr int NT = 64 * WGM * WGN;
+    constexpr int NW = WGM * WGN;
     constexpr int VEC = Vec<T>::n;
     constexpr int CPR = BK / VEC;
     constexpr int WM = BM / WGM, WN = BN / WGN;
     constexpr int TM = WM / 16, TN = WN / 16;
     constexpr int KB = 4 * VEC;
     constexpr int STAGE_ELEMS = (BM + BN) * BK;
-    // DMA loads per thread per tile.  A narrow B tile (fewer than 256 chunks)
+    // DMA loads per thread per tile.  A narrow B tile (fewer than NT chunks)
     // is loaded by the first waves only, so the other waves issue fewer loads
     // and must wait with their own count.
-    constexpr int B_WAVES = BN * CPR >= 256 ? 4 : (BN * CPR) / 64;
+    constexpr int B_WAVES = BN * CPR >= NT ? NW : (BN * CPR) / 64;
     constexpr int NLOADS = ASrc::NL + BSrc::NL;
     constexpr int NLOADS_NO_B = ASrc::NL;
-    static_assert(BN * CPR >= 256 || (BN * CPR) % 64 == 0, "B tile in whole wave loads");
-    static_assert(WGM * WGN == 4 && BK % KB == 0 && WM % 16 == 0 && WN % 16 == 0, "tile shape");
+    static_assert(BM * CPR % NT == 0, "A tile in whole workgroup loads");
+    static_assert(BN * CPR >= NT || (BN * CPR) % 64 == 0, "B tile in whole wave loads");
+    static_assert((NW == 4 || NW == 8) && BK % KB == 0 && WM % 16 == 0 && WN % 16 == 0, "tile shape");
     static_assert(STAGES >= 2, "at least double buffering");
 
     __shared__ __attribute__((aligned(16))) T smem[STAGES * STAGE_ELEMS];
@@ -304,15 +310,15 @@ __global__ void __launch_bounds__(256, 2) conv_gemm_dma_kernel(GemmArgs g) {
 
     const uint32_t lds0 = lds_offset(smem);
     // Issue one tile's loads into stage `st`: load j of wave w covers LDS chunk
-    // slots [j*256 + w*64, +64) of the A (then B) region.
+    // slots [j*NT + w*64, +64) of the A (then B) region.
     auto issue = [&](int st) {
         const uint32_t a_base = lds0 + uint32_t(st * STAGE_ELEMS * sizeof(T));
         const uint32_t b_base = a_base + uint32_t(BM * BK * sizeof(T));
 #pragma unroll
-        for (int j = 0; j < ASrc::NL; ++j) dma16(la.rsrc, la.voff(g, j), a_base + uint32_t((j * 256 + wave * 64) * 16));
+        for (int j = 0; j < ASrc::NL; ++j) dma16(la.rsrc, la.voff(g, j), a_base + uint32_t((j * NT + wave * 64) * 16));
 #pragma unroll
         for (int j = 0; j < BSrc::NL; ++j) {
-            if (wave < B_WAVES) dma16(lb.rsrc, lb.voff(g, j), b_base + uint32_t((j * 256 + wave * 64) * 16));
+            if (wave < B_WAVES) dma16(lb.rsrc, lb.voff(g, j), b_base + uint32_t((j * NT + wave * 64) * 16));
         }
         la.next(g);
         lb.next(g);

@@ -111,6 +111,11 @@ typedef struct {
     int32_t lowering_elided;   /* 1: x is read in place (1x1 NHWC, no padding) */
     int32_t tile_m, tile_n, tile_k;  /* contraction tile chosen for this shape */
     int32_t elem_bytes;
+    /* contraction kernel: 0 register-staged tiles, 1 LDS-DMA pipeline (two
+     * waves per SIMD), 2 LDS-DMA pipeline with one wave per SIMD and 32x32
+     * MFMA tiles, 3 fp32 NCHW windows, 4 input row strips staged in LDS;
+     * kernel_variant indexes that kernel's compiled tile shapes */
+    int32_t kernel, kernel_variant;
 } conv_plan_info_t;
 
 /* Validate *p and build a descriptor.  Host only: no HIP call is made, so it

@@ -41,8 +41,8 @@ def test_exports_every_header_function():
 def test_struct_sizes_match_header():
     # conv_params_t: 7 int64 + 6 int32 + 3 enums (int) -> 92 bytes, padded to 96
     assert ctypes.sizeof(cl.ConvParams) == 96
-    # conv_plan_info_t: 7 int64 + 7 uint64 + 5 int32 -> 132, padded to 136
-    assert ctypes.sizeof(cl.PlanInfo) == 136
+    # conv_plan_info_t: 7 int64 + 7 uint64 + 7 int32 -> 140, padded to 144
+    assert ctypes.sizeof(cl.PlanInfo) == 144
 
 
 @pytest.mark.parametrize("field,value", [
@@ -224,3 +224,30 @@ def test_elided_layers_use_no_lowering_workspace():
     assert c.info["lowering_elided"] == 1 and c.workspace_bytes == 0
     c = cl.Conv2d(32, 128, 64, 64, 128, 1, 1, layout="nhwc", dtype="f16", algo="im2col")
     assert c.workspace_bytes == 0
+
+
+def test_kernel_override_is_host_only_and_checked(monkeypatch):
+    """CONVLOWER_KERNEL forces a compiled kernel variant only where that kernel
+    takes the shape; otherwise (or when malformed) the planner's choice stays."""
+    def plan(**kw):
+        args = dict(N=2, C=64, H=17, W=17, K=72, R=3, S=3, padding=1, layout="nhwc", dtype="f16", algo="implicit")
+        args.update(kw)
+        N, C, H, W, K, R, S = (args.pop(k) for k in ("N", "C", "H", "W", "K", "R", "S"))
+        d = cl.Conv2d(N, C, H, W, K, R, S, **args)
+        return d.info["kernel"], d.info["kernel_variant"], d.info["tile_m"], d.info["tile_n"]
+
+    monkeypatch.delenv("CONVLOWER_KERNEL", raising=False)
+    default = plan()
+    monkeypatch.setenv("CONVLOWER_KERNEL", "strip:0")
+    assert plan()[:3] == (4, 0, 512)
+    assert plan(R=1, S=1, padding=0)[0] != 4       # a single tap: nothing to share
+    assert plan(C=48)[0] != 4                       # C not a multiple of 32
+    assert plan(dtype="f32")[0] != 4                # 16-bit only
+    monkeypatch.setenv("CONVLOWER_KERNEL", "wide:2")
+    assert plan()[:4] == (2, 2, 256, 256)
+    monkeypatch.setenv("CONVLOWER_KERNEL", "nchw:1")
+    assert plan()[0] != 3                           # fp32 NCHW only
+    assert plan(layout="nchw", dtype="f32")[:2] == (3, 1)
+    for bad in ("strip", "strip:99", "bogus:1", ":", "dma:-1"):
+        monkeypatch.setenv("CONVLOWER_KERNEL", bad)
+        assert plan() == default

@@ -1,0 +1,118 @@
+"""GPU parity of every compiled contraction kernel and tile variant.
+
+The planner picks one kernel per shape; CONVLOWER_KERNEL="<kernel>:<variant>"
+forces another one that takes the shape.  Each variant runs here on shapes
+with ragged pixel and channel tiles, strides, dilation and padding, against
+the fp64 reference, to the same per-element bound as the default path.
+"""
+from __future__ import annotations
+
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import cnn_convolution_lowering_amd as cl
+import oracle
+from parity import TORCH_DT, assert_parity, to_f64
+
+pytestmark = pytest.mark.gpu
+
+# kernel name -> (plan_info kernel id, number of compiled variants)
+KERNELS = {"reg": (0, 3), "dma": (1, 7), "wide": (2, 9), "nchw": (3, 9), "strip": (4, 5)}
+
+# (N, C, H, W, K, R, S, stride, pad, dilation)
+SHAPES_C32 = [
+    (2, 64, 17, 17, 72, 3, 3, (1, 1), (1, 1), (1, 1)),
+    (1, 32, 20, 13, 130, 2, 4, (2, 1), (1, 2), (1, 1)),
+    (3, 96, 9, 9, 40, 3, 3, (1, 1), (2, 2), (2, 2)),
+    (1, 32, 70, 70, 128, 5, 5, (1, 1), (2, 2), (1, 1)),
+    (2, 128, 14, 14, 256, 3, 3, (1, 1), (1, 1), (1, 1)),
+]
+SHAPES_SMALL_C = [
+    (2, 3, 30, 30, 32, 3, 3, (1, 1), (1, 1), (1, 1)),
+    (3, 8, 15, 11, 70, 2, 3, (2, 1), (0, 1), (1, 2)),
+    (2, 16, 9, 9, 130, 3, 3, (2, 2), (0, 0), (1, 1)),
+]
+# (kernel, dtype, layout, algo, shapes)
+PLANS = [
+    ("reg", "f32", "nhwc", "implicit", SHAPES_SMALL_C + SHAPES_C32[:2]),
+    ("reg", "f16", "nchw", "implicit", SHAPES_SMALL_C[:2]),
+    ("dma", "f16", "nhwc", "implicit", SHAPES_C32[:3] + SHAPES_SMALL_C[1:]),
+    ("dma", "bf16", "nhwc", "im2win", SHAPES_C32[:2] + SHAPES_SMALL_C[:1]),
+    ("dma", "f32", "nhwc", "implicit", SHAPES_C32[:2] + SHAPES_SMALL_C[1:2]),
+    ("dma", "f32", "nchw", "im2col", SHAPES_SMALL_C[:2]),
+    ("wide", "f16", "nhwc", "implicit", SHAPES_C32),
+    ("wide", "bf16", "nhwc", "implicit", SHAPES_C32[:3]),
+    ("nchw", "f32", "nchw", "implicit", SHAPES_SMALL_C + SHAPES_C32[:2]),
+    ("strip", "f16", "nhwc", "implicit", SHAPES_C32),
+    ("strip", "bf16", "nhwc", "implicit", SHAPES_C32[:3]),
+]
+
+
+def _cases():
+    out = []
+    for kind, dt, lay, algo, shapes in PLANS:
+        for v in range(KERNELS[kind][1]):
+            out.append((kind, v, dt, lay, algo, shapes))
+    return out
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    cl.load_library()
+    return torch.device("cuda:0")
+
+
+def _perm(t, lay):
+    return t.permute(0, 2, 3, 1).contiguous() if lay == "nhwc" else t.contiguous()
+
+
+@pytest.mark.parametrize("case", _cases(), ids=lambda c: "%s%d-%s-%s-%s" % c[:5])
+def test_forced_kernel_parity(dev, monkeypatch, case):
+    kind, v, dt, lay, algo, shapes = case
+    kid = KERNELS[kind][0]
+    monkeypatch.setenv("CONVLOWER_KERNEL", "%s:%d" % (kind, v))
+    ran = 0
+    for si, (N, C, H, W, K, R, S, st, pd, dl) in enumerate(shapes):
+        d = cl.Conv2d(N, C, H, W, K, R, S, stride=st, padding=pd, dilation=dl, layout=lay, dtype=dt, algo=algo)
+        if d.info["kernel"] != kid or d.info["kernel_variant"] != v:
+            continue      # this variant does not take the shape
+        g = torch.Generator().manual_seed(300 + 17 * v + si)
+        x = (torch.rand(N, C, H, W, generator=g) * 2 - 1).to(TORCH_DT[dt])
+        w = (torch.randn(K, C, R, S, generator=g) / np.sqrt(C * R * S)).to(TORCH_DT[dt])
+        b = (torch.randn(K, generator=g) * 0.1).to(TORCH_DT[dt])
+        xl, wl = _perm(x, lay), _perm(w, lay)
+        print("case %s:%d %s %s %s shape %s" % (kind, v, dt, lay, algo, shapes[si]), flush=True)
+        sys.stdout.flush()
+        y = d.forward(xl.to(dev), wl.to(dev), b.to(dev))
+        torch.cuda.synchronize()
+        ref, yabs = oracle.conv2d(xl, wl, b, layout=lay, stride=st, padding=pd, dilation=dl, with_abs=True)
+        assert_parity(to_f64(y.cpu()), ref, yabs, dt, "%s:%d shape %d" % (kind, v, si))
+        ran += 1
+    assert ran > 0, "no listed shape is taken by %s:%d" % (kind, v)
+
+
+def test_forced_kernel_integer_exact(dev, monkeypatch):
+    """Integer inputs through the strip and wide kernels: exact fp32 sums, so
+    the result is the reference rounded once to fp16, bit for bit."""
+    N, C, H, W, K, R, S = 2, 64, 12, 12, 96, 3, 3
+    g = torch.Generator().manual_seed(77)
+    x = torch.randint(-2, 3, (N, C, H, W), generator=g).to(torch.float16)
+    w = torch.randint(-2, 3, (K, C, R, S), generator=g).to(torch.float16)
+    b = torch.randint(-4, 5, (K,), generator=g).to(torch.float16)
+    xl, wl = _perm(x, "nhwc"), _perm(w, "nhwc")
+    ref = oracle.conv2d(xl, wl, b, layout="nhwc", stride=1, padding=1)
+    want = torch.from_numpy(ref).to(torch.float32).to(torch.float16)
+    for forced in ("strip:0", "strip:2", "strip:3", "wide:0", "wide:5"):
+        monkeypatch.setenv("CONVLOWER_KERNEL", forced)
+        d = cl.Conv2d(N, C, H, W, K, R, S, padding=1, layout="nhwc", dtype="f16", algo="implicit")
+        assert d.info["kernel"] == KERNELS[forced.split(":")[0]][0], forced
+        print("int case %s" % forced, flush=True)
+        y = d.forward(xl.to(dev), wl.to(dev), b.to(dev))
+        torch.cuda.synchronize()
+        assert torch.equal(y.cpu().view(torch.int16), want.view(torch.int16)), forced
