@@ -10,6 +10,7 @@
 #include "igemm_dma.hpp"
 #include "igemm_nchw.hpp"
 #include "igemm_strip.hpp"
+#include "igemm_strip_rb.hpp"
 #include "igemm_wide.hpp"
 
 namespace convlower {
@@ -113,7 +114,7 @@ void launch_gemm(const conv_desc& d, const void* x, const void* w, const void* b
                  hipStream_t st) {
     const char* wsb = static_cast<const char*>(ws);
     GemmArgs g{};
-    g.b = d.pack ? static_cast<const void*>(wsb + d.off_filter) : w;
+    g.b = (d.pack || d.frag_pack) ? static_cast<const void*>(wsb + d.off_filter) : w;
     g.bias = bias;
     g.y = y;
     g.M = d.M;
@@ -217,6 +218,29 @@ void launch_gemm(const conv_desc& d, const void* x, const void* w, const void* b
             default: break;
         }
 #undef CONVLOWER_DMA_CASE
+        return;
+    }
+    if (d.kernel == KERN_STRIP_RB) {
+        if constexpr (sizeof(T) == 2) {
+#define CONVLOWER_STRIP_RB_CASE(I)                                                                            \
+    case I: {                                                                                                 \
+        constexpr StripVariant v = kStripRbVariants[I];                                                       \
+        GemmArgs h = g;                                                                                       \
+        h.tiles_n = int32_t((d.p.K + v.bn - 1) / v.bn);                                                       \
+        const uint32_t blocks = uint32_t(((uint64_t(d.M) + v.bm - 1) / v.bm) * h.tiles_n);                   \
+        conv_strip_rb_kernel<T, v.bm, v.bn, v.wgm, v.wgn, v.strip, v.bst><<<blocks, 64 * v.wgm * v.wgn, 0, st>>>(h); \
+        break;                                                                                                \
+    }
+            switch (d.variant) {
+                CONVLOWER_STRIP_RB_CASE(0)
+                CONVLOWER_STRIP_RB_CASE(1)
+                CONVLOWER_STRIP_RB_CASE(2)
+                CONVLOWER_STRIP_RB_CASE(3)
+                CONVLOWER_STRIP_RB_CASE(4)
+                default: break;
+            }
+#undef CONVLOWER_STRIP_RB_CASE
+        }
         return;
     }
     if (d.kernel == KERN_STRIP) {

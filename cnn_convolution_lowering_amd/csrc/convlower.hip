@@ -153,15 +153,20 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d) {
             } else if (name == "strip" && i >= 0 && i < count_of(kStripVariants) && strip_fits(kStripVariants[i])) {
                 d.kernel = KERN_STRIP;
                 d.variant = i;
+            } else if (name == "striprb" && i >= 0 && i < count_of(kStripRbVariants) &&
+                       strip_fits(kStripRbVariants[i])) {
+                d.kernel = KERN_STRIP_RB;
+                d.variant = i;
             } else if (name == "nchw" && nchw_ok && i >= 0 && i < count_of(kNchwVariants)) {
                 d.kernel = KERN_NCHW;
                 d.variant = i;
             }
         }
     }
-    if (d.kernel == KERN_STRIP) {
-        d.tile_m = kStripVariants[d.variant].bm;
-        d.tile_n = kStripVariants[d.variant].bn;
+    if (d.kernel == KERN_STRIP || d.kernel == KERN_STRIP_RB) {
+        const StripVariant& sv = d.kernel == KERN_STRIP ? kStripVariants[d.variant] : kStripRbVariants[d.variant];
+        d.tile_m = sv.bm;
+        d.tile_n = sv.bn;
         d.tile_k = 32;
     } else {
         const TileVariant& tv = d.kernel == KERN_NCHW ? kNchwVariants[d.variant]
@@ -171,6 +176,15 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d) {
         d.tile_m = tv.bm;
         d.tile_n = tv.bn;
         d.tile_k = d.kernel == KERN_NCHW ? tv.bk : (p.dtype == CONV_F32 ? tv.bk / 2 : tv.bk);
+    }
+
+    // The register-streamed strip kernel reads the filter from a copy in MFMA
+    // fragment order: output channels padded to a multiple of 32.
+    d.frag_pack = d.kernel == KERN_STRIP_RB;
+    if (d.frag_pack) {
+        d.off_filter = 0;
+        d.bytes_filter = uint64_t((p.K + 31) / 32 * 32) * d.Kg * e;
+        d.ws_bytes = p.N == 0 ? 0 : d.bytes_filter;
     }
 
     // NCHW staging tile: whole strip columns of R*C values per LDS row.
@@ -250,6 +264,14 @@ uint32_t grid_stride_blocks(uint64_t work) {
 
 template <typename T>
 void launch_pack(const conv_desc& d, const void* w, void* out, hipStream_t st) {
+    if (d.frag_pack) {
+        if constexpr (sizeof(T) == 2) {
+            const int32_t NB = int32_t((d.p.K + 31) / 32);
+            FragPackArgs a{w, out, int32_t(d.p.K), int32_t(d.Kg), NB};
+            pack_filter_frag_kernel<T><<<grid_stride_blocks(uint64_t(NB) * (d.Kg / 16) * 64), 256, 0, st>>>(a);
+        }
+        return;
+    }
     PackArgs a{w, out, int32_t(d.p.K), int32_t(d.p.C), int32_t(d.p.R), int32_t(d.p.S), int32_t(d.RCp), int32_t(d.Kl)};
     const uint32_t blocks = grid_stride_blocks(uint64_t(d.p.K) * d.Kl);
     if (d.p.layout == CONV_NHWC)
@@ -333,7 +355,7 @@ conv_status_t check_ws(const conv_desc& d, const void* ws) {
 
 // Unchecked stage launches (pointers already validated by the caller).
 conv_status_t run_pack(const conv_desc& d, const void* w, void* ws, hipStream_t st) {
-    if (!d.pack || d.p.N == 0) return CONV_OK;
+    if (!(d.pack || d.frag_pack) || d.p.N == 0) return CONV_OK;
     by_dtype<PackOp>(d.p.dtype, d, w, static_cast<char*>(ws) + d.off_filter, st);
     return launch_status();
 }
@@ -425,7 +447,7 @@ conv_status_t conv_plan_info(conv_desc_t d, conv_plan_info_t* info) {
 
 conv_status_t conv_pack_filter(conv_desc_t d, const void* w, void* ws, void* stream) {
     if (!desc_ok(d)) return CONV_ERR_INVALID_ARG;
-    if (!d->pack || d->p.N == 0) return CONV_OK;
+    if (!(d->pack || d->frag_pack) || d->p.N == 0) return CONV_OK;
     conv_status_t s;
     if ((s = check_dev(w, 16)) != CONV_OK) return s;
     if ((s = check_ws(*d, ws)) != CONV_OK) return s;

@@ -15,6 +15,7 @@ enum KernelId : int32_t {
     KERN_WIDE = 2,   // LDS-DMA ring, one wave per SIMD, wide register tiles (16-bit, NHWC windows)
     KERN_NCHW = 3,   // fp32 NCHW windows by 4-byte LDS-DMA
     KERN_STRIP = 4,  // input row strips staged in LDS once per filter row (16-bit, NHWC, C % 32 == 0, S >= 2)
+    KERN_STRIP_RB = 5,  // the same strips, filter fragments streamed into registers from a packed copy
 };
 
 // One compiled tile shape: BM x BN output tile, BK-deep LDS stages (in 16-bit
@@ -53,6 +54,12 @@ constexpr StripVariant kStripVariants[] = {
     {512, 128, 4, 1, 2816, 4}, {256, 128, 2, 2, 1536, 4}, {256, 256, 2, 2, 1536, 4},
     {128, 128, 2, 2, 1024, 4}, {128, 256, 2, 2, 1024, 4},
 };
+// Strip kernel with register-streamed filter fragments: `bst` is the number
+// of steps the filter loads run ahead (DB).
+constexpr StripVariant kStripRbVariants[] = {
+    {512, 128, 4, 1, 2816, 2}, {512, 128, 4, 1, 2816, 3}, {256, 128, 2, 2, 1536, 2},
+    {128, 128, 2, 2, 1024, 2}, {256, 256, 2, 2, 1536, 2},
+};
 template <class V, int N>
 constexpr int count_of(const V (&)[N]) {
     return N;
@@ -64,7 +71,8 @@ struct conv_desc {
     int64_t P, Q, M, Kg, W_used, RCp, Kl;
     int32_t elem, vec;
     bool elided;        // no lowering launch: the contraction reads x (implicit, or 1x1 NHWC unpadded)
-    bool pack;          // filter needs packing into ws
+    bool pack;          // filter needs packing into ws (lowered contraction order)
+    bool frag_pack;     // filter packed into MFMA fragment order in ws (register-streamed kernel)
     uint64_t off_filter, bytes_filter, off_low, bytes_low, ws_bytes;
     uint64_t im2win_bytes, im2col_bytes;
     int32_t kernel;     // KernelId

@@ -284,4 +284,32 @@ __global__ void __launch_bounds__(256) pack_filter_kernel(PackArgs a) {
     }
 }
 
+// Filter in MFMA fragment order: Bf[nb][kk][lane][8] =
+// w[nb*32 + lane%32][kk*16 + (lane/32)*8 + e] (KRSC rows, contraction index
+// (r*S + s)*C + c), zero for output channels >= K.  One 16-byte chunk per
+// thread.
+struct FragPackArgs {
+    const void* w;
+    void* out;
+    int32_t K, Kg, NB;   // NB = ceil(K/32)
+};
+
+template <typename T>
+__global__ void __launch_bounds__(256) pack_filter_frag_kernel(FragPackArgs a) {
+    const int KK = a.Kg / 16;
+    const int64_t total = int64_t(a.NB) * KK * 64;
+    const T* __restrict__ w = static_cast<const T*>(a.w);
+    T* __restrict__ out = static_cast<T*>(a.out);
+    for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < total; i += int64_t(gridDim.x) * 256) {
+        const int lane = int(i & 63);
+        const int64_t blk = i >> 6;
+        const int kk = int(blk % KK);
+        const int nb = int(blk / KK);
+        const int n = nb * 32 + (lane & 31);
+        u32x4 v = zero4();
+        if (n < a.K) v = load16(w + int64_t(n) * a.Kg + kk * 16 + (lane >> 5) * 8);
+        store16(out + i * 8, v);
+    }
+}
+
 }  // namespace convlower

@@ -113,7 +113,9 @@ typedef struct {
     int32_t elem_bytes;
     /* contraction kernel: 0 register-staged tiles, 1 LDS-DMA pipeline (two
      * waves per SIMD), 2 LDS-DMA pipeline with one wave per SIMD and 32x32
-     * MFMA tiles, 3 fp32 NCHW windows, 4 input row strips staged in LDS;
+     * MFMA tiles, 3 fp32 NCHW windows, 4 input row strips staged in LDS,
+     * 5 the same strips with the filter streamed into registers from a copy
+     * in MFMA fragment order (that copy is the workspace's filter part);
      * kernel_variant indexes that kernel's compiled tile shapes */
     int32_t kernel, kernel_variant;
 } conv_plan_info_t;

@@ -21,7 +21,7 @@ from parity import TORCH_DT, assert_parity, to_f64
 pytestmark = pytest.mark.gpu
 
 # kernel name -> (plan_info kernel id, number of compiled variants)
-KERNELS = {"reg": (0, 3), "dma": (1, 7), "wide": (2, 9), "nchw": (3, 9), "strip": (4, 5)}
+KERNELS = {"reg": (0, 3), "dma": (1, 7), "wide": (2, 9), "nchw": (3, 9), "strip": (4, 5), "striprb": (5, 5)}
 
 # (N, C, H, W, K, R, S, stride, pad, dilation)
 SHAPES_C32 = [
@@ -49,6 +49,8 @@ PLANS = [
     ("nchw", "f32", "nchw", "implicit", SHAPES_SMALL_C + SHAPES_C32[:2]),
     ("strip", "f16", "nhwc", "implicit", SHAPES_C32),
     ("strip", "bf16", "nhwc", "implicit", SHAPES_C32[:3]),
+    ("striprb", "f16", "nhwc", "implicit", SHAPES_C32),
+    ("striprb", "bf16", "nhwc", "implicit", SHAPES_C32[:3]),
 ]
 
 
@@ -108,7 +110,7 @@ def test_forced_kernel_integer_exact(dev, monkeypatch):
     xl, wl = _perm(x, "nhwc"), _perm(w, "nhwc")
     ref = oracle.conv2d(xl, wl, b, layout="nhwc", stride=1, padding=1)
     want = torch.from_numpy(ref).to(torch.float32).to(torch.float16)
-    for forced in ("strip:0", "strip:2", "strip:3", "wide:0", "wide:5"):
+    for forced in ("strip:0", "strip:2", "strip:3", "wide:0", "wide:5", "striprb:0", "striprb:3", "striprb:4"):
         monkeypatch.setenv("CONVLOWER_KERNEL", forced)
         d = cl.Conv2d(N, C, H, W, K, R, S, padding=1, layout="nhwc", dtype="f16", algo="implicit")
         assert d.info["kernel"] == KERNELS[forced.split(":")[0]][0], forced
