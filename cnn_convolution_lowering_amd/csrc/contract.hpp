@@ -237,6 +237,8 @@ void launch_gemm(const conv_desc& d, const void* x, const void* w, const void* b
                 CONVLOWER_STRIP_RB_CASE(2)
                 CONVLOWER_STRIP_RB_CASE(3)
                 CONVLOWER_STRIP_RB_CASE(4)
+                CONVLOWER_STRIP_RB_CASE(5)
+                CONVLOWER_STRIP_RB_CASE(6)
                 default: break;
             }
 #undef CONVLOWER_STRIP_RB_CASE

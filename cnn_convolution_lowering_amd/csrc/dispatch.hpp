@@ -58,7 +58,8 @@ constexpr StripVariant kStripVariants[] = {
 // of steps the filter loads run ahead (DB).
 constexpr StripVariant kStripRbVariants[] = {
     {512, 128, 4, 1, 2816, 2}, {512, 128, 4, 1, 2816, 3}, {256, 128, 2, 2, 1536, 2},
-    {128, 128, 2, 2, 1024, 2}, {256, 256, 2, 2, 1536, 2},
+    {128, 128, 2, 2, 1024, 2}, {256, 256, 2, 2, 1536, 2}, {512, 128, 4, 1, 2816, 4},
+    {128, 128, 2, 2, 1024, 4},
 };
 template <class V, int N>
 constexpr int count_of(const V (&)[N]) {
