@@ -9,6 +9,7 @@
 #include "igemm.hpp"
 #include "igemm_dma.hpp"
 #include "igemm_nchw.hpp"
+#include "igemm_nchw_strip.hpp"
 #include "igemm_strip.hpp"
 #include "igemm_strip_rb.hpp"
 #include "igemm_wide.hpp"
@@ -192,6 +193,9 @@ void launch_gemm(const conv_desc& d, const void* x, const void* w, const void* b
                 CONVLOWER_NCHW_CASE(6)
                 CONVLOWER_NCHW_CASE(7)
                 CONVLOWER_NCHW_CASE(8)
+                CONVLOWER_NCHW_CASE(9)
+                CONVLOWER_NCHW_CASE(10)
+                CONVLOWER_NCHW_CASE(11)
                 default: break;
             }
 #undef CONVLOWER_NCHW_CASE
@@ -218,6 +222,34 @@ void launch_gemm(const conv_desc& d, const void* x, const void* w, const void* b
             default: break;
         }
 #undef CONVLOWER_DMA_CASE
+        return;
+    }
+    if (d.kernel == KERN_NCHW_STRIP) {
+        if constexpr (sizeof(T) == 4) {
+#define CONVLOWER_NCHW_STRIP_CASE(I)                                                                          \
+    case I: {                                                                                                 \
+        constexpr NchwStripVariant v = kNchwStripVariants[I];                                                 \
+        GemmArgs h = g;                                                                                       \
+        h.tiles_n = int32_t((d.p.K + v.bn - 1) / v.bn);                                                       \
+        const uint32_t blocks = uint32_t(((uint64_t(d.M) + v.bm - 1) / v.bm) * h.tiles_n);                   \
+        conv_nchw_f32_strip_kernel<v.bm, v.bn, v.wgm, v.wgn, v.strip, v.db, v.nbuf><<<blocks, 256, 0, st>>>(h); \
+        break;                                                                                                \
+    }
+            switch (d.variant) {
+                CONVLOWER_NCHW_STRIP_CASE(0)
+                CONVLOWER_NCHW_STRIP_CASE(1)
+                CONVLOWER_NCHW_STRIP_CASE(2)
+                CONVLOWER_NCHW_STRIP_CASE(3)
+                CONVLOWER_NCHW_STRIP_CASE(4)
+                CONVLOWER_NCHW_STRIP_CASE(5)
+                CONVLOWER_NCHW_STRIP_CASE(6)
+                CONVLOWER_NCHW_STRIP_CASE(7)
+                CONVLOWER_NCHW_STRIP_CASE(8)
+                CONVLOWER_NCHW_STRIP_CASE(9)
+                default: break;
+            }
+#undef CONVLOWER_NCHW_STRIP_CASE
+        }
         return;
     }
     if (d.kernel == KERN_STRIP_RB) {

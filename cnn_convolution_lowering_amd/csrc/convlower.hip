@@ -8,6 +8,7 @@
 // enqueue kernels on the caller's stream and report launch errors.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
@@ -108,21 +109,41 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d) {
     const bool wide_ok = dma_ok && implicit && nhwc && p.dtype != CONV_F32 && p.C % 32 == 0;
     // The strip kernel: the same operands, a filter at least two taps wide,
     // and the input rows under a tile's pixels fitting its strip buffer.
+    // fp32 NCHW strips: no horizontal padding (rows are loaded from column
+    // 0 in 16-byte pieces), 16-channel blocks, and the rows under a tile's
+    // pixels fitting the buffer.
+    auto nchw_strip_fits = [&](const NchwStripVariant& v) {
+        const int64_t rows = (v.bm - 1) / d.Q + 2, wq = (d.W_used + 3) / 4;
+        return nchw_ok && p.pad_w == 0 && p.C % 16 == 0 &&
+               uint64_t((p.K + 15) / 16 * 16) * d.Kg * 4 < (uint64_t(1) << 31) && rows < 256 && wq < 256 &&
+               rows * wq <= nchw_strip_plane(v.strip);
+    };
     auto strip_fits = [&](const StripVariant& v) {
         const int64_t rows = (v.bm - 1) / d.Q + 2;
         return wide_ok && p.S >= 2 && rows * d.W_used * 4 <= v.strip;
     };
     if (nchw_ok) {
-        // fp32 NCHW: narrow K -> 128-row tiles, 16-deep stages x4; wide K ->
+        // fp32 NCHW: narrow K -> 128-row tiles, 16-deep stages; wide K ->
         // 64-row tiles, 64 or 128 channels wide depending on how many
         // workgroups that gives.
         d.kernel = KERN_NCHW;
         if (p.K <= 32)
-            d.variant = 8;
+            d.variant = d.Kg <= 32 ? 9 : 8;   // a contraction of one or two tiles: two stages leave room for more workgroups
         else if (p.K <= 64)
             d.variant = 4;
         else
             d.variant = (d.M / 64) * ((p.K + 127) / 128) >= 768 ? 3 : 7;
+        // Unpadded rows, 16-channel blocks and taps sharing a row: the strip
+        // kernel (a sweep over the encoder's strided layers put it ahead):
+        // 128 x 64 tiles up to 64 output channels, else 128 x 128 while that
+        // still gives about two tiles per CU, else 64 x 64.
+        if (p.S >= 2) {
+            const int v = p.K <= 64 ? 0 : ((d.M / 128) * ((p.K + 127) / 128) >= 384 ? 5 : 3);
+            if (nchw_strip_fits(kNchwStripVariants[v])) {
+                d.kernel = KERN_NCHW_STRIP;
+                d.variant = v;
+            }
+        }
     } else if (dma_ok) {
         // BN covers the output channels up to 128; BM = 256 where that still
         // gives two workgroups per CU, else 128.
@@ -166,13 +187,21 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d) {
                        strip_fits(kStripRbVariants[i])) {
                 d.kernel = KERN_STRIP_RB;
                 d.variant = i;
+            } else if (name == "nchwstrip" && i >= 0 && i < count_of(kNchwStripVariants) &&
+                       nchw_strip_fits(kNchwStripVariants[i])) {
+                d.kernel = KERN_NCHW_STRIP;
+                d.variant = i;
             } else if (name == "nchw" && nchw_ok && i >= 0 && i < count_of(kNchwVariants)) {
                 d.kernel = KERN_NCHW;
                 d.variant = i;
             }
         }
     }
-    if (d.kernel == KERN_STRIP || d.kernel == KERN_STRIP_RB) {
+    if (d.kernel == KERN_NCHW_STRIP) {
+        d.tile_m = kNchwStripVariants[d.variant].bm;
+        d.tile_n = kNchwStripVariants[d.variant].bn;
+        d.tile_k = 16;
+    } else if (d.kernel == KERN_STRIP || d.kernel == KERN_STRIP_RB) {
         const StripVariant& sv = d.kernel == KERN_STRIP ? kStripVariants[d.variant] : kStripRbVariants[d.variant];
         d.tile_m = sv.bm;
         d.tile_n = sv.bn;
@@ -189,10 +218,11 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d) {
 
     // The register-streamed strip kernel reads the filter from a copy in MFMA
     // fragment order: output channels padded to a multiple of 32.
-    d.frag_pack = d.kernel == KERN_STRIP_RB;
+    d.frag_pack = d.kernel == KERN_STRIP_RB || d.kernel == KERN_NCHW_STRIP;
     if (d.frag_pack) {
+        const int64_t kpad = d.kernel == KERN_STRIP_RB ? (p.K + 31) / 32 * 32 : (p.K + 15) / 16 * 16;
         d.off_filter = 0;
-        d.bytes_filter = uint64_t((p.K + 31) / 32 * 32) * d.Kg * e;
+        d.bytes_filter = uint64_t(kpad) * d.Kg * e;
         d.ws_bytes = p.N == 0 ? 0 : d.bytes_filter;
     }
 
@@ -278,6 +308,10 @@ void launch_pack(const conv_desc& d, const void* w, void* out, hipStream_t st) {
             const int32_t NB = int32_t((d.p.K + 31) / 32);
             FragPackArgs a{w, out, int32_t(d.p.K), int32_t(d.Kg), NB};
             pack_filter_frag_kernel<T><<<grid_stride_blocks(uint64_t(NB) * (d.Kg / 16) * 64), 256, 0, st>>>(a);
+        } else {
+            const int32_t NB = int32_t((d.p.K + 15) / 16);
+            FragPackF32Args a{w, out, int32_t(d.p.K), int32_t(d.p.C), int32_t(d.p.R), int32_t(d.p.S), NB};
+            pack_filter_frag_f32_kernel<<<grid_stride_blocks(uint64_t(NB) * (d.Kg / 16) * 64), 256, 0, st>>>(a);
         }
         return;
     }

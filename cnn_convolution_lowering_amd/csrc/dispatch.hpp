@@ -16,6 +16,7 @@ enum KernelId : int32_t {
     KERN_NCHW = 3,   // fp32 NCHW windows by 4-byte LDS-DMA
     KERN_STRIP = 4,  // input row strips staged in LDS once per filter row (16-bit, NHWC, C % 32 == 0, S >= 2)
     KERN_STRIP_RB = 5,  // the same strips, filter fragments streamed into registers from a packed copy
+    KERN_NCHW_STRIP = 6,  // fp32 NCHW strips (16-byte row loads), register-streamed filter (pad_w == 0, C % 16 == 0)
 };
 
 // One compiled tile shape: BM x BN output tile, BK-deep LDS stages (in 16-bit
@@ -42,7 +43,7 @@ constexpr TileVariant kWideVariants[] = {
 constexpr TileVariant kNchwVariants[] = {
     {128, 32, 32, 4, 1, 3}, {128, 64, 32, 2, 2, 3}, {128, 128, 32, 2, 2, 3}, {64, 128, 32, 2, 2, 3},
     {128, 64, 16, 2, 2, 4}, {128, 64, 16, 2, 2, 6}, {64, 64, 32, 2, 2, 4},  {64, 64, 16, 2, 2, 6},
-    {128, 32, 16, 4, 1, 4},
+    {128, 32, 16, 4, 1, 4}, {128, 32, 16, 4, 1, 2}, {64, 32, 16, 4, 1, 2}, {128, 32, 16, 4, 1, 3},
 };
 // Strip-staged kernel: BM x BN tile, WGM x WGN waves, STRIP 16-byte chunk
 // slots per strip buffer (bounds (ceil-ish BM/Q + 1) * W_used * 4), BST
@@ -61,6 +62,23 @@ constexpr StripVariant kStripRbVariants[] = {
     {128, 128, 2, 2, 1024, 2}, {256, 256, 2, 2, 1536, 2}, {512, 128, 4, 1, 2816, 4},
     {128, 128, 2, 2, 1024, 4},
 };
+// fp32 NCHW strip kernel: strip = 16-byte slots per buffer (16 channel
+// planes of ((BM-1)/Q + 2) rows x ceil(W_used/4) slots), db = filter
+// prefetch depth in steps, nbuf = strip buffers (strips loaded nbuf-1
+// ahead).
+struct NchwStripVariant {
+    int bm, bn, wgm, wgn, strip, db, nbuf;
+};
+constexpr NchwStripVariant kNchwStripVariants[] = {
+    {128, 64, 2, 2, 1536, 3, 2}, {128, 64, 2, 2, 1536, 4, 3}, {64, 64, 2, 2, 1024, 4, 3},
+    {64, 64, 2, 2, 1024, 4, 2},  {64, 128, 2, 2, 1024, 4, 3}, {128, 128, 2, 2, 1536, 2, 2},
+    {64, 64, 2, 2, 1024, 6, 3},  {128, 32, 4, 1, 1536, 4, 3}, {64, 32, 4, 1, 1024, 4, 3},
+    {64, 64, 4, 1, 1024, 4, 3},
+};
+// Slots per channel plane in a strip buffer of `strip` slots: the most that
+// fit, rounded to 1 mod 4, so that planes 4 apart (one per lane group) start
+// 16 banks apart.
+constexpr int32_t nchw_strip_plane(int32_t strip) { return strip / 16 - (strip / 16 - 1) % 4; }
 template <class V, int N>
 constexpr int count_of(const V (&)[N]) {
     return N;

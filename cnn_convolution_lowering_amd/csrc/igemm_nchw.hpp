@@ -241,7 +241,54 @@ __global__ void __launch_bounds__(256, 2) conv_nchw_f32_dma_kernel(GemmArgs g) {
         if (kt + STAGES - 1 < nkt) issue((kt + STAGES - 1) % STAGES);
     }
 
-    store_tile<float, BM, BN, WM, WN, TM, TN, false>(g, acc, m0, n0, wm, wn, lane);
+    // Fused epilogue through LDS: the tile is written channel-major into the
+    // (now idle) pipeline buffer, bias added, then stored as 16-byte pieces
+    // of contiguous NKPQ rows -- consecutive lanes write consecutive pixels
+    // of one output channel, instead of 16 channels 64 bytes each.
+    constexpr int OP = BM + 4;   // row pitch (floats): rows 4 banks apart for the 16-row writes
+    static_assert(BN * OP <= STAGES * STAGE_ELEMS, "output tile fits the pipeline buffer");
+    __syncthreads();
+    {
+        const float* __restrict__ bias = static_cast<const float*>(g.bias);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int nl = wn * WN + j * 16 + (lane & 15);
+            const float bk = (bias && n0 + nl < g.K) ? bias[n0 + nl] : 0.f;
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                const int ml = wm * WM + i * 16 + 4 * (lane >> 4);
+                store16(smem + nl * OP + ml, u32x4{__float_as_uint(acc[i][j][0] + bk), __float_as_uint(acc[i][j][1] + bk),
+                                                   __float_as_uint(acc[i][j][2] + bk), __float_as_uint(acc[i][j][3] + bk)});
+            }
+        }
+    }
+    __syncthreads();
+    {
+        float* __restrict__ y = static_cast<float*>(g.y);
+        constexpr int G = BM / 4;                  // 4-pixel groups per channel row
+        const bool vec = (g.PQ & 3) == 0;          // groups never straddle an image
+        for (int t = tid; t < BN * G; t += 256) {
+            const int nl = t / G, gi = t - (t / G) * G;
+            const int n = n0 + nl;
+            const int64_t m = m0 + 4 * gi;
+            if (n >= g.K || m >= g.M) continue;
+            const u32x4 v = load16(smem + nl * OP + 4 * gi);
+            if (vec && m + 3 < g.M) {
+                const int32_t img = int32_t(m / g.PQ);
+                const int32_t pq = int32_t(m - int64_t(img) * g.PQ);
+                store16(y + (int64_t(img) * g.K + n) * g.PQ + pq, v);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int64_t me = m + e;
+                    if (me >= g.M) break;
+                    const int32_t img = int32_t(me / g.PQ);
+                    const int32_t pq = int32_t(me - int64_t(img) * g.PQ);
+                    y[(int64_t(img) * g.K + n) * g.PQ + pq] = __uint_as_float(v[e]);
+                }
+            }
+        }
+    }
 }
 
 }  // namespace convlower

@@ -312,4 +312,46 @@ __global__ void __launch_bounds__(256) pack_filter_frag_kernel(FragPackArgs a) {
     }
 }
 
+// fp32 KCRS filter in the MFMA fragment order of the fp32 NCHW strip
+// kernel: contraction index k' = (r*C + c)*S + s (filter row outermost), and
+// Bf[nb][kk][lane][4] = w[nb*16 + lane%16][k' = kk*16 + 4*(lane/16) + e],
+// zero for output channels >= K.  One 16-byte chunk per thread.
+struct FragPackF32Args {
+    const void* w;
+    void* out;
+    int32_t K, C, R, S, NB;   // NB = ceil(K/16)
+};
+
+// fp32 KCRS filter into 16x16x4 MFMA B fragments in the order of the fp32
+// NCHW strip kernel: fragment kk = (r*(C/16) + cb)*S + s is the 16-deep step
+// of tap (r, s) over channels cb*16 .. cb*16+15; lane (gq, l16) element e
+// holds w[nb*16 + l16][cb*16 + 4*gq + e][r][s] (zero past K), at
+// ((nb*KK + kk)*64 + lane)*16 bytes.  C % 16 == 0.
+__global__ void __launch_bounds__(256) pack_filter_frag_f32_kernel(FragPackF32Args a) {
+    const int CBN = a.C / 16;
+    const int KK = CBN * a.R * a.S;
+    const int64_t total = int64_t(a.NB) * KK * 64;
+    const float* __restrict__ w = static_cast<const float*>(a.w);
+    float* __restrict__ out = static_cast<float*>(a.out);
+    for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < total; i += int64_t(gridDim.x) * 256) {
+        const int lane = int(i & 63);
+        const int64_t blk = i >> 6;
+        const int kk = int(blk % KK);
+        const int nb = int(blk / KK);
+        const int n = nb * 16 + (lane & 15);
+        const int strip = kk / a.S, s = kk - strip * a.S;
+        const int r = strip / CBN, cb = strip - r * CBN;
+        float v[4] = {0.f, 0.f, 0.f, 0.f};
+        if (n < a.K) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int c = cb * 16 + 4 * (lane >> 4) + e;
+                v[e] = w[((int64_t(n) * a.C + c) * a.R + r) * a.S + s];
+            }
+        }
+        store16(out + i * 4, u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                                   __float_as_uint(v[3])});
+    }
+}
+
 }  // namespace convlower

@@ -115,7 +115,9 @@ typedef struct {
      * waves per SIMD), 2 LDS-DMA pipeline with one wave per SIMD and 32x32
      * MFMA tiles, 3 fp32 NCHW windows, 4 input row strips staged in LDS,
      * 5 the same strips with the filter streamed into registers from a copy
-     * in MFMA fragment order (that copy is the workspace's filter part);
+     * in MFMA fragment order (that copy is the workspace's filter part),
+     * 6 fp32 NCHW row strips loaded 16 bytes per lane, filter streamed the
+     * same way;
      * kernel_variant indexes that kernel's compiled tile shapes */
     int32_t kernel, kernel_variant;
 } conv_plan_info_t;

@@ -21,7 +21,7 @@ from parity import TORCH_DT, assert_parity, to_f64
 pytestmark = pytest.mark.gpu
 
 # kernel name -> (plan_info kernel id, number of compiled variants)
-KERNELS = {"reg": (0, 3), "dma": (1, 7), "wide": (2, 9), "nchw": (3, 9), "strip": (4, 5), "striprb": (5, 7)}
+KERNELS = {"reg": (0, 3), "dma": (1, 7), "wide": (2, 9), "nchw": (3, 12), "strip": (4, 5), "striprb": (5, 7), "nchwstrip": (6, 10)}
 
 # (N, C, H, W, K, R, S, stride, pad, dilation)
 SHAPES_C32 = [
@@ -35,6 +35,15 @@ SHAPES_SMALL_C = [
     (2, 3, 30, 30, 32, 3, 3, (1, 1), (1, 1), (1, 1)),
     (3, 8, 15, 11, 70, 2, 3, (2, 1), (0, 1), (1, 2)),
     (2, 16, 9, 9, 130, 3, 3, (2, 2), (0, 0), (1, 1)),
+]
+# fp32 NCHW, no horizontal padding, C % 16 == 0: the encoder's strided layers and ragged variants
+SHAPES_NCHW_F32 = [
+    (3, 32, 30, 30, 64, 3, 3, (2, 2), (0, 0), (1, 1)),
+    (2, 64, 14, 14, 128, 2, 2, (2, 2), (0, 0), (1, 1)),
+    (2, 128, 7, 7, 256, 2, 2, (2, 2), (0, 0), (1, 1)),
+    (2, 16, 13, 22, 40, 3, 4, (1, 1), (1, 0), (1, 1)),
+    (1, 48, 20, 17, 70, 2, 3, (1, 2), (0, 0), (2, 1)),
+    (2, 32, 9, 40, 33, 3, 2, (2, 1), (2, 0), (1, 3)),
 ]
 # (kernel, dtype, layout, algo, shapes)
 PLANS = [
@@ -51,6 +60,7 @@ PLANS = [
     ("strip", "bf16", "nhwc", "implicit", SHAPES_C32[:3]),
     ("striprb", "f16", "nhwc", "implicit", SHAPES_C32),
     ("striprb", "bf16", "nhwc", "implicit", SHAPES_C32[:3]),
+    ("nchwstrip", "f32", "nchw", "implicit", SHAPES_NCHW_F32),
 ]
 
 
@@ -118,3 +128,4 @@ def test_forced_kernel_integer_exact(dev, monkeypatch):
         y = d.forward(xl.to(dev), wl.to(dev), b.to(dev))
         torch.cuda.synchronize()
         assert torch.equal(y.cpu().view(torch.int16), want.view(torch.int16)), forced
+
