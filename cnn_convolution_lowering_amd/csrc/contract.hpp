@@ -10,6 +10,7 @@
 #include "igemm_dma.hpp"
 #include "igemm_nchw.hpp"
 #include "igemm_nchw_strip.hpp"
+#include "igemm_nchw_tile.hpp"
 #include "igemm_strip.hpp"
 #include "igemm_strip_rb.hpp"
 #include "igemm_wide.hpp"
@@ -222,6 +223,33 @@ void launch_gemm(const conv_desc& d, const void* x, const void* w, const void* b
             default: break;
         }
 #undef CONVLOWER_DMA_CASE
+        return;
+    }
+    if (d.kernel == KERN_NCHW_TILE) {
+        if constexpr (sizeof(T) == 4) {
+            GemmArgs h = g;
+            h.tile_rows = d.tile_rows;
+            const int64_t P = d.P, TP = d.tile_rows;
+            const uint32_t blocks = uint32_t(d.p.N * ((P + TP - 1) / TP));
+            const int64_t rows_in = (TP - 1) * d.p.stride_h + (d.p.R - 1) * d.p.dil_h + 1;
+            // C planes, a zero plane and the padded filter
+            const size_t lds = size_t(((d.p.C + 1) * rows_in * d.W_used + 3 +
+                                       256 * kNchwTileVariants[d.variant].tn * kNchwTileVariants[d.variant].ks) * 4);
+#define CONVLOWER_NCHW_TILE_CASE(I)                                                                            \
+    case I:                                                                                                    \
+        conv_nchw_f32_tile_kernel<kNchwTileVariants[I].ks, kNchwTileVariants[I].tn><<<blocks, 256, lds, st>>>(h); \
+        break;
+            switch (d.variant) {
+                CONVLOWER_NCHW_TILE_CASE(0)
+                CONVLOWER_NCHW_TILE_CASE(1)
+                CONVLOWER_NCHW_TILE_CASE(2)
+                CONVLOWER_NCHW_TILE_CASE(3)
+                CONVLOWER_NCHW_TILE_CASE(4)
+                CONVLOWER_NCHW_TILE_CASE(5)
+                default: break;
+            }
+#undef CONVLOWER_NCHW_TILE_CASE
+        }
         return;
     }
     if (d.kernel == KERN_NCHW_STRIP) {

@@ -118,6 +118,19 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d) {
                uint64_t((p.K + 15) / 16 * 16) * d.Kg * 4 < (uint64_t(1) << 31) && rows < 256 && wq < 256 &&
                rows * wq <= nchw_strip_plane(v.strip);
     };
+    // fp32 NCHW small windows (C*R*S <= 64, K <= 64): output rows per
+    // workgroup so that there are about kNchwTileWgs workgroups and a
+    // block's staged input rows fit kNchwTileLds; 0 where it does not apply.
+    auto nchw_tile_rows = [&](const NchwTileVariant& v) -> int64_t {
+        if (!nchw_ok || d.Kg > 16 * v.ks || p.K > 16 * v.tn) return 0;
+        const int64_t row_bytes = (p.C + 1) * d.W_used * 4;   // C planes and a zero plane
+        const int64_t fit_rows = (kNchwTileLds - 1024 * v.tn * v.ks - 16) / row_bytes - (p.R - 1) * int64_t(p.dil_h) - 1;
+        if (fit_rows < 0) return 0;
+        const int64_t tmax = fit_rows / p.stride_h + 1;
+        const int64_t per_img = (kNchwTileWgs + p.N - 1) / p.N;
+        const int64_t tp = (d.P + per_img - 1) / per_img;
+        return tp < tmax ? tp : tmax;
+    };
     auto strip_fits = [&](const StripVariant& v) {
         const int64_t rows = (v.bm - 1) / d.Q + 2;
         return wide_ok && p.S >= 2 && rows * d.W_used * 4 <= v.strip;
@@ -141,6 +154,15 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d) {
             const int v = p.K <= 64 ? 0 : ((d.M / 128) * ((p.K + 127) / 128) >= 384 ? 5 : 3);
             if (nchw_strip_fits(kNchwStripVariants[v])) {
                 d.kernel = KERN_NCHW_STRIP;
+                d.variant = v;
+            }
+        }
+        // Small windows and few output channels: the whole filter in
+        // registers and the input rows staged once per block of output rows.
+        if (d.Kg <= 64 && p.K <= 64) {
+            const int v = (d.Kg <= 16 ? 0 : d.Kg <= 32 ? 1 : 2) + (p.K <= 32 ? 0 : 3);
+            if (nchw_tile_rows(kNchwTileVariants[v]) > 0) {
+                d.kernel = KERN_NCHW_TILE;
                 d.variant = v;
             }
         }
@@ -187,6 +209,10 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d) {
                        strip_fits(kStripRbVariants[i])) {
                 d.kernel = KERN_STRIP_RB;
                 d.variant = i;
+            } else if (name == "nchwtile" && i >= 0 && i < count_of(kNchwTileVariants) &&
+                       nchw_tile_rows(kNchwTileVariants[i]) > 0) {
+                d.kernel = KERN_NCHW_TILE;
+                d.variant = i;
             } else if (name == "nchwstrip" && i >= 0 && i < count_of(kNchwStripVariants) &&
                        nchw_strip_fits(kNchwStripVariants[i])) {
                 d.kernel = KERN_NCHW_STRIP;
@@ -197,7 +223,13 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d) {
             }
         }
     }
-    if (d.kernel == KERN_NCHW_STRIP) {
+    d.tile_rows = 0;
+    if (d.kernel == KERN_NCHW_TILE) {
+        d.tile_rows = int32_t(nchw_tile_rows(kNchwTileVariants[d.variant]));
+        d.tile_m = 16;
+        d.tile_n = 16 * kNchwTileVariants[d.variant].tn;
+        d.tile_k = 16 * kNchwTileVariants[d.variant].ks;
+    } else if (d.kernel == KERN_NCHW_STRIP) {
         d.tile_m = kNchwStripVariants[d.variant].bm;
         d.tile_n = kNchwStripVariants[d.variant].bn;
         d.tile_k = 16;

@@ -17,6 +17,7 @@ enum KernelId : int32_t {
     KERN_STRIP = 4,  // input row strips staged in LDS once per filter row (16-bit, NHWC, C % 32 == 0, S >= 2)
     KERN_STRIP_RB = 5,  // the same strips, filter fragments streamed into registers from a packed copy
     KERN_NCHW_STRIP = 6,  // fp32 NCHW strips (16-byte row loads), register-streamed filter (pad_w == 0, C % 16 == 0)
+    KERN_NCHW_TILE = 7,   // fp32 NCHW small windows: input rows staged once per block of output rows, filter in registers
 };
 
 // One compiled tile shape: BM x BN output tile, BK-deep LDS stages (in 16-bit
@@ -75,6 +76,15 @@ constexpr NchwStripVariant kNchwStripVariants[] = {
     {64, 64, 2, 2, 1024, 6, 3},  {128, 32, 4, 1, 1536, 4, 3}, {64, 32, 4, 1, 1024, 4, 3},
     {64, 64, 4, 1, 1024, 4, 3},
 };
+// fp32 NCHW small-window kernel: ks 16-deep steps (C*R*S <= 16*ks), tn
+// 16-channel blocks (K <= 16*tn).
+struct NchwTileVariant {
+    int ks, tn;
+};
+constexpr NchwTileVariant kNchwTileVariants[] = {{1, 2}, {2, 2}, {4, 2}, {1, 4}, {2, 4}, {4, 4}};
+// LDS budget of its staged rows, and the workgroups it aims for.
+constexpr int64_t kNchwTileLds = 32768;
+constexpr int64_t kNchwTileWgs = 1024;
 // Slots per channel plane in a strip buffer of `strip` slots: the most that
 // fit, rounded to 1 mod 4, so that planes 4 apart (one per lane group) start
 // 16 banks apart.
@@ -97,6 +107,7 @@ struct conv_desc {
     int32_t kernel;     // KernelId
     int32_t variant;    // index into that kernel's variant table
     int32_t tile_m, tile_n, tile_k;
+    int32_t tile_rows;  // fp32 NCHW small-window kernel: output rows per workgroup
     // NCHW staging (0 = use the element-wise kernel)
     int32_t stage_chunk, stage_ld;
 };

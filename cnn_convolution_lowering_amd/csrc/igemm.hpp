@@ -49,6 +49,7 @@ struct GemmArgs {
     int32_t RCp, sS;    // StridedRows: column offset
     int32_t ldb;        // filter row pitch (elements)
     int32_t tiles_n;    // ceil(K / BN)
+    int32_t tile_rows;  // output rows per workgroup (fp32 NCHW small-window kernel)
     // window loaders: the convolution itself
     int32_t C, H, W, R, S;
     int32_t sh, sw, ph, pw, dh, dw;

@@ -117,7 +117,8 @@ typedef struct {
      * 5 the same strips with the filter streamed into registers from a copy
      * in MFMA fragment order (that copy is the workspace's filter part),
      * 6 fp32 NCHW row strips loaded 16 bytes per lane, filter streamed the
-     * same way;
+     * same way, 7 fp32 NCHW small windows (C*R*S <= 64, K <= 64): input rows
+     * staged once per block of output rows, whole filter in registers;
      * kernel_variant indexes that kernel's compiled tile shapes */
     int32_t kernel, kernel_variant;
 } conv_plan_info_t;

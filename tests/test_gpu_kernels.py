@@ -21,7 +21,7 @@ from parity import TORCH_DT, assert_parity, to_f64
 pytestmark = pytest.mark.gpu
 
 # kernel name -> (plan_info kernel id, number of compiled variants)
-KERNELS = {"reg": (0, 3), "dma": (1, 7), "wide": (2, 9), "nchw": (3, 12), "strip": (4, 5), "striprb": (5, 7), "nchwstrip": (6, 10)}
+KERNELS = {"reg": (0, 3), "dma": (1, 7), "wide": (2, 9), "nchw": (3, 12), "strip": (4, 5), "striprb": (5, 7), "nchwstrip": (6, 10), "nchwtile": (7, 6)}
 
 # (N, C, H, W, K, R, S, stride, pad, dilation)
 SHAPES_C32 = [
@@ -45,6 +45,18 @@ SHAPES_NCHW_F32 = [
     (1, 48, 20, 17, 70, 2, 3, (1, 2), (0, 0), (2, 1)),
     (2, 32, 9, 40, 33, 3, 2, (2, 1), (2, 0), (1, 3)),
 ]
+# fp32 NCHW small windows (C*R*S <= 64, K <= 64): padding, strides, dilation, ragged pixel blocks
+SHAPES_SMALL_KG = [
+    (3, 3, 30, 30, 32, 3, 3, (1, 1), (1, 1), (1, 1)),
+    (2, 3, 17, 23, 20, 3, 3, (2, 1), (1, 2), (1, 1)),
+    (2, 2, 9, 11, 64, 3, 2, (1, 2), (2, 0), (2, 3)),
+    (1, 1, 40, 33, 50, 1, 5, (3, 1), (0, 2), (1, 1)),
+    (2, 7, 12, 12, 16, 3, 3, (1, 1), (1, 1), (1, 1)),
+    (1, 4, 70, 9, 33, 2, 2, (1, 1), (1, 0), (1, 1)),
+    (2, 1, 25, 27, 24, 3, 5, (1, 1), (1, 2), (1, 1)),
+    (1, 5, 11, 13, 40, 3, 3, (1, 1), (0, 1), (1, 1)),
+    (1, 3, 14, 16, 48, 3, 3, (2, 2), (1, 1), (1, 1)),
+]
 # (kernel, dtype, layout, algo, shapes)
 PLANS = [
     ("reg", "f32", "nhwc", "implicit", SHAPES_SMALL_C + SHAPES_C32[:2]),
@@ -61,6 +73,7 @@ PLANS = [
     ("striprb", "f16", "nhwc", "implicit", SHAPES_C32),
     ("striprb", "bf16", "nhwc", "implicit", SHAPES_C32[:3]),
     ("nchwstrip", "f32", "nchw", "implicit", SHAPES_NCHW_F32),
+    ("nchwtile", "f32", "nchw", "implicit", SHAPES_SMALL_KG),
 ]
 
 
