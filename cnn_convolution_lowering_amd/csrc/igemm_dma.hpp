@@ -52,6 +52,18 @@ __device__ __forceinline__ uint32_t lds_offset(const void* p) {
 
 constexpr uint32_t kOutOfRange = 0x80000000u;   // any offset >= num_records (< 2^31) reads as zero
 
+// floor(a / d) for 0 <= a < 2^22 and d >= 1, given rcp ~ 1/d (within a few
+// ulp): float(a) is exact and a*rcp is within 1 of a/d, so one correction
+// step on the remainder gives the quotient.  A few instructions instead of
+// the ~30 of a general 32-bit division.
+__device__ __forceinline__ int div_small(int a, int d, float rcp) {
+    int q = int(float(a) * rcp);
+    const int r = a - q * d;
+    q += r >= d ? 1 : 0;
+    q -= r < 0 ? 1 : 0;
+    return q;
+}
+
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 // 16 bytes from rsrc+voffset into LDS at m0 + 16*lane (m0 wave-uniform).

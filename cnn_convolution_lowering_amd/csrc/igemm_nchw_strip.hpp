@@ -44,23 +44,26 @@ struct NchwStripSrc {
     i32x4 rsrc;
 
     // g0: first output row (n*P + p) of the tile, t_rows its rows, np the
-    // output rows in all
+    // output rows in all; x has fewer than 2^29 elements.
+    template <int PER_C>
     __device__ __forceinline__ void init(const GemmArgs& g, int32_t g0, int32_t t_rows, int32_t np, int32_t wq,
-                                         int32_t per_c, int tid) {
-        const int64_t x_bytes = (g.M / g.PQ) * int64_t(g.C) * g.H * g.W * 4;
-        rsrc = make_rsrc(g.a, uint32_t(x_bytes < int64_t(0x7fffffff) ? x_bytes : int64_t(0x7fffffff)));
+                                         int tid) {
         const int32_t P = g.PQ / g.Q;
+        const int32_t n_img = int32_t(g.M) / g.PQ;
+        rsrc = make_rsrc(g.a, uint32_t(n_img * g.C * g.H * g.W * 4));
+        const int32_t n0 = g0 / P, p0 = g0 - n0 * P;   // image and row of the tile's first output row
+        const float rwq = 1.0f / float(wq), rP = 1.0f / float(P);
 #pragma unroll
         for (int j = 0; j < NL; ++j) {
             const int sl = j * NT + tid;
-            const int c = sl / per_c;
-            const int rem = sl - c * per_c;
-            const int t = rem / wq;
-            const int32_t gr = g0 + t;
-            const bool ok = c < 16 && t < t_rows && gr < np;
-            const int32_t n = ok ? gr / P : 0;
-            const int32_t hv = ok ? (gr - n * P) * g.sh - g.ph : 0;
-            base[j] = ((n * g.C + (ok ? c : 0)) * g.H + hv) * g.W * 4 + (ok ? rem - t * wq : 0) * 16;
+            const int c = sl / PER_C;
+            const int rem = sl - c * PER_C;
+            const int t = div_small(rem, wq, rwq);
+            const int dn = div_small(p0 + t, P, rP);
+            const bool ok = c < 16 && t < t_rows && g0 + t < np;
+            const int32_t n = n0 + dn;
+            const int32_t hv = (p0 + t - dn * P) * g.sh - g.ph;
+            base[j] = ok ? ((n * g.C + c) * g.H + hv) * g.W * 4 + (rem - t * wq) * 16 : 0;
             hrow[j] = ok ? hv : -(1 << 28);
         }
     }
@@ -104,7 +107,9 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 2) conv_nchw_f32_strip_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WGN, wn = wave - (wave / WGN) * WGN;
 
-    // x has fewer than 2^29 elements here, so pixel indices fit 32 bits.
+    // x has fewer than 2^29 elements here, so pixel indices fit 32 bits
+    // (and every index below is non-negative and far below 2^22 where
+    // div_small is used).
     const int32_t M = int32_t(g.M);
     const int tile = int(xcd_tile(blockIdx.x, gridDim.x));
     const int tile_m = tile / g.tiles_n;
@@ -121,21 +126,18 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 2) conv_nchw_f32_strip_kernel(
     const int32_t t_rows = m_last / g.Q - g0 + 1;
 
     ASrc la;
-    la.init(g, g0, t_rows, M / g.Q, wq, PER_C, tid);
+    la.template init<PER_C>(g, g0, t_rows, M / g.Q, wq, tid);
 
     // This lane's fragment pixels: float offset (strip row, first column)
     // into a strip buffer.
     int32_t pix[TM];
+    const int32_t q0 = m0 - g0 * g.Q;   // column of the tile's first pixel
+    const float rQ = 1.0f / float(g.Q);
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
-        const int32_t m = m0 + wm * WM + i * 16 + (lane & 15);
-        int32_t t = 0, q = 0;
-        if (m < M) {
-            const int32_t gr = m / g.Q;
-            t = gr - g0;
-            q = m - gr * g.Q;
-        }
-        pix[i] = t * wp + q * g.sw;
+        const int32_t rel = wm * WM + i * 16 + (lane & 15);
+        const int32_t t = div_small(q0 + rel, g.Q, rQ);
+        pix[i] = m0 + rel < M ? t * wp + (q0 + rel - t * g.Q) * g.sw : 0;
     }
 
     // Packed filter: fragment (nb, kk) at ((nb*KK + kk)*64 + lane)*16 bytes.
@@ -289,6 +291,8 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 2) conv_nchw_f32_strip_kernel(
     wait_vmcnt<0>();
 
     float* __restrict__ y = static_cast<float*>(g.y);
+    const int32_t img0 = m0 / g.PQ, pq0 = m0 - img0 * g.PQ;   // image and position of the tile's first pixel
+    const float rPQ = 1.0f / float(g.PQ);
     if ((g.PQ & 3) == 0) {
         // Output, bias added, straight from the accumulators: lane (gq, l16)
         // holds pixels m .. m+3 of channel n, contiguous in NKPQ (4-pixel
@@ -298,11 +302,11 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 2) conv_nchw_f32_strip_kernel(
             const int n = n0 + wn * WN + j * 16 + (lane & 15);
 #pragma unroll
             for (int i = 0; i < TM; ++i) {
-                const int32_t m = m0 + wm * WM + i * 16 + 4 * (lane >> 4);
-                if (n >= g.K || m >= M) continue;
-                const int32_t img = m / g.PQ;
-                const int32_t pq = m - img * g.PQ;
-                store16(y + (int64_t(img) * g.K + n) * g.PQ + pq,
+                const int32_t rel = wm * WM + i * 16 + 4 * (lane >> 4);
+                if (n >= g.K || m0 + rel >= M) continue;
+                const int32_t di = div_small(pq0 + rel, g.PQ, rPQ);
+                const int32_t pq = pq0 + rel - di * g.PQ;
+                store16(y + (int64_t(img0 + di) * g.K + n) * g.PQ + pq,
                         u32x4{__float_as_uint(acc[i][j][0] + bias_v[j]), __float_as_uint(acc[i][j][1] + bias_v[j]),
                               __float_as_uint(acc[i][j][2] + bias_v[j]), __float_as_uint(acc[i][j][3] + bias_v[j])});
             }
@@ -327,10 +331,9 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 2) conv_nchw_f32_strip_kernel(
     for (int t = tid; t < BN * BM; t += NT) {
         const int nl = t / BM, ml = t - (t / BM) * BM;
         const int n = n0 + nl;
-        const int32_t m = m0 + ml;
-        if (n >= g.K || m >= M) continue;
-        const int32_t img = m / g.PQ;
-        y[(int64_t(img) * g.K + n) * g.PQ + (m - img * g.PQ)] = smem[nl * OP + ml];
+        if (n >= g.K || m0 + ml >= M) continue;
+        const int32_t di = div_small(pq0 + ml, g.PQ, rPQ);
+        y[(int64_t(img0 + di) * g.K + n) * g.PQ + (pq0 + ml - di * g.PQ)] = smem[nl * OP + ml];
     }
 }
 

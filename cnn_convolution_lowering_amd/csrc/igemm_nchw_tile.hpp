@@ -53,13 +53,14 @@ __global__ void __launch_bounds__(256) conv_nchw_f32_tile_kernel(GemmArgs g) {
                                uint32_t(g.C * g.H * g.W * 4));
     const i32x4 wr = make_rsrc(g.b, uint32_t(g.K * Kg * 4));
     const uint32_t lds0 = lds_offset(lds);
+    const float rPWd = 1.0f / float(PWd), rrows = 1.0f / float(rows_in);
     for (int i0 = 0; i0 < total; i0 += 256) {
         const int i = i0 + tid;
         if (i >= total) continue;
         const uint32_t m0 = lds0 + uint32_t((i0 + wave * 64) * 4);
         if (i < fil0) {   // input rows, the zero plane and up to 3 pad floats (zero)
-            const int row = i / PWd, j = i - (i / PWd) * PWd;
-            const int c = row / rows_in, h = h0 + (row - (row / rows_in) * rows_in), w = j - g.pw;
+            const int row = div_small(i, PWd, rPWd), j = i - row * PWd;
+            const int c = div_small(row, rows_in, rrows), h = h0 + (row - c * rows_in), w = j - g.pw;
             const bool in = i < staged && unsigned(h) < unsigned(g.H) && unsigned(w) < unsigned(g.W);
             dma4(xr, in ? uint32_t(((c * g.H + h) * g.W + w) * 4) : kOutOfRange, m0);
         } else {
