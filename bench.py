@@ -144,10 +144,22 @@ def kernel_work(l, stage):
     return 0, w_bytes + info["ws_filter_bytes"]
 
 
+CONTRACT_KERNELS = ["conv_gemm_kernel", "conv_gemm_dma_kernel", "conv_gemm_wide_kernel", "conv_nchw_f32_dma_kernel",
+                    "conv_strip_kernel", "conv_strip_rb_kernel", "conv_nchw_f32_strip_kernel",
+                    "conv_nchw_f32_tile_kernel"]
+
+
 def kernel_symbol(l, stage):
+    """Name of the kernel a stage launches (as the kernel trace shows it)."""
     d = l["desc"]
-    return {"pack": "pack_filter_kernel", "contract": "igemm_kernel"}.get(
-        stage, "%s_%s_kernel" % (d.algo, d.layout))
+    info = d.info
+    if stage == "contract":
+        return CONTRACT_KERNELS[info["kernel"]]
+    if stage == "pack":
+        if info["kernel"] == 5:
+            return "pack_filter_frag_kernel"
+        return "pack_filter_frag_f32_kernel" if info["kernel"] == 6 else "pack_filter_kernel"
+    return "%s_%s_kernel" % (d.algo, d.layout)
 
 
 def cpu_baseline(wl, budget_s=10.0):

@@ -15,8 +15,10 @@
 // in whole 16-byte pieces from column 0, so up to three columns past W_used
 // land in the strip too (never read; past the end of x they read as zero).
 //
-// Contraction order: strip (r, channel block cb) after strip, and within a
-// strip one 16-deep step per tap s over the block's 16 channels; lane group
+// Contraction order: strip (cb, r) after strip, filter rows inner (so the
+// rows that strips of neighbouring r share are fetched again while still in
+// L2), and within a strip one 16-deep step per tap s over the block's 16
+// channels; lane group
 // gq = lane/16 takes channels 4*gq .. 4*gq+3 of the step, so the four
 // elements of a lane lie one channel plane (a compile-time pitch) apart and
 // a step's A fragment is one address add plus immediate-offset LDS reads.
@@ -183,9 +185,9 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 2) conv_nchw_f32_strip_kernel(
     };
     auto strip_advance = [&]() __attribute__((always_inline)) {
         ++next_strip;
-        if (++ncb == CBN) {
-            ncb = 0;
-            ++nsr;
+        if (++nsr == g.R) {
+            nsr = 0;
+            ++ncb;
         }
     };
 

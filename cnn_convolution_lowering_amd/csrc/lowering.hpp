@@ -323,7 +323,7 @@ struct FragPackF32Args {
 };
 
 // fp32 KCRS filter into 16x16x4 MFMA B fragments in the order of the fp32
-// NCHW strip kernel: fragment kk = (r*(C/16) + cb)*S + s is the 16-deep step
+// NCHW strip kernel: fragment kk = (cb*R + r)*S + s is the 16-deep step
 // of tap (r, s) over channels cb*16 .. cb*16+15; lane (gq, l16) element e
 // holds w[nb*16 + l16][cb*16 + 4*gq + e][r][s] (zero past K), at
 // ((nb*KK + kk)*64 + lane)*16 bytes.  C % 16 == 0.
@@ -340,7 +340,7 @@ __global__ void __launch_bounds__(256) pack_filter_frag_f32_kernel(FragPackF32Ar
         const int nb = int(blk / KK);
         const int n = nb * 16 + (lane & 15);
         const int strip = kk / a.S, s = kk - strip * a.S;
-        const int r = strip / CBN, cb = strip - r * CBN;
+        const int cb = strip / a.R, r = strip - cb * a.R;
         float v[4] = {0.f, 0.f, 0.f, 0.f};
         if (n < a.K) {
 #pragma unroll
