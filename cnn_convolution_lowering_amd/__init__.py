@@ -78,6 +78,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "conv_pack_filter": [vp, vp, vp, vp],
         "conv_lower_input": [vp, vp, vp, vp],
         "conv_contract": [vp, vp, vp, vp, vp, vp, vp],
+        "conv_lstm_create_desc": [ctypes.POINTER(ConvParams), ctypes.c_int64, ctypes.POINTER(vp)],
+        "conv_lstm_step": [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -237,6 +239,71 @@ class Conv2d:
         self._tensor(y, self.y_shape(), "y")
         _check(self.lib.conv_contract(self._desc, self._ptr(x), self._ptr(w), self._ptr(bias), self._ptr(y),
                                       self._ptr(ws), self._stream(stream, y.device)), "conv_contract")
+
+
+class ConvLSTMCell:
+    """One ConvLSTM step plan (conv_lstm_create_desc): fp32 NCHW, x (N, Cx, H,
+    W), h and c (N, Kh, H, W), gate filter w (4*Kh, Cx+Kh, R, S) in gate order
+    i, f, g, o, bias (4*Kh,).  Padding / dilation must keep H x W."""
+
+    def __init__(self, N, Cx, Kh, H, W, R, S, *, padding=0, dilation=1, algo="im2win"):
+        self.lib = load_library()
+        ph, pw = _pair(padding)
+        dh, dw = _pair(dilation)
+        if algo not in ALGOS:
+            raise ValueError("algo must be one of %s" % list(ALGOS))
+        self.N, self.Cx, self.Kh, self.H, self.W, self.R, self.S = (int(v) for v in (N, Cx, Kh, H, W, R, S))
+        self.params = ConvParams(self.N, self.Cx + self.Kh, self.H, self.W, 4 * self.Kh, self.R, self.S, 1, 1, ph, pw,
+                                 dh, dw, LAYOUTS["nchw"], DTYPES["f32"], ALGOS[algo])
+        self.algo, self.padding, self.dilation = algo, (ph, pw), (dh, dw)
+        self._desc = ctypes.c_void_p()
+        _check(self.lib.conv_lstm_create_desc(ctypes.byref(self.params), ctypes.c_int64(self.Cx),
+                                              ctypes.byref(self._desc)), "conv_lstm_create_desc")
+        info = PlanInfo()
+        _check(self.lib.conv_plan_info(self._desc, ctypes.byref(info)), "conv_plan_info")
+        self.info: Dict[str, int] = {name: getattr(info, name) for name, _ in PlanInfo._fields_}
+        self.workspace_bytes = int(self.info["ws_bytes"])
+
+    def __del__(self):
+        desc = getattr(self, "_desc", None)
+        if desc is not None and desc.value:
+            self.lib.conv_destroy_desc(desc)
+            self._desc = None
+
+    def _check_tensor(self, t, shape, what):
+        torch = _torch()
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError("%s has shape %s, expected %s" % (what, tuple(t.shape), tuple(shape)))
+        if not t.is_contiguous() or t.dtype != torch.float32:
+            raise ValueError("%s must be a contiguous float32 tensor" % what)
+
+    def new_workspace(self, device):
+        torch = _torch()
+        return None if self.workspace_bytes == 0 else torch.empty(self.workspace_bytes, dtype=torch.uint8,
+                                                                   device=device)
+
+    def step(self, x, h, c, w, bias=None, h_out=None, c_out=None, ws=None, stream=None):
+        """conv_lstm_step: returns (h_t, c_t)."""
+        torch = _torch()
+        st = (self.N, self.Kh, self.H, self.W)
+        self._check_tensor(x, (self.N, self.Cx, self.H, self.W), "x")
+        self._check_tensor(h, st, "h")
+        self._check_tensor(c, st, "c")
+        self._check_tensor(w, (4 * self.Kh, self.Cx + self.Kh, self.R, self.S), "w")
+        if bias is not None:
+            self._check_tensor(bias, (4 * self.Kh,), "bias")
+        h_out = torch.empty(st, dtype=torch.float32, device=x.device) if h_out is None else h_out
+        c_out = torch.empty(st, dtype=torch.float32, device=x.device) if c_out is None else c_out
+        self._check_tensor(h_out, st, "h_out")
+        self._check_tensor(c_out, st, "c_out")
+        if ws is None:
+            ws = self.new_workspace(x.device)
+        elif ws.numel() * ws.element_size() < self.workspace_bytes:
+            raise ValueError("workspace too small")
+        p = Conv2d._ptr
+        _check(self.lib.conv_lstm_step(self._desc, p(x), p(h), p(c), p(w), p(bias), p(h_out), p(c_out), p(ws),
+                                       Conv2d._stream(stream, x.device)), "conv_lstm_step")
+        return h_out, c_out
 
 
 _cache: Dict[tuple, Conv2d] = {}

@@ -61,7 +61,7 @@ void launch_gemm_tile(const conv_desc& d, const GemmArgs& g, hipStream_t st) {
 }
 
 template <typename T, int BM, int BN, int BK, int WGM, int WGN, int STAGES, bool WIDE, bool NHWC_OUT, class ASrc,
-          class BSrc>
+          class BSrc, int EPI = 0>
 void launch_dma_core(const conv_desc& d, GemmArgs g, hipStream_t st) {
     g.tiles_n = int32_t((d.p.K + BN - 1) / BN);
     const uint64_t tiles_m = (uint64_t(d.M) + BM - 1) / BM;
@@ -70,7 +70,7 @@ void launch_dma_core(const conv_desc& d, GemmArgs g, hipStream_t st) {
     if constexpr (WIDE)
         conv_gemm_wide_kernel<T, BM, BN, BK, WGM, WGN, STAGES, ASrc, BSrc><<<blocks, NT, 0, st>>>(g);
     else
-        conv_gemm_dma_kernel<T, BM, BN, BK, WGM, WGN, STAGES, NHWC_OUT, ASrc, BSrc><<<blocks, NT, 0, st>>>(g);
+        conv_gemm_dma_kernel<T, BM, BN, BK, WGM, WGN, STAGES, NHWC_OUT, ASrc, BSrc, EPI><<<blocks, NT, 0, st>>>(g);
 }
 
 template <typename T, int BM, int BN, int WGM, int WGN, int STRIP, int BST>

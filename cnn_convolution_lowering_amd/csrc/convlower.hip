@@ -283,6 +283,29 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d) {
     return CONV_OK;
 }
 
+// A ConvLSTM step: the gate convolution over concat(x, h) of p (C = c_x +
+// hidden channels, K = 4 * hidden, stride 1, output the size of the input),
+// fp32 NCHW, lowered (im2win or im2col) so that the lowering reads the two
+// tensors; hidden channels a multiple of 16 (64 packed gate rows per tile).
+conv_status_t plan_lstm(const conv_params_t& p, int64_t c_x, conv_desc& d) {
+    if (p.layout != CONV_NCHW || p.dtype != CONV_F32) return CONV_ERR_UNSUPPORTED;
+    if (p.algo != CONV_ALGO_IM2WIN && p.algo != CONV_ALGO_IM2COL) return CONV_ERR_UNSUPPORTED;
+    if (c_x <= 0 || p.K <= 0 || p.K % 4 != 0 || p.C != c_x + p.K / 4) return CONV_ERR_INVALID_ARG;
+    if (p.stride_h != 1 || p.stride_w != 1) return CONV_ERR_INVALID_ARG;
+    if ((p.K / 4) % 16 != 0) return CONV_ERR_UNSUPPORTED;
+    conv_status_t s = plan(p, d);
+    if (s != CONV_OK) return s;
+    if (d.P != p.H || d.Q != p.W) return CONV_ERR_INVALID_ARG;
+    if (d.bytes_low / 16 > 0xffffffffull) return CONV_ERR_UNSUPPORTED;
+    d.lstm_cx = c_x;
+    d.kernel = KERN_DMA;
+    d.variant = -1;   // the dedicated ConvLSTM tile (kLstmVariant)
+    d.tile_m = kLstmVariant.bm;
+    d.tile_n = kLstmVariant.bn;
+    d.tile_k = kLstmVariant.bk / 2;
+    return CONV_OK;
+}
+
 // ---------------------------------------------------------------- pointer checks
 
 conv_status_t check_dev(const void* ptr, size_t align) {
@@ -322,6 +345,8 @@ LowerArgs lower_args(const conv_desc& d, const void* x, void* out) {
     a.Kl = int32_t(d.Kl);
     a.chunk = d.stage_chunk;
     a.lds_ld = d.stage_ld;
+    a.x2 = nullptr;
+    a.C1 = int32_t(d.p.C);
     return a;
 }
 
@@ -347,7 +372,15 @@ void launch_pack(const conv_desc& d, const void* w, void* out, hipStream_t st) {
         }
         return;
     }
-    PackArgs a{w, out, int32_t(d.p.K), int32_t(d.p.C), int32_t(d.p.R), int32_t(d.p.S), int32_t(d.RCp), int32_t(d.Kl)};
+    PackArgs a{w,
+               out,
+               int32_t(d.p.K),
+               int32_t(d.p.C),
+               int32_t(d.p.R),
+               int32_t(d.p.S),
+               int32_t(d.RCp),
+               int32_t(d.Kl),
+               int32_t(d.lstm_cx ? d.p.K / 4 : 0)};
     const uint32_t blocks = grid_stride_blocks(uint64_t(d.p.K) * d.Kl);
     if (d.p.layout == CONV_NHWC)
         pack_filter_kernel<T, true><<<blocks, 256, 0, st>>>(a);
@@ -448,6 +481,38 @@ conv_status_t run_contract(const conv_desc& d, const void* x, const void* w, con
     return launch_status();
 }
 
+// ConvLSTM step: lowering of concat(x, h_prev), then the gate contraction
+// with the cell update.
+conv_status_t run_lstm(const conv_desc& d, const void* x, const void* h_prev, const void* c_prev, const void* bias,
+                       void* h_out, void* c_out, void* ws, hipStream_t st) {
+    if (d.p.N == 0) return CONV_OK;
+    LowerArgs a = lower_args(d, x, static_cast<char*>(ws) + d.off_low);
+    a.x2 = h_prev;
+    a.C1 = int32_t(d.lstm_cx);
+    if (d.p.algo == CONV_ALGO_IM2WIN) {
+        if (d.stage_chunk > 0) {
+            dim3 grid(uint32_t(d.p.N * d.P), uint32_t((d.W_used + d.stage_chunk - 1) / d.stage_chunk));
+            im2win_nchw_kernel<float><<<grid, 256, size_t(d.stage_chunk) * d.stage_ld * 4, st>>>(a);
+        } else {
+            const uint64_t total = d.im2win_bytes / 16;
+            lower_generic_kernel<float, false, false><<<grid_stride_blocks(total), 256, 0, st>>>(a, uint32_t(total));
+        }
+    } else {
+        const uint64_t total = uint64_t(d.M) * d.Kl / 4;
+        if (d.stage_chunk > 0) {
+            dim3 grid(uint32_t(d.p.N * d.P), uint32_t((d.Q + d.stage_chunk - 1) / d.stage_chunk));
+            const int64_t cols = int64_t(d.stage_chunk - 1) * d.p.stride_w + (d.p.S - 1) * int64_t(d.p.dil_w) + 1;
+            im2col_nchw_kernel<float><<<grid, 256, size_t(cols) * d.stage_ld * 4, st>>>(a);
+        } else {
+            lower_generic_kernel<float, false, true><<<grid_stride_blocks(total), 256, 0, st>>>(a, uint32_t(total));
+        }
+    }
+    conv_status_t s = launch_status();
+    if (s != CONV_OK) return s;
+    launch_lstm_gemm(d, bias, c_prev, h_out, c_out, ws, st);
+    return launch_status();
+}
+
 }  // namespace
 
 // ====================================================================== C ABI
@@ -466,6 +531,34 @@ conv_status_t conv_create_desc(const conv_params_t* p, conv_desc_t* out) {
     d->magic = kDescMagic;
     *out = d;
     return CONV_OK;
+}
+
+conv_status_t conv_lstm_create_desc(const conv_params_t* p, int64_t c_x, conv_desc_t* out) {
+    if (!p || !out) return CONV_ERR_NULL_PTR;
+    *out = nullptr;
+    conv_desc tmp{};
+    tmp.p = *p;
+    conv_status_t s = plan_lstm(*p, c_x, tmp);
+    if (s != CONV_OK) return s;
+    conv_desc* d = new (std::nothrow) conv_desc(tmp);
+    if (!d) return CONV_ERR_OOM;
+    d->magic = kDescMagic;
+    *out = d;
+    return CONV_OK;
+}
+
+conv_status_t conv_lstm_step(conv_desc_t d, const void* x, const void* h_prev, const void* c_prev, const void* w,
+                             const void* bias, void* h_out, void* c_out, void* ws, void* stream) {
+    if (!desc_ok(d) || d->lstm_cx == 0) return CONV_ERR_INVALID_ARG;
+    if (d->p.N == 0) return CONV_OK;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    conv_status_t s;
+    for (const void* ptr : {x, h_prev, c_prev, w, static_cast<const void*>(h_out), static_cast<const void*>(c_out)})
+        if ((s = check_dev(ptr, 16)) != CONV_OK) return s;
+    if (bias && (s = check_dev(bias, 4)) != CONV_OK) return s;
+    if ((s = check_ws(*d, ws)) != CONV_OK) return s;
+    if ((s = run_pack(*d, w, ws, st)) != CONV_OK) return s;
+    return run_lstm(*d, x, h_prev, c_prev, bias, h_out, c_out, ws, st);
 }
 
 conv_status_t conv_destroy_desc(conv_desc_t d) {
@@ -521,7 +614,7 @@ conv_status_t conv_plan_info(conv_desc_t d, conv_plan_info_t* info) {
 }
 
 conv_status_t conv_pack_filter(conv_desc_t d, const void* w, void* ws, void* stream) {
-    if (!desc_ok(d)) return CONV_ERR_INVALID_ARG;
+    if (!desc_ok(d) || d->lstm_cx) return CONV_ERR_INVALID_ARG;
     if (!(d->pack || d->frag_pack) || d->p.N == 0) return CONV_OK;
     conv_status_t s;
     if ((s = check_dev(w, 16)) != CONV_OK) return s;
@@ -530,7 +623,7 @@ conv_status_t conv_pack_filter(conv_desc_t d, const void* w, void* ws, void* str
 }
 
 conv_status_t conv_lower_input(conv_desc_t d, const void* x, void* ws, void* stream) {
-    if (!desc_ok(d)) return CONV_ERR_INVALID_ARG;
+    if (!desc_ok(d) || d->lstm_cx) return CONV_ERR_INVALID_ARG;
     if (d->elided || d->p.N == 0) return CONV_OK;
     conv_status_t s;
     if ((s = check_dev(x, 16)) != CONV_OK) return s;
@@ -540,7 +633,7 @@ conv_status_t conv_lower_input(conv_desc_t d, const void* x, void* ws, void* str
 
 conv_status_t conv_contract(conv_desc_t d, const void* x, const void* w, const void* bias, void* y, const void* ws,
                             void* stream) {
-    if (!desc_ok(d)) return CONV_ERR_INVALID_ARG;
+    if (!desc_ok(d) || d->lstm_cx) return CONV_ERR_INVALID_ARG;
     if (d->p.N == 0) return CONV_OK;
     conv_status_t s;
     if ((s = check_dev(y, 16)) != CONV_OK) return s;
@@ -553,7 +646,7 @@ conv_status_t conv_contract(conv_desc_t d, const void* x, const void* w, const v
 
 conv_status_t conv2d_fwd(conv_desc_t d, const void* x, const void* w, const void* bias, void* y, void* ws,
                          void* stream) {
-    if (!desc_ok(d)) return CONV_ERR_INVALID_ARG;
+    if (!desc_ok(d) || d->lstm_cx) return CONV_ERR_INVALID_ARG;
     if (d->p.N == 0) return CONV_OK;
     const hipStream_t st = static_cast<hipStream_t>(stream);
     conv_status_t s;

@@ -34,6 +34,9 @@ constexpr TileVariant kDmaVariants[] = {
     {128, 32, 32, 4, 1, 4}, {128, 64, 32, 2, 2, 4}, {128, 128, 32, 2, 2, 4}, {256, 128, 32, 2, 2, 3},
     {256, 128, 32, 4, 2, 4}, {256, 256, 32, 4, 2, 3}, {128, 128, 64, 2, 2, 2},
 };
+// The ConvLSTM step's contraction: 64 packed gate rows per tile, one wave
+// across them (the cell update needs all four gates of a hidden channel).
+constexpr TileVariant kLstmVariant = {128, 64, 32, 4, 1, 4};
 constexpr TileVariant kWideVariants[] = {
     {512, 128, 32, 4, 1, 4}, {512, 128, 32, 4, 1, 3}, {256, 256, 32, 2, 2, 3}, {256, 256, 32, 2, 2, 4},
     {256, 128, 32, 2, 2, 4}, {128, 128, 32, 2, 2, 4}, {256, 128, 32, 2, 1, 3}, {256, 128, 64, 2, 2, 3},
@@ -108,6 +111,7 @@ struct conv_desc {
     int32_t variant;    // index into that kernel's variant table
     int32_t tile_m, tile_n, tile_k;
     int32_t tile_rows;  // fp32 NCHW small-window kernel: output rows per workgroup
+    int64_t lstm_cx;    // ConvLSTM step descriptor: input channels taken from x (0: a plain convolution)
     // NCHW staging (0 = use the element-wise kernel)
     int32_t stage_chunk, stage_ld;
 };
@@ -118,6 +122,10 @@ namespace convlower {
 template <typename T>
 void launch_gemm(const conv_desc& d, const void* x, const void* w, const void* bias, void* y, const void* ws,
                  hipStream_t st);
+
+// The contraction of a ConvLSTM step with its cell-update epilogue (fp32).
+void launch_lstm_gemm(const conv_desc& d, const void* bias, const void* c_prev, void* h_out, void* c_out,
+                      const void* ws, hipStream_t st);
 
 extern template void launch_gemm<float>(const conv_desc&, const void*, const void*, const void*, void*,
                                         const void*, hipStream_t);

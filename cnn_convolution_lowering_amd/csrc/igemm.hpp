@@ -50,6 +50,11 @@ struct GemmArgs {
     int32_t ldb;        // filter row pitch (elements)
     int32_t tiles_n;    // ceil(K / BN)
     int32_t tile_rows;  // output rows per workgroup (fp32 NCHW small-window kernel)
+    // ConvLSTM step epilogue: y is h_t; c_prev / c_out the cell states
+    // (NCHW, lstm_kh channels); 0 for an ordinary convolution.
+    const void* c_prev;
+    void* c_out;
+    int32_t lstm_kh;
     // window loaders: the convolution itself
     int32_t C, H, W, R, S;
     int32_t sh, sw, ph, pw, dh, dw;
@@ -361,6 +366,74 @@ struct WindowElem {
         for (int j = 0; j < NV; ++j) store16(lds + row * BK + swz_chunk<BK / VEC>(row, kq * NV + j) * VEC, r[j]);
     }
 };
+
+// ConvLSTM step epilogue (fp32, NCHW), one cell update per output element;
+// "GPU-Accelerating MSCRED with CUDA, im2col, GEMM, and a Custom PyTorch
+// Extension" names the ConvLSTM stage without equations, read here as the
+// standard peephole-free cell: with the gates z = acc + bias,
+//     c_t = sigmoid(z_f) * c_prev + sigmoid(z_i) * tanh(z_g)
+//     h_t = sigmoid(z_o) * tanh(c_t).
+// The tile is BN = 64 packed gate rows (see PackArgs::lstm_kh) seen by one
+// wave (WN = 64): block j of the lane's accumulators is gate j (i, f, g, o)
+// of hidden channel n0/4 + (lane & 15), pixels m .. m+3.
+__device__ __forceinline__ float sigmoid_f32(float z) { return 1.0f / (1.0f + expf(-z)); }
+
+template <int WM, int TM, int TN>
+__device__ __forceinline__ void lstm_store_tile(const GemmArgs& g, const f32x4 (&acc)[TM][TN], int64_t m0, int n0,
+                                                int wm, int lane) {
+    static_assert(TN == 4, "one 16-column block per gate");
+    const int kh = g.lstm_kh;
+    const int hid = n0 / 4 + (lane & 15);
+    const float* __restrict__ bias = static_cast<const float*>(g.bias);
+    float bg[4];
+#pragma unroll
+    for (int gt = 0; gt < 4; ++gt) bg[gt] = bias ? bias[gt * kh + hid] : 0.f;
+    const float* __restrict__ cp = static_cast<const float*>(g.c_prev);
+    float* __restrict__ co = static_cast<float*>(g.c_out);
+    float* __restrict__ ho = static_cast<float*>(g.y);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int64_t mb = m0 + wm * WM + i * 16 + 4 * (lane >> 4);
+        if (mb >= g.M) continue;
+        float cv[4], hv[4], cprev[4];
+        const bool vec = (g.PQ & 3) == 0;   // then mb % 4 == 0: four pixels of one image, contiguous
+        int64_t off[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int64_t m = mb + e < g.M ? mb + e : mb;
+            const int32_t n = int32_t(m / g.PQ);
+            off[e] = (int64_t(n) * kh + hid) * g.PQ + (m - int64_t(n) * g.PQ);
+        }
+        if (vec) {
+            const f32x4 c4 = __builtin_bit_cast(f32x4, load16(cp + off[0]));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) cprev[e] = c4[e];
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) cprev[e] = cp[off[e]];
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float zi = acc[i][0][e] + bg[0], zf = acc[i][1][e] + bg[1];
+            const float zg = acc[i][2][e] + bg[2], zo = acc[i][3][e] + bg[3];
+            cv[e] = sigmoid_f32(zf) * cprev[e] + sigmoid_f32(zi) * tanhf(zg);
+            hv[e] = sigmoid_f32(zo) * tanhf(cv[e]);
+        }
+        if (vec) {
+            store16(co + off[0], u32x4{__float_as_uint(cv[0]), __float_as_uint(cv[1]), __float_as_uint(cv[2]),
+                                       __float_as_uint(cv[3])});
+            store16(ho + off[0], u32x4{__float_as_uint(hv[0]), __float_as_uint(hv[1]), __float_as_uint(hv[2]),
+                                       __float_as_uint(hv[3])});
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if (mb + e >= g.M) break;
+                co[off[e]] = cv[e];
+                ho[off[e]] = hv[e];
+            }
+        }
+    }
+}
 
 // Epilogue shared by the contraction kernels: y = round(acc + bias[k]),
 // stored in NPQK (NHWC_OUT) or NKPQ order.

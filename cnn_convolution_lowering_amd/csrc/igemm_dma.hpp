@@ -283,7 +283,10 @@ struct DmaRows {
 // ---------------------------------------------------------------------------
 // NT = 64*WGM*WGN threads (4 or 8 waves); two waves per SIMD either way
 // (two 4-wave or one 8-wave workgroup per CU).
-template <typename T, int BM, int BN, int BK, int WGM, int WGN, int STAGES, bool NHWC_OUT, class ASrc, class BSrc>
+// EPI 0: bias add and store; 1: the ConvLSTM cell update (fp32 NCHW, BN = 64
+// with WGN = 1).
+template <typename T, int BM, int BN, int BK, int WGM, int WGN, int STAGES, bool NHWC_OUT, class ASrc, class BSrc,
+          int EPI = 0>
 __global__ void __launch_bounds__(64 * WGM * WGN, 8 / (WGM * WGN)) conv_gemm_dma_kernel(GemmArgs g) {
     constexpr int NT = 64 * WGM * WGN;
     constexpr int NW = WGM * WGN;
@@ -391,7 +394,12 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 8 / (WGM * WGN)) conv_gemm_dma
         if (kt + STAGES - 1 < nkt) issue((kt + STAGES - 1) % STAGES);
     }
 
-    store_tile<T, BM, BN, WM, WN, TM, TN, NHWC_OUT>(g, acc, m0, n0, wm, wn, lane);
+    if constexpr (EPI == 1) {
+        static_assert(sizeof(T) == 4 && !NHWC_OUT && BN == 64 && WGN == 1, "ConvLSTM epilogue tile");
+        lstm_store_tile<WM, TM, TN>(g, acc, m0, n0, wm, lane);
+    } else {
+        store_tile<T, BM, BN, WM, WN, TM, TN, NHWC_OUT>(g, acc, m0, n0, wm, wn, lane);
+    }
 }
 
 }  // namespace convlower

@@ -104,7 +104,6 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) conv_strip_rb_kernel(GemmAr
         dma16(la.rsrc, la.voff(g, j, r, cb),
               lds0 + uint32_t(buf * STRIP_ELEMS * sizeof(T)) + uint32_t((j * NT + wave * 64) * 16));
     };
-    const int frag_row = lane & 31;
     const int frag_chunk = lane >> 5;
     auto read_a1 = [&](u32x4& fa, int i, int buf, int s, int kb) __attribute__((always_inline)) {
         const int row = srow[i] + s * g.dw;

@@ -35,14 +35,21 @@ struct LowerArgs {
     int32_t Kl;       // S*RCp
     int32_t chunk;    // strip columns (im2win NCHW) or output columns (im2col NCHW) per block
     int32_t lds_ld;   // LDS row pitch (elements) of the NCHW staging tile
+    // NCHW input split over two tensors (a ConvLSTM step's x and h): channels
+    // c < C1 come from x (C1 per image), the rest from x2 (C - C1 per image).
+    // C1 == C and x2 == nullptr for an ordinary convolution.
+    const void* x2;
+    int32_t C1;
 };
 
 // x element (n, c, h, w) in either layout, zero outside the image.
 template <typename T, bool NHWC>
 __device__ __forceinline__ T x_at(const LowerArgs& a, const T* __restrict__ x, int n, int c, int h, int w) {
     if (h < 0 || h >= a.H || w < 0 || w >= a.W) return T(0);
+    if (!NHWC && c >= a.C1)
+        return static_cast<const T*>(a.x2)[((int64_t(n) * (a.C - a.C1) + (c - a.C1)) * a.H + h) * a.W + w];
     int64_t off = NHWC ? ((int64_t(n) * a.H + h) * a.W + w) * a.C + c
-                       : ((int64_t(n) * a.C + c) * a.H + h) * a.W + w;
+                       : ((int64_t(n) * a.C1 + c) * a.H + h) * a.W + w;
     return x[off];
 }
 
@@ -263,6 +270,11 @@ struct PackArgs {
     const void* w;
     void* out;
     int32_t K, C, R, S, RCp, Kl;
+    // ConvLSTM gate filters (K = 4*lstm_kh, gate order i f g o): packed row
+    // hb*64 + gate*16 + l holds filter row gate*lstm_kh + hb*16 + l, so that a
+    // 64-row tile carries all four gates of 16 hidden channels.  0: rows in
+    // order.
+    int32_t lstm_kh;
 };
 
 template <typename T, bool NHWC>
@@ -271,7 +283,8 @@ __global__ void __launch_bounds__(256) pack_filter_kernel(PackArgs a) {
     T* out = static_cast<T*>(a.out);
     const int total = a.K * a.Kl;
     for (int i = blockIdx.x * 256 + threadIdx.x; i < total; i += gridDim.x * 256) {
-        const int k = i / a.Kl, kk = i - (i / a.Kl) * a.Kl;
+        const int kp = i / a.Kl, kk = i - (i / a.Kl) * a.Kl;
+        const int k = a.lstm_kh ? ((kp % 64) / 16) * a.lstm_kh + (kp / 64) * 16 + kp % 16 : kp;
         const int s = kk / a.RCp, t = kk - (kk / a.RCp) * a.RCp;
         T val = T(0);
         if (t < a.R * a.C) {

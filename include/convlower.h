@@ -175,6 +175,43 @@ conv_status_t conv_lower_input(conv_desc_t d, const void* x, void* ws, void* str
 conv_status_t conv_contract(conv_desc_t d, const void* x, const void* w, const void* bias, void* y,
                             const void* ws, void* stream);
 
+/* ---------------------------------------------------------------- ConvLSTM step
+ * "GPU-Accelerating MSCRED with CUDA, im2col, GEMM, and a Custom PyTorch
+ * Extension", sections "MSCRED and ConvLSTM Architecture" and "Why the
+ * Encoder Improved More Than ConvLSTM": after the encoder, ConvLSTM layers
+ * carry the encoded maps through time and become the bottleneck.  The pages
+ * give no cell equations; this library reads the cell as the standard one
+ * without peepholes, its four gates from one convolution over the channel
+ * concatenation of the step's input and the previous hidden state:
+ *   z   = conv(concat(x, h_prev), w) + bias     (4*Kh channels, order i, f, g, o)
+ *   c_t = sigmoid(z_f) * c_prev + sigmoid(z_i) * tanh(z_g)
+ *   h_t = sigmoid(z_o) * tanh(c_t)
+ * The gate convolution runs through this library's lowering (im2win or
+ * im2col, reading x and h_prev in place of their concatenation) and MFMA
+ * contraction; the cell update is fused into the contraction's epilogue. */
+
+/* Plan a ConvLSTM step.  p describes the gate convolution: C = c_x + Kh
+ * input channels (c_x from x, Kh from h_prev), K = 4*Kh, stride 1, and
+ * padding / dilation that keep the output H x W; layout CONV_NCHW, dtype
+ * CONV_F32, algo CONV_ALGO_IM2WIN or CONV_ALGO_IM2COL.  Kh must be a multiple
+ * of 16.  Host only; CONV_ERR_INVALID_ARG for inconsistent sizes,
+ * CONV_ERR_UNSUPPORTED for another layout, dtype or algorithm.  The
+ * descriptor is used with conv_lstm_step (the plain-convolution entry points
+ * reject it) and conv_workspace_size / conv_output_dims / conv_plan_info /
+ * conv_destroy_desc. */
+conv_status_t conv_lstm_create_desc(const conv_params_t* p, int64_t c_x, conv_desc_t* out);
+
+/* One ConvLSTM step on `stream`; device pointers, caller-owned, NCHW fp32,
+ * 16-byte aligned (bias 4-byte):
+ *   x       N*c_x*H*W             h_prev, c_prev   N*Kh*H*W
+ *   w       4*Kh*(c_x+Kh)*R*S (KCRS, gate blocks in the order i, f, g, o)
+ *   bias    4*Kh, or NULL
+ *   h_out, c_out   N*Kh*H*W, fully overwritten; must not alias the inputs
+ *   ws      at least conv_workspace_size bytes
+ * N == 0 enqueues nothing. */
+conv_status_t conv_lstm_step(conv_desc_t d, const void* x, const void* h_prev, const void* c_prev, const void* w,
+                             const void* bias, void* h_out, void* c_out, void* ws, void* stream);
+
 /* Static English text for a status code. */
 const char* conv_status_string(conv_status_t s);
 

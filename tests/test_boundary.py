@@ -256,3 +256,28 @@ def test_kernel_override_is_host_only_and_checked(monkeypatch):
     for bad in ("strip", "strip:99", "bogus:1", ":", "dma:-1"):
         monkeypatch.setenv("CONVLOWER_KERNEL", bad)
         assert plan() == default
+
+
+def test_lstm_descriptor_validation_and_entry_separation():
+    """ConvLSTM descriptors: sizes checked on the host; the plain-convolution
+    entry points and conv_lstm_step reject each other's descriptors before
+    touching any pointer."""
+    import ctypes
+    lib = cl.load_library()
+    cell = cl.ConvLSTMCell(2, 32, 32, 30, 30, 3, 3, padding=1)
+    assert cell.info["ws_lowered_bytes"] > 0 and cell.info["ws_filter_bytes"] == 128 * 64 * 9 * 4
+    fake = ctypes.c_void_p(1 << 20)
+    assert lib.conv2d_fwd(cell._desc, fake, fake, None, fake, fake, None) == -1
+    plain = cl.Conv2d(2, 64, 30, 30, 128, 3, 3, padding=1, layout="nchw", dtype="f32")
+    assert lib.conv_lstm_step(plain.handle, fake, fake, fake, fake, None, fake, fake, fake, None) == -1
+    bad = [dict(Kh=8), dict(pad=0), dict(algo="implicit")]
+    for b in bad:
+        kw = dict(Kh=32, pad=1, algo="im2win")
+        kw.update(b)
+        with pytest.raises(cl.ConvError):
+            cl.ConvLSTMCell(2, 32, kw["Kh"], 30, 30, 3, 3, padding=kw["pad"], algo=kw["algo"])
+    p = cl.ConvParams(2, 64, 30, 30, 128, 3, 3, 1, 1, 1, 1, 1, 1, 0, 0, 0)
+    d = ctypes.c_void_p()
+    assert lib.conv_lstm_create_desc(ctypes.byref(p), 31, ctypes.byref(d)) == -1   # C != c_x + K/4
+    p.layout = 1
+    assert lib.conv_lstm_create_desc(ctypes.byref(p), 32, ctypes.byref(d)) == -2   # NHWC unsupported
