@@ -34,8 +34,16 @@ METRIC = "conv2d fwd TFLOPS and % of MFMA peak; workspace bytes vs im2col"
 # MI355X published peaks: dense MFMA per storage type, HBM3E bandwidth
 PEAK_TFLOPS = {"f32": 157.3, "f16": 2516.6, "bf16": 2516.6}
 PEAK_HBM_GBS = 8000.0
+# ConvLSTM step measured beside the stack (--workload lstm): one cell per
+# encoder level of c2 (hidden channels = the level's channels, 3x3 gate
+# filter, same padding), 256 windows, 5 time steps per pass.
+LSTM_LEVELS = [(32, 30), (64, 14), (128, 7), (256, 3)]   # (channels, H = W)
+LSTM_WINDOWS, LSTM_STEPS = 256, 5
 WORKLOAD_TEXT = {
     "c1": "single conv2d fp32 NCHW N=1 3x30x30, 3x3 3->32 s1 p1",
+    "lstm": "ConvLSTM cells over the four c2 encoder levels (32x30x30, 64x14x14, 128x7x7, 256x3x3), fp32 "
+            "NCHW, 256 windows, 5 time steps, gates from a 3x3 same-padded convolution over concat(x_t, "
+            "h_t-1), cell update fused into the contraction",
     "c2": "MSCRED-style encoder stack fp32 NCHW N=1280 (256 windows x 5 steps) of 3x30x30 symmetric signature "
           "matrices: 3x3 3->32 s1p1; 3x3 32->64 s2; 2x2 64->128 s2; 2x2 128->256 s2",
     "c3": "ResNet-style 3x3 fp16 NHWC N=64 C=K=256 14x14 s1 p1",
@@ -199,6 +207,87 @@ def cpu_baseline(wl, budget_s=10.0):
                       % (n, spec.N, spec.name, len(wl.layers), t)}
 
 
+def bench_lstm(args, dev):
+    """ConvLSTM passes: LSTM_STEPS time steps of the cell at every level,
+    h and c carried on the GPU; the value counts the gate convolutions'
+    flops.  The dominant level's conv_lstm_step call (pack, lowering,
+    contraction) is timed with HIP events inside the timed region."""
+    import torch
+    import cnn_convolution_lowering_amd as cl
+    g = torch.Generator().manual_seed(5)
+    levels = []
+    for ch, hw in LSTM_LEVELS:
+        cell = cl.ConvLSTMCell(LSTM_WINDOWS, ch, ch, hw, hw, 3, 3, padding=1, algo=args.algo)
+        xs = [(torch.rand(LSTM_WINDOWS, ch, hw, hw, generator=g) * 2 - 1).to(dev) for _ in range(LSTM_STEPS)]
+        w = (torch.randn(4 * ch, 2 * ch, 3, 3, generator=g) / (18 * ch) ** 0.5).to(dev)
+        b = (torch.randn(4 * ch, generator=g) * 0.01).to(dev)
+        st = [torch.zeros(LSTM_WINDOWS, ch, hw, hw, device=dev) for _ in range(4)]   # h, c, h', c'
+        flops = 2.0 * LSTM_WINDOWS * 4 * ch * hw * hw * 2 * ch * 9
+        levels.append({"cell": cell, "xs": xs, "w": w, "b": b, "st": st, "ws": cell.new_workspace(dev),
+                       "flops": flops, "ch": ch, "hw": hw})
+    step_flops = sum(l["flops"] for l in levels) * LSTM_STEPS
+    dom = max(range(len(levels)), key=lambda i: levels[i]["flops"])
+
+    def one_pass(rec=None):
+        for i, l in enumerate(levels):
+            h, c, h2, c2 = l["st"]
+            for t in range(LSTM_STEPS):
+                if rec is not None and i == dom and t == 0:
+                    rec[0].record()
+                l["cell"].step(l["xs"][t], h, c, l["w"], l["b"], h_out=h2, c_out=c2, ws=l["ws"])
+                if rec is not None and i == dom and t == 0:
+                    rec[1].record()
+                h, c, h2, c2 = h2, c2, h, c
+
+    for _ in range(args.warmup):
+        one_pass()
+    torch.cuda.synchronize()
+    recs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(args.steps):
+        one_pass(recs[i])
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    dom_ms = sum(a.elapsed_time(b) for a, b in recs) / args.steps
+    achieved = levels[dom]["flops"] / (dom_ms * 1e-3) / 1e12
+    out = {"metric": "ConvLSTM step gate-convolution TFLOP/s", "value": step_flops / (ms * 1e-3) / 1e12,
+           "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+           "config": {"workload": "lstm: " + WORKLOAD_TEXT["lstm"], "algo": args.algo},
+           "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_TFLOPS["f32"], "unit": "TFLOP/s",
+                        "frac": achieved / PEAK_TFLOPS["f32"], "traffic": None,
+                        "kernel": "conv_lstm_step (pack, lowering, conv_gemm_dma_kernel with the cell epilogue)",
+                        "level": "%dx%dx%d" % (levels[dom]["ch"], levels[dom]["hw"], levels[dom]["hw"]),
+                        "avg_launch_ms": dom_ms}}
+    if not args.no_cpu_baseline:
+        import numpy as np
+        from oracle.convlstm import convlstm_step
+        l = levels[0]
+
+        def run(n):
+            x = l["xs"][0][:n].cpu()
+            h = torch.zeros(n, l["ch"], l["hw"], l["hw"])
+            t = time.perf_counter()
+            convlstm_step(x, h, h, l["w"].cpu(), l["b"].cpu(), padding=1)
+            return time.perf_counter() - t
+
+        n = 2
+        dt = run(n)
+        m = int(min(LSTM_WINDOWS, max(n, n * args.cpu_budget / max(dt, 1e-6))))
+        if m > n:
+            n, dt = m, run(m)
+        import oracle
+        out["cpu_baseline"] = {"value": l["flops"] * n / LSTM_WINDOWS / dt / 1e12, "unit": "TFLOP/s",
+                               "cores": oracle.default_threads(), "kind": "oracle",
+                               "sample": "%d of %d windows, one step of the 32x30x30 level, fp64 reference, %.2f s"
+                                         % (n, LSTM_WINDOWS, dt)}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def time_steps(wl, dev, algo, steps, warmup, layer=None):
     """ms per step of the whole path with one lowering, HIP events on the
     current stream; also the largest workspace of its layers."""
@@ -285,6 +374,10 @@ def main(argv=None):
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_per_launch": n, "launches": 5}))
         return 0
+    if args.workload == "lstm":
+        if args.algo == "implicit":
+            args.algo = "im2win"   # the ConvLSTM step reads x and h through the lowering
+        return bench_lstm(args, dev)
     wl = make_workload(args.workload)
     spec = wl.spec
     print("bench: workload %s, algo %s, building inputs" % (spec.name, args.algo), file=sys.stderr, flush=True)
