@@ -344,6 +344,8 @@ def main(argv=None):
     ap.add_argument("--only-algo", action="store_true", help="time only --algo")
     ap.add_argument("--layer", type=int, default=None,
                     help="time only this layer of the workload (chained inputs are still computed once)")
+    ap.add_argument("--tune", action="store_true",
+                    help="conv_tune every layer (kernel and tile variant) before timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of reference work to time")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -383,6 +385,14 @@ def main(argv=None):
     print("bench: workload %s, algo %s, building inputs" % (spec.name, args.algo), file=sys.stderr, flush=True)
     layers, ws = build_layers(wl, dev, args.algo)
     stream = torch.cuda.current_stream(dev)
+    tuned = None
+    if args.tune:
+        print("bench: tuning the layers' kernels", file=sys.stderr, flush=True)
+        tuned = []
+        for l in layers:   # in order: a chained layer's input is its producer's output
+            r = l["desc"].tune(l["x"], l["w"], l["b"], l["y"], ws, reps=5)
+            tuned.append({"layer": l["spec"].label, "kernel": r["kernel"], "variant": r["kernel_variant"],
+                          "candidates": r["candidates"], "default_ms": r["default_ms"], "best_ms": r["best_ms"]})
     if args.layer is not None:
         # inputs of a chained layer come from one pass of the layers before it
         for l in layers[:args.layer]:
@@ -475,6 +485,9 @@ def main(argv=None):
                       "ratio_max_over_layers": max(p["ws_vs_im2col"] for p in per_layer)},
         "layers": per_layer,
     }
+    if tuned is not None:
+        out["config"]["tuned"] = True
+        out["tuning"] = tuned
     if not args.only_algo:
         flops_total = step_flops
         algos = {}

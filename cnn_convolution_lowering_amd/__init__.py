@@ -55,6 +55,11 @@ class PlanInfo(ctypes.Structure):
                 ("elem_bytes", ctypes.c_int32), ("kernel", ctypes.c_int32), ("kernel_variant", ctypes.c_int32)]
 
 
+class TuneResult(ctypes.Structure):
+    _fields_ = [("candidates", ctypes.c_int32), ("kernel", ctypes.c_int32), ("kernel_variant", ctypes.c_int32),
+                ("default_ms", ctypes.c_float), ("best_ms", ctypes.c_float)]
+
+
 _lib = None
 
 
@@ -80,6 +85,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "conv_contract": [vp, vp, vp, vp, vp, vp, vp],
         "conv_lstm_create_desc": [ctypes.POINTER(ConvParams), ctypes.c_int64, ctypes.POINTER(vp)],
         "conv_lstm_step": [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
+        "conv_tune": [vp, vp, vp, vp, vp, vp, ctypes.c_size_t, ctypes.c_int32, vp, ctypes.POINTER(TuneResult)],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -224,6 +230,26 @@ class Conv2d:
         _check(self.lib.conv2d_fwd(self._desc, self._ptr(x), self._ptr(w), self._ptr(bias), self._ptr(y),
                                    self._ptr(ws), self._stream(stream, x.device)), "conv2d_fwd")
         return y
+
+    def tune(self, x, w, bias=None, y=None, ws=None, reps=5, stream=None):
+        """conv_tune: time every kernel / tile variant that takes this
+        convolution (within the workspace given) and keep the fastest.
+        Returns the result as a dict; refreshes ``info``."""
+        self._tensor(x, self.x_shape(), "x")
+        self._tensor(w, self.w_shape(), "w")
+        self._tensor(bias, (self.params.K,), "bias")
+        y = self.new_output(x.device) if y is None else self._tensor(y, self.y_shape(), "y")
+        ws = self._ws(ws, x.device)
+        ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+        res = TuneResult()
+        _check(self.lib.conv_tune(self._desc, self._ptr(x), self._ptr(w), self._ptr(bias), self._ptr(y),
+                                  self._ptr(ws), ws_bytes, int(reps), self._stream(stream, x.device),
+                                  ctypes.byref(res)), "conv_tune")
+        info = PlanInfo()
+        _check(self.lib.conv_plan_info(self._desc, ctypes.byref(info)), "conv_plan_info")
+        self.info = {name: getattr(info, name) for name, _ in PlanInfo._fields_}
+        self.workspace_bytes = int(self.info["ws_bytes"])
+        return {name: getattr(res, name) for name, _ in TuneResult._fields_}
 
     def pack_filter(self, w, ws, stream=None):
         self._tensor(w, self.w_shape(), "w")

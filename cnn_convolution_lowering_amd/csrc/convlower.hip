@@ -10,6 +10,7 @@
 
 #include <algorithm>
 #include <cstdint>
+#include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <new>
@@ -39,7 +40,9 @@ conv_status_t from_hip(hipError_t e) { return e == hipSuccess ? CONV_OK : CONV_E
 
 // ---------------------------------------------------------------- planning
 
-conv_status_t plan(const conv_params_t& p, conv_desc& d) {
+// force: "<kernel>:<variant>" (the tuning override), or nullptr for the
+// default choice.
+conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force) {
     if (p.N < 0 || p.C <= 0 || p.H <= 0 || p.W <= 0 || p.K <= 0 || p.R <= 0 || p.S <= 0) return CONV_ERR_INVALID_ARG;
     if (p.stride_h <= 0 || p.stride_w <= 0 || p.dil_h <= 0 || p.dil_w <= 0 || p.pad_h < 0 || p.pad_w < 0)
         return CONV_ERR_INVALID_ARG;
@@ -185,9 +188,9 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d) {
         d.kernel = KERN_REG;
         d.variant = p.K <= 32 ? 2 : (p.K <= 64 ? 1 : 0);
     }
-    // Tuning override: CONVLOWER_KERNEL="<kernel>:<variant>" with kernel one
-    // of reg, dma, wide, nchw, where that kernel takes this convolution.
-    if (const char* v = std::getenv("CONVLOWER_KERNEL")) {
+    // Forced choice "<kernel>:<variant>" with kernel one of the names in
+    // kKernelFamilies, applied where that kernel takes this convolution.
+    if (const char* v = force) {
         const char* colon = std::strchr(v, ':');
         if (colon) {
             const std::string name(v, colon - v);
@@ -283,6 +286,24 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d) {
     return CONV_OK;
 }
 
+// Names of the contraction kernels for forced choices, with their variant
+// counts (the candidates conv_tune times).
+struct KernelFamily {
+    const char* name;
+    int kernel;
+    int variants;
+};
+constexpr KernelFamily kKernelFamilies[] = {
+    {"reg", KERN_REG, count_of(kRegVariants)},
+    {"dma", KERN_DMA, count_of(kDmaVariants)},
+    {"wide", KERN_WIDE, count_of(kWideVariants)},
+    {"nchw", KERN_NCHW, count_of(kNchwVariants)},
+    {"strip", KERN_STRIP, count_of(kStripVariants)},
+    {"striprb", KERN_STRIP_RB, count_of(kStripRbVariants)},
+    {"nchwstrip", KERN_NCHW_STRIP, count_of(kNchwStripVariants)},
+    {"nchwtile", KERN_NCHW_TILE, count_of(kNchwTileVariants)},
+};
+
 // A ConvLSTM step: the gate convolution over concat(x, h) of p (C = c_x +
 // hidden channels, K = 4 * hidden, stride 1, output the size of the input),
 // fp32 NCHW, lowered (im2win or im2col) so that the lowering reads the two
@@ -293,7 +314,7 @@ conv_status_t plan_lstm(const conv_params_t& p, int64_t c_x, conv_desc& d) {
     if (c_x <= 0 || p.K <= 0 || p.K % 4 != 0 || p.C != c_x + p.K / 4) return CONV_ERR_INVALID_ARG;
     if (p.stride_h != 1 || p.stride_w != 1) return CONV_ERR_INVALID_ARG;
     if ((p.K / 4) % 16 != 0) return CONV_ERR_UNSUPPORTED;
-    conv_status_t s = plan(p, d);
+    conv_status_t s = plan(p, d, nullptr);
     if (s != CONV_OK) return s;
     if (d.P != p.H || d.Q != p.W) return CONV_ERR_INVALID_ARG;
     if (d.bytes_low / 16 > 0xffffffffull) return CONV_ERR_UNSUPPORTED;
@@ -524,7 +545,7 @@ conv_status_t conv_create_desc(const conv_params_t* p, conv_desc_t* out) {
     *out = nullptr;
     conv_desc tmp{};
     tmp.p = *p;
-    conv_status_t s = plan(*p, tmp);
+    conv_status_t s = plan(*p, tmp, std::getenv("CONVLOWER_KERNEL"));
     if (s != CONV_OK) return s;
     conv_desc* d = new (std::nothrow) conv_desc(tmp);
     if (!d) return CONV_ERR_OOM;
@@ -659,6 +680,79 @@ conv_status_t conv2d_fwd(conv_desc_t d, const void* x, const void* w, const void
     if ((s = run_pack(*d, w, ws, st)) != CONV_OK) return s;
     if ((s = run_lower(*d, x, ws, st)) != CONV_OK) return s;
     return run_contract(*d, x, w, bias, y, ws, st);
+}
+
+conv_status_t conv_tune(conv_desc_t d, const void* x, const void* w, const void* bias, void* y, void* ws,
+                        size_t ws_bytes, int32_t reps, void* stream, conv_tune_result_t* result) {
+    if (!desc_ok(d) || d->lstm_cx || reps < 1) return CONV_ERR_INVALID_ARG;
+    if (!result) return CONV_ERR_NULL_PTR;
+    *result = conv_tune_result_t{};
+    result->kernel = d->kernel;
+    result->kernel_variant = d->variant;
+    if (d->p.N == 0) return CONV_OK;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    conv_status_t s;
+    if ((s = check_dev(x, 16)) != CONV_OK) return s;
+    if ((s = check_dev(w, 16)) != CONV_OK) return s;
+    if ((s = check_dev(y, 16)) != CONV_OK) return s;
+    if (bias && (s = check_dev(bias, size_t(d->elem))) != CONV_OK) return s;
+    if (ws_bytes < d->ws_bytes) return CONV_ERR_INVALID_ARG;
+    if (ws_bytes && (s = check_dev(ws, 16)) != CONV_OK) return s;
+
+    hipEvent_t e0, e1;
+    if (hipEventCreate(&e0) != hipSuccess) return CONV_ERR_HIP;
+    if (hipEventCreate(&e1) != hipSuccess) {
+        (void)hipEventDestroy(e0);
+        return CONV_ERR_HIP;
+    }
+    // ms per call of one plan: one untimed call, then reps timed ones.
+    auto time_plan = [&](const conv_desc& c, float* ms) -> conv_status_t {
+        conv_status_t r;
+        for (int i = 0; i <= reps; ++i) {
+            if (i == 1 && hipEventRecord(e0, st) != hipSuccess) return CONV_ERR_HIP;
+            if ((r = run_pack(c, w, ws, st)) != CONV_OK) return r;
+            if ((r = run_lower(c, x, ws, st)) != CONV_OK) return r;
+            if ((r = run_contract(c, x, w, bias, y, ws, st)) != CONV_OK) return r;
+        }
+        if (hipEventRecord(e1, st) != hipSuccess || hipEventSynchronize(e1) != hipSuccess) return CONV_ERR_HIP;
+        float t = 0.f;
+        if (hipEventElapsedTime(&t, e0, e1) != hipSuccess) return CONV_ERR_HIP;
+        *ms = t / float(reps);
+        return CONV_OK;
+    };
+    conv_desc best = *d;
+    float best_ms = 0.f;
+    s = time_plan(*d, &best_ms);
+    result->default_ms = best_ms;
+    int n = 1;
+    for (const KernelFamily& f : kKernelFamilies) {
+        for (int v = 0; v < f.variants && s == CONV_OK; ++v) {
+            char force[32];
+            std::snprintf(force, sizeof(force), "%s:%d", f.name, v);
+            conv_desc c{};
+            c.p = d->p;
+            if (plan(d->p, c, force) != CONV_OK || c.kernel != f.kernel || c.variant != v) continue;
+            if (c.ws_bytes > ws_bytes || (c.kernel == d->kernel && c.variant == d->variant)) continue;
+            float ms = 0.f;
+            s = time_plan(c, &ms);
+            ++n;
+            if (s == CONV_OK && ms < best_ms) {
+                best = c;
+                best_ms = ms;
+            }
+        }
+    }
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    if (s != CONV_OK) return s;
+    const uint32_t magic = d->magic;
+    *d = best;
+    d->magic = magic;
+    result->candidates = n;
+    result->kernel = d->kernel;
+    result->kernel_variant = d->variant;
+    result->best_ms = best_ms;
+    return CONV_OK;
 }
 
 const char* conv_status_string(conv_status_t s) {

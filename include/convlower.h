@@ -212,6 +212,33 @@ conv_status_t conv_lstm_create_desc(const conv_params_t* p, int64_t c_x, conv_de
 conv_status_t conv_lstm_step(conv_desc_t d, const void* x, const void* h_prev, const void* c_prev, const void* w,
                              const void* bias, void* h_out, void* c_out, void* ws, void* stream);
 
+/* ---------------------------------------------------------------- tile choice
+ * The pages sweep tile sizes and thread-block shapes ("GPU-Accelerating
+ * MSCRED ...", section "CUDA Kernel Design"; the im2win abstract) without
+ * fixing a rule.  conv_tune times, on the caller's tensors, the descriptor's
+ * current plan and every other compiled contraction kernel and tile variant
+ * that takes its convolution and whose workspace fits ws_bytes, and keeps the
+ * fastest in d. */
+typedef struct {
+    int32_t candidates;       /* plans timed, the current one included */
+    int32_t kernel;           /* the plan kept (conv_plan_info_t numbering) */
+    int32_t kernel_variant;
+    float default_ms;         /* ms per conv2d_fwd-equivalent call, the plan d had on entry */
+    float best_ms;            /* ms per call of the plan kept */
+} conv_tune_result_t;
+
+/* Tune d (not a ConvLSTM descriptor) with reps timed calls per candidate, on
+ * `stream`, with the same pointer rules as conv2d_fwd; ws_bytes is the size
+ * of ws (at least conv_workspace_size(d)).  Blocks the calling thread until
+ * the timings are in.  On return y holds the output of the last candidate
+ * run, d may need a different (never larger than ws_bytes) workspace --
+ * query conv_workspace_size again -- and *result says what was kept.  d must
+ * not be used by any other call while it is tuned; afterwards it is
+ * immutable again.  Errors as conv2d_fwd, CONV_ERR_INVALID_ARG for reps < 1
+ * or ws_bytes below the current workspace size. */
+conv_status_t conv_tune(conv_desc_t d, const void* x, const void* w, const void* bias, void* y, void* ws,
+                        size_t ws_bytes, int32_t reps, void* stream, conv_tune_result_t* result);
+
 /* Static English text for a status code. */
 const char* conv_status_string(conv_status_t s);
 

@@ -281,3 +281,19 @@ def test_lstm_descriptor_validation_and_entry_separation():
     assert lib.conv_lstm_create_desc(ctypes.byref(p), 31, ctypes.byref(d)) == -1   # C != c_x + K/4
     p.layout = 1
     assert lib.conv_lstm_create_desc(ctypes.byref(p), 32, ctypes.byref(d)) == -2   # NHWC unsupported
+
+
+def test_tune_argument_checks_on_the_host():
+    import ctypes
+    lib = cl.load_library()
+    d = cl.Conv2d(2, 16, 8, 8, 16, 3, 3, padding=1, layout="nchw", dtype="f32")
+    res = cl.TuneResult()
+    fake = ctypes.c_void_p(1 << 20)
+    assert lib.conv_tune(d.handle, fake, fake, None, fake, fake, 1 << 30, 0, None, ctypes.byref(res)) == -1
+    assert lib.conv_tune(d.handle, fake, fake, None, fake, fake, 1 << 30, 3, None, None) == -3
+    cell = cl.ConvLSTMCell(2, 16, 16, 8, 8, 3, 3, padding=1)
+    assert lib.conv_tune(cell.handle if hasattr(cell, "handle") else cell._desc, fake, fake, None, fake, fake,
+                         1 << 30, 3, None, ctypes.byref(res)) == -1
+    empty = cl.Conv2d(0, 16, 8, 8, 16, 3, 3, padding=1, layout="nchw", dtype="f32")
+    assert lib.conv_tune(empty.handle, None, None, None, None, None, 0, 3, None, ctypes.byref(res)) == 0
+    assert (res.kernel, res.kernel_variant) == (empty.info["kernel"], empty.info["kernel_variant"])

@@ -142,3 +142,33 @@ def test_forced_kernel_integer_exact(dev, monkeypatch):
         torch.cuda.synchronize()
         assert torch.equal(y.cpu().view(torch.int16), want.view(torch.int16)), forced
 
+
+
+@pytest.mark.parametrize("case", [
+    ("f32", "nchw", (64, 32, 30, 30, 64, 3, 3, (2, 2), (0, 0), (1, 1))),
+    ("f32", "nchw", (16, 3, 30, 30, 32, 3, 3, (1, 1), (1, 1), (1, 1))),
+    ("f16", "nhwc", (4, 128, 32, 32, 128, 3, 3, (1, 1), (1, 1), (1, 1))),
+    ("bf16", "nhwc", (8, 64, 14, 14, 96, 3, 3, (1, 1), (1, 1), (1, 1))),
+], ids=lambda c: "%s-%s" % c[:2])
+def test_tune_keeps_a_correct_plan(dev, monkeypatch, case):
+    """conv_tune times the candidates and keeps the fastest; the kept plan
+    still matches the oracle, and is never slower than the default it timed."""
+    monkeypatch.delenv("CONVLOWER_KERNEL", raising=False)
+    dt, lay, (N, C, H, W, K, R, S, st, pd, dl) = case
+    d = cl.Conv2d(N, C, H, W, K, R, S, stride=st, padding=pd, dilation=dl, layout=lay, dtype=dt, algo="implicit")
+    g = torch.Generator().manual_seed(61)
+    x = (torch.rand(N, C, H, W, generator=g) * 2 - 1).to(TORCH_DT[dt])
+    w = (torch.randn(K, C, R, S, generator=g) / np.sqrt(C * R * S)).to(TORCH_DT[dt])
+    b = (torch.randn(K, generator=g) * 0.1).to(TORCH_DT[dt])
+    xl, wl = _perm(x, lay), _perm(w, lay)
+    xd, wd, bd = xl.to(dev), wl.to(dev), b.to(dev)
+    ws = torch.empty(max(d.workspace_bytes, 8 << 20), dtype=torch.uint8, device=dev)
+    print("tune %s %s %s" % (dt, lay, case[2]), flush=True)
+    r = d.tune(xd, wd, bd, ws=ws, reps=3)
+    assert r["candidates"] >= 2 and r["best_ms"] <= r["default_ms"]
+    assert (r["kernel"], r["kernel_variant"]) == (d.info["kernel"], d.info["kernel_variant"])
+    assert d.workspace_bytes <= ws.numel()
+    y = d.forward(xd, wd, bd, ws=ws)
+    torch.cuda.synchronize()
+    ref, yabs = oracle.conv2d(xl, wl, b, layout=lay, stride=st, padding=pd, dilation=dl, with_abs=True)
+    assert_parity(to_f64(y.cpu()), ref, yabs, dt, "tuned %s" % (r,))
