@@ -154,7 +154,7 @@ def kernel_work(l, stage):
 
 CONTRACT_KERNELS = ["conv_gemm_kernel", "conv_gemm_dma_kernel", "conv_gemm_wide_kernel", "conv_nchw_f32_dma_kernel",
                     "conv_strip_kernel", "conv_strip_rb_kernel", "conv_nchw_f32_strip_kernel",
-                    "conv_nchw_f32_tile_kernel"]
+                    "conv_nchw_f32_tile_kernel", "conv_nhwc_tile16_kernel"]
 
 
 def kernel_symbol(l, stage):
@@ -166,7 +166,8 @@ def kernel_symbol(l, stage):
     if stage == "pack":
         if info["kernel"] == 5:
             return "pack_filter_frag_kernel"
-        return "pack_filter_frag_f32_kernel" if info["kernel"] == 6 else "pack_filter_kernel"
+        return {6: "pack_filter_frag_f32_kernel", 8: "pack_filter_tile16_kernel"}.get(info["kernel"],
+                                                                                    "pack_filter_kernel")
     return "%s_%s_kernel" % (d.algo, d.layout)
 
 

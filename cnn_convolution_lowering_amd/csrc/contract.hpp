@@ -13,6 +13,7 @@
 #include "igemm_nchw_tile.hpp"
 #include "igemm_strip.hpp"
 #include "igemm_strip_rb.hpp"
+#include "igemm_tile16.hpp"
 #include "igemm_wide.hpp"
 
 namespace convlower {
@@ -249,6 +250,33 @@ void launch_gemm(const conv_desc& d, const void* x, const void* w, const void* b
                 default: break;
             }
 #undef CONVLOWER_NCHW_TILE_CASE
+        }
+        return;
+    }
+    if (d.kernel == KERN_TILE16) {
+        if constexpr (sizeof(T) == 2) {
+            GemmArgs h = g;
+            h.tile_rows = d.tile_rows;
+            const int64_t P = d.P, TP = d.tile_rows;
+            const uint32_t blocks = uint32_t(d.p.N * ((P + TP - 1) / TP));
+            const int64_t rows_in = (TP - 1) * d.p.stride_h + (d.p.R - 1) * d.p.dil_h + 1;
+            const Tile16Geom geo = tile16_geom(int(d.p.C), int(d.p.S), int(d.p.pad_w));
+            const size_t lds = size_t(rows_in * ((d.Q - 1) * d.p.stride_w * d.p.C + 8 * geo.cpr) * 2);
+#define CONVLOWER_TILE16_CASE(I)                                                                               \
+    case I:                                                                                                    \
+        conv_nhwc_tile16_kernel<T, kTile16Variants[I].ks, kTile16Variants[I].tn><<<blocks, 256, lds, st>>>(h); \
+        break;
+            switch (d.variant) {
+                CONVLOWER_TILE16_CASE(0)
+                CONVLOWER_TILE16_CASE(1)
+                CONVLOWER_TILE16_CASE(2)
+                CONVLOWER_TILE16_CASE(3)
+                CONVLOWER_TILE16_CASE(4)
+                CONVLOWER_TILE16_CASE(5)
+                CONVLOWER_TILE16_CASE(6)
+                default: break;
+            }
+#undef CONVLOWER_TILE16_CASE
         }
         return;
     }

@@ -138,6 +138,28 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force) {
         const int64_t rows = (v.bm - 1) / d.Q + 2;
         return wide_ok && p.S >= 2 && rows * d.W_used * 4 <= v.strip;
     };
+    // 16-bit NHWC small windows: unit horizontal dilation, every staged
+    // word and window run 4-byte aligned ((C*sw) and (W*C) even), a window
+    // row of at most 256 elements, and one image within 32-bit offsets.
+    const bool tile16_ok = implicit && nhwc && p.dtype != CONV_F32 && p.dil_w == 1 &&
+                           (p.C * int64_t(p.stride_w)) % 2 == 0 && (p.W * int64_t(p.C)) % 2 == 0 &&
+                           p.S * int64_t(p.C) <= 256 && p.pad_w <= 65536 &&
+                           uint64_t(p.C) * p.H * p.W * e < (uint64_t(1) << 31);
+    // Its output rows per workgroup for a variant (the window rows in at most
+    // 4*ks chunks, K <= 16*tn): about kTile16Wgs workgroups, a block's staged
+    // rows within kTile16Lds; 0 where it does not apply.
+    auto tile16_rows = [&](const Tile16Variant& v) -> int64_t {
+        if (!tile16_ok || p.K > 16 * v.tn) return 0;
+        const Tile16Geom geo = tile16_geom(int(p.C), int(p.S), int(p.pad_w));
+        if (p.R * int64_t(geo.cpr) > 4 * v.ks) return 0;
+        const int64_t row_bytes = ((d.Q - 1) * p.stride_w * p.C + 8 * geo.cpr) * 2;
+        const int64_t fit_rows = kTile16Lds / row_bytes - (p.R - 1) * int64_t(p.dil_h) - 1;
+        if (fit_rows < 0) return 0;
+        const int64_t tmax = fit_rows / p.stride_h + 1;
+        const int64_t per_img = (kTile16Wgs + p.N - 1) / p.N;
+        const int64_t tp = (d.P + per_img - 1) / per_img;
+        return tp < tmax ? tp : tmax;
+    };
     if (nchw_ok) {
         // fp32 NCHW: narrow K -> 128-row tiles, 16-deep stages; wide K ->
         // 64-row tiles, 64 or 128 channels wide depending on how many
@@ -188,6 +210,18 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force) {
         d.kernel = KERN_REG;
         d.variant = p.K <= 32 ? 2 : (p.K <= 64 ? 1 : 0);
     }
+    // 16-bit NHWC windows of channels that do not fill whole vectors (the
+    // stem layers) into at most 64 output channels: the small-window kernel
+    // with the fewest steps that cover its chunks.
+    if (tile16_ok && !dma_ok && p.K <= 64) {
+        const int tn = p.K <= 32 ? 2 : 4;
+        for (int i = 0; i < count_of(kTile16Variants); ++i)
+            if (kTile16Variants[i].tn == tn && tile16_rows(kTile16Variants[i]) > 0) {
+                d.kernel = KERN_TILE16;
+                d.variant = i;
+                break;
+            }
+    }
     // Forced choice "<kernel>:<variant>" with kernel one of the names in
     // kKernelFamilies, applied where that kernel takes this convolution.
     if (const char* v = force) {
@@ -220,6 +254,10 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force) {
                        nchw_strip_fits(kNchwStripVariants[i])) {
                 d.kernel = KERN_NCHW_STRIP;
                 d.variant = i;
+            } else if (name == "tile16" && i >= 0 && i < count_of(kTile16Variants) &&
+                       tile16_rows(kTile16Variants[i]) > 0) {
+                d.kernel = KERN_TILE16;
+                d.variant = i;
             } else if (name == "nchw" && nchw_ok && i >= 0 && i < count_of(kNchwVariants)) {
                 d.kernel = KERN_NCHW;
                 d.variant = i;
@@ -232,6 +270,11 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force) {
         d.tile_m = 16;
         d.tile_n = 16 * kNchwTileVariants[d.variant].tn;
         d.tile_k = 16 * kNchwTileVariants[d.variant].ks;
+    } else if (d.kernel == KERN_TILE16) {
+        d.tile_rows = int32_t(tile16_rows(kTile16Variants[d.variant]));
+        d.tile_m = 16;
+        d.tile_n = 16 * kTile16Variants[d.variant].tn;
+        d.tile_k = 32 * kTile16Variants[d.variant].ks;
     } else if (d.kernel == KERN_NCHW_STRIP) {
         d.tile_m = kNchwStripVariants[d.variant].bm;
         d.tile_n = kNchwStripVariants[d.variant].bn;
@@ -253,11 +296,15 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force) {
 
     // The register-streamed strip kernel reads the filter from a copy in MFMA
     // fragment order: output channels padded to a multiple of 32.
-    d.frag_pack = d.kernel == KERN_STRIP_RB || d.kernel == KERN_NCHW_STRIP;
+    // The small-window kernel's copy: one 16-byte A fragment per lane, 32-deep
+    // step and 16-channel block.
+    d.frag_pack = d.kernel == KERN_STRIP_RB || d.kernel == KERN_NCHW_STRIP || d.kernel == KERN_TILE16;
     if (d.frag_pack) {
         const int64_t kpad = d.kernel == KERN_STRIP_RB ? (p.K + 31) / 32 * 32 : (p.K + 15) / 16 * 16;
         d.off_filter = 0;
-        d.bytes_filter = uint64_t(kpad) * d.Kg * e;
+        d.bytes_filter = d.kernel == KERN_TILE16
+                             ? uint64_t(1024) * kTile16Variants[d.variant].tn * kTile16Variants[d.variant].ks
+                             : uint64_t(kpad) * d.Kg * e;
         d.ws_bytes = p.N == 0 ? 0 : d.bytes_filter;
     }
 
@@ -302,6 +349,7 @@ constexpr KernelFamily kKernelFamilies[] = {
     {"striprb", KERN_STRIP_RB, count_of(kStripRbVariants)},
     {"nchwstrip", KERN_NCHW_STRIP, count_of(kNchwStripVariants)},
     {"nchwtile", KERN_NCHW_TILE, count_of(kNchwTileVariants)},
+    {"tile16", KERN_TILE16, count_of(kTile16Variants)},
 };
 
 // A ConvLSTM step: the gate convolution over concat(x, h) of p (C = c_x +
@@ -381,6 +429,15 @@ uint32_t grid_stride_blocks(uint64_t work) {
 
 template <typename T>
 void launch_pack(const conv_desc& d, const void* w, void* out, hipStream_t st) {
+    if (d.kernel == KERN_TILE16) {
+        if constexpr (sizeof(T) == 2) {
+            const Tile16Variant& v = kTile16Variants[d.variant];
+            Tile16PackArgs a{w, out, int32_t(d.p.K), int32_t(d.p.C), int32_t(d.p.R), int32_t(d.p.S), d.p.pad_w,
+                             v.ks, v.tn};
+            pack_filter_tile16_kernel<T><<<(v.ks * v.tn * 64 + 255) / 256, 256, 0, st>>>(a);
+        }
+        return;
+    }
     if (d.frag_pack) {
         if constexpr (sizeof(T) == 2) {
             const int32_t NB = int32_t((d.p.K + 31) / 32);

@@ -42,4 +42,22 @@ __device__ __forceinline__ float to_f32(T v) { return static_cast<float>(v); }
 template <typename T>
 __device__ __forceinline__ T from_f32(float v) { return static_cast<T>(v); }
 
+// 16-bit NHWC small-window kernel: chunk geometry shared by the kernel, its
+// filter pack and the planner.  `lead` zero-weight elements (0 or 1) come
+// before each filter row's run of S*C elements, so that the run starts at an
+// even element; cpr 8-element chunks cover lead + S*C.
+struct Tile16Geom {
+    int lead, cpr;
+};
+__host__ __device__ inline Tile16Geom tile16_geom(int C, int S, int pw) {
+    const int lead = (pw * C) & 1;
+    return {lead, (lead + S * C + 7) / 8};
+}
+
+// A row i of the 16 x 32 filter fragment of channel block jb holds output
+// channel (i/4)*4*TN + jb*4 + i%4, so that the accumulator lane group g
+// (rows 4g .. 4g+3 of every block) ends up with channels g*4*TN .. g*4*TN +
+// 4*TN - 1 of its pixel.
+__host__ __device__ inline int tile16_channel(int i, int jb, int tn) { return (i / 4) * 4 * tn + jb * 4 + (i % 4); }
+
 }  // namespace convlower

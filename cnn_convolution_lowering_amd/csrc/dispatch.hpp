@@ -18,6 +18,7 @@ enum KernelId : int32_t {
     KERN_STRIP_RB = 5,  // the same strips, filter fragments streamed into registers from a packed copy
     KERN_NCHW_STRIP = 6,  // fp32 NCHW strips (16-byte row loads), register-streamed filter (pad_w == 0, C % 16 == 0)
     KERN_NCHW_TILE = 7,   // fp32 NCHW small windows: input rows staged once per block of output rows, filter in registers
+    KERN_TILE16 = 8,      // 16-bit NHWC small windows: the same staging, window rows read as contiguous runs
 };
 
 // One compiled tile shape: BM x BN output tile, BK-deep LDS stages (in 16-bit
@@ -88,6 +89,15 @@ constexpr NchwTileVariant kNchwTileVariants[] = {{1, 2}, {2, 2}, {4, 2}, {1, 4},
 // LDS budget of its staged rows, and the workgroups it aims for.
 constexpr int64_t kNchwTileLds = 32768;
 constexpr int64_t kNchwTileWgs = 1024;
+// 16-bit NHWC small-window kernel: ks 32-deep steps (4*ks 8-element chunks
+// >= R * cpr), tn 16-channel blocks (K <= 16*tn).
+struct Tile16Variant {
+    int ks, tn;
+};
+constexpr Tile16Variant kTile16Variants[] = {{2, 2}, {4, 2}, {6, 2}, {8, 2}, {2, 4}, {4, 4}, {6, 4}};
+// LDS budget of its staged rows, and the workgroups it aims for.
+constexpr int64_t kTile16Lds = 49152;
+constexpr int64_t kTile16Wgs = 2048;
 // Slots per channel plane in a strip buffer of `strip` slots: the most that
 // fit, rounded to 1 mod 4, so that planes 4 apart (one per lane group) start
 // 16 banks apart.

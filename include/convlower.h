@@ -118,7 +118,11 @@ typedef struct {
      * in MFMA fragment order (that copy is the workspace's filter part),
      * 6 fp32 NCHW row strips loaded 16 bytes per lane, filter streamed the
      * same way, 7 fp32 NCHW small windows (C*R*S <= 64, K <= 64): input rows
-     * staged once per block of output rows, whole filter in registers;
+     * staged once per block of output rows, whole filter in registers,
+     * 8 16-bit NHWC small windows (the stem layers: C*sw and W*C even, unit
+     * horizontal dilation, K <= 64): the same staging, each filter row's
+     * window part read as one contiguous run, filter in registers from a
+     * copy in MFMA fragment order;
      * kernel_variant indexes that kernel's compiled tile shapes */
     int32_t kernel, kernel_variant;
 } conv_plan_info_t;

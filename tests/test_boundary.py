@@ -214,14 +214,22 @@ def test_workload_workspace_ratios():
 def test_implicit_needs_no_workspace(layout, dtype):
     """The fused path never lowers x: no lowered workspace.  The only
     workspace it may take is the filter copy in MFMA fragment order of the
-    register-streamed kernels (K rounded up to 16 or 32, times C*R*S)."""
+    register-streamed kernels (K rounded up to 16 or 32, times C*R*S), or of
+    the 16-bit NHWC small-window kernel (at most 64 channels by R filter
+    rows of ceil((S*C + 1) / 8) 8-element chunks, rounded up to 4 chunks)."""
     for (C, R, S, st, pd) in [(3, 7, 7, 2, 3), (32, 3, 3, 2, 0), (128, 1, 1, 1, 0), (5, 2, 3, 1, 1)]:
         c = cl.Conv2d(4, C, 20, 20, 16, R, S, stride=st, padding=pd, layout=layout, dtype=dtype, algo="implicit")
         assert c.info["ws_lowered_bytes"] == 0 and c.info["lowering_elided"] == 1
         assert c.workspace_bytes == c.info["ws_filter_bytes"]
-        assert c.info["ws_filter_bytes"] <= 32 * C * R * S * {"f32": 4, "f16": 2, "bf16": 2}[dtype]
-        if C % 16:
-            assert c.workspace_bytes == 0
+        elem = {"f32": 4, "f16": 2, "bf16": 2}[dtype]
+        if c.info["kernel"] == 8:
+            assert layout == "nhwc" and dtype != "f32" and C * st % 2 == 0
+            chunks = R * ((S * C + 1 + 7) // 8)
+            assert 0 < c.info["ws_filter_bytes"] <= 64 * 8 * 4 * ((chunks + 3) // 4) * elem
+        else:
+            assert c.info["ws_filter_bytes"] <= 32 * C * R * S * elem
+            if C % 16:
+                assert c.workspace_bytes == 0
 
 
 def test_elided_layers_use_no_lowering_workspace():

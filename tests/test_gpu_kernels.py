@@ -21,7 +21,7 @@ from parity import TORCH_DT, assert_parity, to_f64
 pytestmark = pytest.mark.gpu
 
 # kernel name -> (plan_info kernel id, number of compiled variants)
-KERNELS = {"reg": (0, 3), "dma": (1, 7), "wide": (2, 9), "nchw": (3, 12), "strip": (4, 5), "striprb": (5, 7), "nchwstrip": (6, 10), "nchwtile": (7, 6)}
+KERNELS = {"reg": (0, 3), "dma": (1, 7), "wide": (2, 9), "nchw": (3, 12), "strip": (4, 5), "striprb": (5, 7), "nchwstrip": (6, 10), "nchwtile": (7, 6), "tile16": (8, 7)}
 
 # (N, C, H, W, K, R, S, stride, pad, dilation)
 SHAPES_C32 = [
@@ -57,6 +57,20 @@ SHAPES_SMALL_KG = [
     (1, 5, 11, 13, 40, 3, 3, (1, 1), (0, 1), (1, 1)),
     (1, 3, 14, 16, 48, 3, 3, (2, 2), (1, 1), (1, 1)),
 ]
+# 16-bit NHWC small windows (C*sw and W*C even, unit horizontal dilation):
+# odd and even padding (one lead element or none), vertical dilation,
+# output rows shorter and longer than a 16-pixel block, K not a multiple of
+# 8 or of the lane's channel run, and a batch large enough for several
+# output rows per workgroup with a ragged last block of rows
+SHAPES_TILE16 = [
+    (2, 3, 30, 30, 32, 3, 3, (2, 2), (1, 1), (1, 1)),
+    (2, 3, 36, 34, 64, 7, 7, (2, 2), (3, 3), (1, 1)),
+    (1, 4, 19, 21, 20, 5, 5, (1, 1), (2, 2), (1, 1)),
+    (2, 2, 23, 17, 40, 3, 3, (1, 1), (1, 1), (2, 1)),
+    (1, 6, 9, 50, 16, 3, 3, (2, 1), (0, 1), (1, 1)),
+    (3, 3, 11, 10, 8, 2, 4, (1, 2), (0, 1), (1, 1)),
+    (256, 2, 40, 12, 16, 3, 3, (2, 2), (1, 1), (1, 1)),
+]
 # (kernel, dtype, layout, algo, shapes)
 PLANS = [
     ("reg", "f32", "nhwc", "implicit", SHAPES_SMALL_C + SHAPES_C32[:2]),
@@ -74,6 +88,8 @@ PLANS = [
     ("striprb", "bf16", "nhwc", "implicit", SHAPES_C32[:3]),
     ("nchwstrip", "f32", "nchw", "implicit", SHAPES_NCHW_F32),
     ("nchwtile", "f32", "nchw", "implicit", SHAPES_SMALL_KG),
+    ("tile16", "bf16", "nhwc", "implicit", SHAPES_TILE16),
+    ("tile16", "f16", "nhwc", "implicit", SHAPES_TILE16),
 ]
 
 
@@ -143,12 +159,38 @@ def test_forced_kernel_integer_exact(dev, monkeypatch):
         assert torch.equal(y.cpu().view(torch.int16), want.view(torch.int16)), forced
 
 
+def test_small_window_kernel_integer_exact(dev, monkeypatch):
+    """Integer inputs through the 16-bit NHWC small-window kernel (the stem
+    shape at reduced size, every variant that takes it): exact fp32 sums, so
+    the result is the reference rounded once, bit for bit."""
+    N, C, H, W, K, R, S = 3, 3, 28, 26, 32, 7, 7
+    g = torch.Generator().manual_seed(78)
+    x = torch.randint(-2, 3, (N, C, H, W), generator=g).to(torch.bfloat16)
+    w = torch.randint(-2, 3, (K, C, R, S), generator=g).to(torch.bfloat16)
+    b = torch.randint(-4, 5, (K,), generator=g).to(torch.bfloat16)
+    xl, wl = _perm(x, "nhwc"), _perm(w, "nhwc")
+    ref = oracle.conv2d(xl, wl, b, layout="nhwc", stride=2, padding=3)
+    want = torch.from_numpy(ref).to(torch.float32).to(torch.bfloat16)
+    ran = 0
+    for v in range(KERNELS["tile16"][1]):
+        monkeypatch.setenv("CONVLOWER_KERNEL", "tile16:%d" % v)
+        d = cl.Conv2d(N, C, H, W, K, R, S, stride=2, padding=3, layout="nhwc", dtype="bf16", algo="implicit")
+        if d.info["kernel"] != KERNELS["tile16"][0] or d.info["kernel_variant"] != v:
+            continue
+        print("int case tile16:%d" % v, flush=True)
+        y = d.forward(xl.to(dev), wl.to(dev), b.to(dev))
+        torch.cuda.synchronize()
+        assert torch.equal(y.cpu().view(torch.int16), want.view(torch.int16)), v
+        ran += 1
+    assert ran >= 2
+
 
 @pytest.mark.parametrize("case", [
     ("f32", "nchw", (64, 32, 30, 30, 64, 3, 3, (2, 2), (0, 0), (1, 1))),
     ("f32", "nchw", (16, 3, 30, 30, 32, 3, 3, (1, 1), (1, 1), (1, 1))),
     ("f16", "nhwc", (4, 128, 32, 32, 128, 3, 3, (1, 1), (1, 1), (1, 1))),
     ("bf16", "nhwc", (8, 64, 14, 14, 96, 3, 3, (1, 1), (1, 1), (1, 1))),
+    ("bf16", "nhwc", (8, 3, 64, 64, 64, 7, 7, (2, 2), (3, 3), (1, 1))),
 ], ids=lambda c: "%s-%s" % c[:2])
 def test_tune_keeps_a_correct_plan(dev, monkeypatch, case):
     """conv_tune times the candidates and keeps the fastest; the kept plan
