@@ -258,14 +258,22 @@ void launch_gemm(const conv_desc& d, const void* x, const void* w, const void* b
             GemmArgs h = g;
             h.tile_rows = d.tile_rows;
             const int64_t P = d.P, TP = d.tile_rows;
-            const uint32_t blocks = uint32_t(d.p.N * ((P + TP - 1) / TP));
+            const int64_t tiles = d.p.N * ((P + TP - 1) / TP);
+            const int64_t wgs = kTile16Cus * tile16_wgs_per_cu(kTile16Variants[d.variant].tn);
+            const uint32_t blocks = uint32_t(tiles < wgs ? tiles : wgs);
             const int64_t rows_in = (TP - 1) * d.p.stride_h + (d.p.R - 1) * d.p.dil_h + 1;
             const Tile16Geom geo = tile16_geom(int(d.p.C), int(d.p.S), int(d.p.pad_w));
-            const size_t lds = size_t(rows_in * ((d.Q - 1) * d.p.stride_w * d.p.C + 8 * geo.cpr) * 2);
-#define CONVLOWER_TILE16_CASE(I)                                                                               \
-    case I:                                                                                                    \
-        conv_nhwc_tile16_kernel<T, kTile16Variants[I].ks, kTile16Variants[I].tn><<<blocks, 256, lds, st>>>(h); \
-        break;
+            // two staging buffers (rounded to 16 bytes), then four waves' output
+            // transpose buffers of 16 rows of 32*tn + 16 bytes
+            const int64_t bufw = rows_in * ((d.Q - 1) * d.p.stride_w * d.p.C + 8 * geo.cpr) / 2;
+            const size_t lds = size_t(((2 * bufw + 3) & ~int64_t(3)) * 4 +
+                                      64 * (32 * kTile16Variants[d.variant].tn + 16));
+#define CONVLOWER_TILE16_CASE(I)                                                                          \
+    case I: {                                                                                             \
+        constexpr Tile16Variant v = kTile16Variants[I];                                                   \
+        conv_nhwc_tile16_kernel<T, v.ks, v.tn, v.split><<<blocks, 256, lds, st>>>(h);                     \
+        break;                                                                                            \
+    }
             switch (d.variant) {
                 CONVLOWER_TILE16_CASE(0)
                 CONVLOWER_TILE16_CASE(1)
@@ -274,6 +282,10 @@ void launch_gemm(const conv_desc& d, const void* x, const void* w, const void* b
                 CONVLOWER_TILE16_CASE(4)
                 CONVLOWER_TILE16_CASE(5)
                 CONVLOWER_TILE16_CASE(6)
+                CONVLOWER_TILE16_CASE(7)
+                CONVLOWER_TILE16_CASE(8)
+                CONVLOWER_TILE16_CASE(9)
+                CONVLOWER_TILE16_CASE(10)
                 default: break;
             }
 #undef CONVLOWER_TILE16_CASE

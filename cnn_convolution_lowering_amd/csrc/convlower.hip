@@ -145,18 +145,18 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force) {
                            (p.C * int64_t(p.stride_w)) % 2 == 0 && (p.W * int64_t(p.C)) % 2 == 0 &&
                            p.S * int64_t(p.C) <= 256 && p.pad_w <= 65536 &&
                            uint64_t(p.C) * p.H * p.W * e < (uint64_t(1) << 31);
-    // Its output rows per workgroup for a variant (the window rows in at most
-    // 4*ks chunks, K <= 16*tn): about kTile16Wgs workgroups, a block's staged
+    // Its output rows per tile for a variant (the window rows in at most
+    // 4*ks chunks, K <= 16*tn*split): about kTile16Tiles tiles, two tiles' staged
     // rows within kTile16Lds; 0 where it does not apply.
     auto tile16_rows = [&](const Tile16Variant& v) -> int64_t {
-        if (!tile16_ok || p.K > 16 * v.tn) return 0;
+        if (!tile16_ok || p.K > 16 * v.tn * v.split) return 0;
         const Tile16Geom geo = tile16_geom(int(p.C), int(p.S), int(p.pad_w));
         if (p.R * int64_t(geo.cpr) > 4 * v.ks) return 0;
         const int64_t row_bytes = ((d.Q - 1) * p.stride_w * p.C + 8 * geo.cpr) * 2;
-        const int64_t fit_rows = kTile16Lds / row_bytes - (p.R - 1) * int64_t(p.dil_h) - 1;
+        const int64_t fit_rows = kTile16Lds / 2 / row_bytes - (p.R - 1) * int64_t(p.dil_h) - 1;
         if (fit_rows < 0) return 0;
         const int64_t tmax = fit_rows / p.stride_h + 1;
-        const int64_t per_img = (kTile16Wgs + p.N - 1) / p.N;
+        const int64_t per_img = (kTile16Tiles + p.N - 1) / p.N;
         const int64_t tp = (d.P + per_img - 1) / per_img;
         return tp < tmax ? tp : tmax;
     };
@@ -214,9 +214,10 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force) {
     // stem layers) into at most 64 output channels: the small-window kernel
     // with the fewest steps that cover its chunks.
     if (tile16_ok && !dma_ok && p.K <= 64) {
+        // K <= 32: two channel blocks per wave; else four (one wave per pixel block)
         const int tn = p.K <= 32 ? 2 : 4;
         for (int i = 0; i < count_of(kTile16Variants); ++i)
-            if (kTile16Variants[i].tn == tn && tile16_rows(kTile16Variants[i]) > 0) {
+            if (kTile16Variants[i].tn == tn && kTile16Variants[i].split == 1 && tile16_rows(kTile16Variants[i]) > 0) {
                 d.kernel = KERN_TILE16;
                 d.variant = i;
                 break;
@@ -273,7 +274,7 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force) {
     } else if (d.kernel == KERN_TILE16) {
         d.tile_rows = int32_t(tile16_rows(kTile16Variants[d.variant]));
         d.tile_m = 16;
-        d.tile_n = 16 * kTile16Variants[d.variant].tn;
+        d.tile_n = 16 * kTile16Variants[d.variant].tn * kTile16Variants[d.variant].split;
         d.tile_k = 32 * kTile16Variants[d.variant].ks;
     } else if (d.kernel == KERN_NCHW_STRIP) {
         d.tile_m = kNchwStripVariants[d.variant].bm;
@@ -303,7 +304,8 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force) {
         const int64_t kpad = d.kernel == KERN_STRIP_RB ? (p.K + 31) / 32 * 32 : (p.K + 15) / 16 * 16;
         d.off_filter = 0;
         d.bytes_filter = d.kernel == KERN_TILE16
-                             ? uint64_t(1024) * kTile16Variants[d.variant].tn * kTile16Variants[d.variant].ks
+                             ? uint64_t(1024) * kTile16Variants[d.variant].tn * kTile16Variants[d.variant].split *
+                                   kTile16Variants[d.variant].ks
                              : uint64_t(kpad) * d.Kg * e;
         d.ws_bytes = p.N == 0 ? 0 : d.bytes_filter;
     }
@@ -433,8 +435,8 @@ void launch_pack(const conv_desc& d, const void* w, void* out, hipStream_t st) {
         if constexpr (sizeof(T) == 2) {
             const Tile16Variant& v = kTile16Variants[d.variant];
             Tile16PackArgs a{w, out, int32_t(d.p.K), int32_t(d.p.C), int32_t(d.p.R), int32_t(d.p.S), d.p.pad_w,
-                             v.ks, v.tn};
-            pack_filter_tile16_kernel<T><<<(v.ks * v.tn * 64 + 255) / 256, 256, 0, st>>>(a);
+                             v.ks, v.tn, v.split};
+            pack_filter_tile16_kernel<T><<<(v.ks * v.tn * v.split * 64 + 255) / 256, 256, 0, st>>>(a);
         }
         return;
     }

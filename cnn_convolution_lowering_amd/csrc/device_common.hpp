@@ -54,6 +54,11 @@ __host__ __device__ inline Tile16Geom tile16_geom(int C, int S, int pw) {
     return {lead, (lead + S * C + 7) / 8};
 }
 
+// Workgroups of that kernel resident per CU (its persistent grid is this many
+// per CU): 4*tn channels per lane and the filter in registers leave room
+// for two waves per SIMD at tn = 4, three at tn = 2.
+__host__ __device__ constexpr int tile16_wgs_per_cu(int tn) { return tn == 4 ? 2 : 3; }
+
 // A row i of the 16 x 32 filter fragment of channel block jb holds output
 // channel (i/4)*4*TN + jb*4 + i%4, so that the accumulator lane group g
 // (rows 4g .. 4g+3 of every block) ends up with channels g*4*TN .. g*4*TN +

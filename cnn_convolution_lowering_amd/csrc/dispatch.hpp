@@ -90,14 +90,19 @@ constexpr NchwTileVariant kNchwTileVariants[] = {{1, 2}, {2, 2}, {4, 2}, {1, 4},
 constexpr int64_t kNchwTileLds = 32768;
 constexpr int64_t kNchwTileWgs = 1024;
 // 16-bit NHWC small-window kernel: ks 32-deep steps (4*ks 8-element chunks
-// >= R * cpr), tn 16-channel blocks (K <= 16*tn).
+// >= R * cpr), tn 16-channel blocks per wave, split waves per pixel block
+// (K <= 16*tn*split).
 struct Tile16Variant {
-    int ks, tn;
+    int ks, tn, split;
 };
-constexpr Tile16Variant kTile16Variants[] = {{2, 2}, {4, 2}, {6, 2}, {8, 2}, {2, 4}, {4, 4}, {6, 4}};
-// LDS budget of its staged rows, and the workgroups it aims for.
-constexpr int64_t kTile16Lds = 49152;
-constexpr int64_t kTile16Wgs = 2048;
+constexpr Tile16Variant kTile16Variants[] = {{2, 2, 1}, {4, 2, 1}, {6, 2, 1}, {8, 2, 1}, {2, 2, 2}, {4, 2, 2},
+                                             {6, 2, 2}, {8, 2, 2}, {2, 4, 1}, {4, 4, 1}, {6, 4, 1}};
+// LDS budget of its two staging buffers (three workgroups per CU), the
+// tiles (blocks of output rows) it aims for, and the CUs its persistent
+// grid covers (tile16_wgs_per_cu workgroups each).
+constexpr int64_t kTile16Lds = 40960;
+constexpr int64_t kTile16Tiles = 4096;
+constexpr int64_t kTile16Cus = 256;
 // Slots per channel plane in a strip buffer of `strip` slots: the most that
 // fit, rounded to 1 mod 4, so that planes 4 apart (one per lane group) start
 // 16 banks apart.

@@ -368,28 +368,29 @@ __global__ void __launch_bounds__(256) pack_filter_frag_f32_kernel(FragPackF32Ar
 }
 
 // 16-bit KRSC filter in the A-fragment order of the NHWC small-window
-// kernel: fragment (jb, st) of lane l = (g, i) (g = l/16, i = l%16) holds
-// the 8 contraction elements of chunk j = st*4 + g for output channel
-// tile16_channel(i, jb, tn): filter row r = j / cpr, elements t = 8*(j % cpr)
+// kernel: fragment (hc, jb, st) (channel part hc < split, block jb < tn) of
+// lane l = (g, i) (g = l/16, i = l%16) holds the 8 contraction elements of
+// chunk j = st*4 + g for output channel hc*16*tn + tile16_channel(i, jb,
+// tn): filter row r = j / cpr, elements t = 8*(j % cpr)
 // + e of that row's run, which are w[ch][r][(t - lead) / C][(t - lead) % C]
 // where 0 <= t - lead < S*C and zero elsewhere (also past R rows and past K
 // channels).  One 16-byte fragment per thread.
 struct Tile16PackArgs {
     const void* w;
     void* out;
-    int32_t K, C, R, S, pw, ks, tn;
+    int32_t K, C, R, S, pw, ks, tn, split;
 };
 
 template <typename T>
 __global__ void __launch_bounds__(256) pack_filter_tile16_kernel(Tile16PackArgs a) {
     const Tile16Geom geo = tile16_geom(a.C, a.S, a.pw);
     const int run = a.S * a.C;
-    const int total = a.tn * a.ks * 64;
+    const int total = a.split * a.tn * a.ks * 64;
     const T* __restrict__ w = static_cast<const T*>(a.w);
     for (int i = int(blockIdx.x) * 256 + threadIdx.x; i < total; i += int(gridDim.x) * 256) {
         const int lane = i & 63, blk = i >> 6;
-        const int st = blk % a.ks, jb = blk / a.ks;
-        const int ch = tile16_channel(lane & 15, jb, a.tn);
+        const int st = blk % a.ks, jbg = blk / a.ks, hc = jbg / a.tn, jb = jbg - hc * a.tn;
+        const int ch = hc * 16 * a.tn + tile16_channel(lane & 15, jb, a.tn);
         const int j = st * 4 + (lane >> 4);
         const int r = j / geo.cpr, t0 = (j - r * geo.cpr) * 8;
         Pack16<T> pk;

@@ -21,7 +21,7 @@ from parity import TORCH_DT, assert_parity, to_f64
 pytestmark = pytest.mark.gpu
 
 # kernel name -> (plan_info kernel id, number of compiled variants)
-KERNELS = {"reg": (0, 3), "dma": (1, 7), "wide": (2, 9), "nchw": (3, 12), "strip": (4, 5), "striprb": (5, 7), "nchwstrip": (6, 10), "nchwtile": (7, 6), "tile16": (8, 7)}
+KERNELS = {"reg": (0, 3), "dma": (1, 7), "wide": (2, 9), "nchw": (3, 12), "strip": (4, 5), "striprb": (5, 7), "nchwstrip": (6, 10), "nchwtile": (7, 6), "tile16": (8, 11)}
 
 # (N, C, H, W, K, R, S, stride, pad, dilation)
 SHAPES_C32 = [
@@ -69,7 +69,7 @@ SHAPES_TILE16 = [
     (2, 2, 23, 17, 40, 3, 3, (1, 1), (1, 1), (2, 1)),
     (1, 6, 9, 50, 16, 3, 3, (2, 1), (0, 1), (1, 1)),
     (3, 3, 11, 10, 8, 2, 4, (1, 2), (0, 1), (1, 1)),
-    (256, 2, 40, 12, 16, 3, 3, (2, 2), (1, 1), (1, 1)),
+    (256, 2, 42, 12, 16, 3, 3, (2, 2), (1, 1), (1, 1)),
 ]
 # (kernel, dtype, layout, algo, shapes)
 PLANS = [
