@@ -233,9 +233,9 @@ void launch_gemm(const conv_desc& d, const void* x, const void* w, const void* b
             const int64_t P = d.P, TP = d.tile_rows;
             const uint32_t blocks = uint32_t(d.p.N * ((P + TP - 1) / TP));
             const int64_t rows_in = (TP - 1) * d.p.stride_h + (d.p.R - 1) * d.p.dil_h + 1;
-            // C planes, a zero plane and the padded filter
-            const size_t lds = size_t(((d.p.C + 1) * rows_in * d.W_used + 3 +
-                                       256 * kNchwTileVariants[d.variant].tn * kNchwTileVariants[d.variant].ks) * 4);
+            // C planes, a zero plane, the padded filter and the padded bias
+            const int64_t tn = kNchwTileVariants[d.variant].tn, ks = kNchwTileVariants[d.variant].ks;
+            const size_t lds = size_t(((d.p.C + 1) * rows_in * d.W_used + 3 + 256 * tn * ks + 16 * tn) * 4);
 #define CONVLOWER_NCHW_TILE_CASE(I)                                                                            \
     case I:                                                                                                    \
         conv_nchw_f32_tile_kernel<kNchwTileVariants[I].ks, kNchwTileVariants[I].tn><<<blocks, 256, lds, st>>>(h); \

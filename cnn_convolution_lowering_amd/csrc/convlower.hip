@@ -127,7 +127,7 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force) {
     auto nchw_tile_rows = [&](const NchwTileVariant& v) -> int64_t {
         if (!nchw_ok || d.Kg > 16 * v.ks || p.K > 16 * v.tn) return 0;
         const int64_t row_bytes = (p.C + 1) * d.W_used * 4;   // C planes and a zero plane
-        const int64_t fit_rows = (kNchwTileLds - 1024 * v.tn * v.ks - 16) / row_bytes - (p.R - 1) * int64_t(p.dil_h) - 1;
+        const int64_t fit_rows = (kNchwTileLds - 1024 * v.tn * v.ks - 64 * v.tn - 16) / row_bytes - (p.R - 1) * int64_t(p.dil_h) - 1;
         if (fit_rows < 0) return 0;
         const int64_t tmax = fit_rows / p.stride_h + 1;
         const int64_t per_img = (kNchwTileWgs + p.N - 1) / p.N;

@@ -9,10 +9,12 @@
 // channel, PWd = (Q-1)*sw + (S-1)*dw + 1 padded columns, plus one plane of
 // zeros that the padded contraction elements past C*R*S read), and reads
 // every pixel's window from there.  The whole filter lives in registers as MFMA
-// B fragments for the kernel's life (loaded from KCRS directly: no packed
-// copy), so the loop is LDS reads, v_mfma_f32_16x16x4_f32 (full fp32
-// products) and 16-byte stores of four consecutive pixels of one channel.
-// Contraction order k = (c*R + r)*S + s, the filter's own.
+// A fragments for the kernel's life (loaded from KCRS directly: no packed
+// copy), the pixels are the B operand, so the loop is LDS reads,
+// v_mfma_f32_16x16x4_f32 (full fp32 products) and 4-byte stores in which
+// 16 consecutive lanes write 16 consecutive pixels of one output channel
+// (one 64-byte run per lane group: the stores coalesce).  Contraction order
+// k = (c*R + r)*S + s, the filter's own.
 #pragma once
 
 #include "igemm_dma.hpp"
@@ -41,17 +43,20 @@ __global__ void __launch_bounds__(256) conv_nchw_f32_tile_kernel(GemmArgs g) {
 
     // Stage, with 4-byte LDS-DMA loads (all in flight at once): the input
     // rows h0 .. h0+rows_in-1, columns -pw .. PWd-pw-1 of every channel,
-    // zero outside the image; the zero plane; and the filter as a zero-padded
-    // [16*TN][16*KS] block (KCRS rows are contiguous in k = (c*R + r)*S + s).
+    // zero outside the image; the zero plane; the filter as a zero-padded
+    // [16*TN][16*KS] block (KCRS rows are contiguous in k = (c*R + r)*S + s);
+    // and the bias, zero-padded to 16*TN channels (zero without one).
     const int h0 = p0 * g.sh - g.ph;
     const int staged = g.C * plane;
     const int RS = g.R * g.S, Kg = g.C * RS;
     constexpr int KP = 16 * KS;
     const int fil0 = (staged + plane + 3) & ~3;   // 16-byte aligned for the fragment reads
-    const int total = fil0 + 16 * TN * KP;
+    const int bias0 = fil0 + 16 * TN * KP;
+    const int total = bias0 + 16 * TN;
     const i32x4 xr = make_rsrc(static_cast<const float*>(g.a) + int64_t(n) * g.C * g.H * g.W,
                                uint32_t(g.C * g.H * g.W * 4));
     const i32x4 wr = make_rsrc(g.b, uint32_t(g.K * Kg * 4));
+    const i32x4 br = make_rsrc(g.bias ? g.bias : g.b, g.bias ? uint32_t(g.K * 4) : 0u);
     const uint32_t lds0 = lds_offset(lds);
     const float rPWd = 1.0f / float(PWd), rrows = 1.0f / float(rows_in);
     for (int i0 = 0; i0 < total; i0 += 256) {
@@ -63,9 +68,11 @@ __global__ void __launch_bounds__(256) conv_nchw_f32_tile_kernel(GemmArgs g) {
             const int c = div_small(row, rows_in, rrows), h = h0 + (row - c * rows_in), w = j - g.pw;
             const bool in = i < staged && unsigned(h) < unsigned(g.H) && unsigned(w) < unsigned(g.W);
             dma4(xr, in ? uint32_t(((c * g.H + h) * g.W + w) * 4) : kOutOfRange, m0);
-        } else {
+        } else if (i < bias0) {
             const int f = i - fil0, ch = f / KP, k = f - (f / KP) * KP;
             dma4(wr, (ch < g.K && k < Kg) ? uint32_t((ch * Kg + k) * 4) : kOutOfRange, m0);
+        } else {
+            dma4(br, uint32_t((i - bias0) * 4), m0);   // past K (or no bias): out of range, zero
         }
     }
 
@@ -82,17 +89,15 @@ __global__ void __launch_bounds__(256) conv_nchw_f32_tile_kernel(GemmArgs g) {
             const int r = rs / g.S, s = rs - (rs / g.S) * g.S;
             off[st][e] = k < Kg ? c * plane + r * g.dh * PWd + s * g.dw : staged;
         }
-    const float* __restrict__ bias = static_cast<const float*>(g.bias);
-    float bv[TN];
-#pragma unroll
-    for (int jb = 0; jb < TN; ++jb) {
-        const int ch = jb * 16 + l16;
-        bv[jb] = (bias && ch < g.K) ? bias[ch] : 0.f;
-    }
     wait_vmcnt<0>();
     __syncthreads();
+    // Bias of the lane's output channels jb*16 + 4*gq + e: the accumulators'
+    // start.
+    f32x4 bv[TN];
+#pragma unroll
+    for (int jb = 0; jb < TN; ++jb) bv[jb] = __builtin_bit_cast(f32x4, load16(lds + bias0 + jb * 16 + 4 * gq));
     // Filter fragments: lane (gq, l16) of block jb, step st holds
-    // w[jb*16 + l16][st*16 + 4*gq + e].
+    // w[jb*16 + l16][st*16 + 4*gq + e] (row l16 of the A operand).
     float bf[TN][KS][4];
 #pragma unroll
     for (int jb = 0; jb < TN; ++jb)
@@ -104,15 +109,14 @@ __global__ void __launch_bounds__(256) conv_nchw_f32_tile_kernel(GemmArgs g) {
         }
 
     // Pixel blocks of 16, wave-strided: lane l16's pixel (pl, q) advances
-    // by 64 pixels per pass without a division.  Software-pipelined: the A
-    // values of the next block are read, and the previous block is stored,
-    // while this block's MFMAs run.
+    // by 64 pixels per pass without a division.  Software-pipelined: the
+    // window values of the next block are read, and the previous block is
+    // stored, while this block's MFMAs run.
     const int count = np * g.Q;
     const int dp = 64 / g.Q, dq = 64 - (64 / g.Q) * g.Q;
     int ml = wave * 16 + l16;
     int pl = ml / g.Q, q = ml - (ml / g.Q) * g.Q;
     float* __restrict__ y = static_cast<float*>(g.y) + int64_t(n) * g.K * g.PQ + p0 * g.Q;
-    const bool vec = (g.PQ & 3) == 0 && ((p0 * g.Q) & 3) == 0;
     auto read_block = [&](float (&a)[KS][4]) __attribute__((always_inline)) {
         const float* src = lds + (ml < count ? pl * g.sh * PWd + q * g.sw : 0);
 #pragma unroll
@@ -129,25 +133,17 @@ __global__ void __launch_bounds__(256) conv_nchw_f32_tile_kernel(GemmArgs g) {
             ++pl;
         }
     };
-    // lane (gq, l16) holds pixels b*16 + 4*gq .. +3 of channel jb*16 + l16
+    // lane (gq, l16) holds channels jb*16 + 4*gq + e of pixel b*16 + l16
     auto store_block = [&](const f32x4 (&acc)[TN], int b) __attribute__((always_inline)) {
-        const int mo = b * 16 + 4 * gq;
+        const int m = b * 16 + l16;
+        if (m >= count) return;
 #pragma unroll
-        for (int jb = 0; jb < TN; ++jb) {
-            const int ch = jb * 16 + l16;
-            if (ch >= g.K || mo >= count) continue;
-            float* yc = y + int64_t(ch) * g.PQ + mo;
-            const float v0 = acc[jb][0] + bv[jb], v1 = acc[jb][1] + bv[jb];
-            const float v2 = acc[jb][2] + bv[jb], v3 = acc[jb][3] + bv[jb];
-            if (vec && mo + 3 < count) {
-                store16(yc, u32x4{__float_as_uint(v0), __float_as_uint(v1), __float_as_uint(v2), __float_as_uint(v3)});
-            } else {
-                yc[0] = v0;
-                if (mo + 1 < count) yc[1] = v1;
-                if (mo + 2 < count) yc[2] = v2;
-                if (mo + 3 < count) yc[3] = v3;
+        for (int jb = 0; jb < TN; ++jb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int ch = jb * 16 + 4 * gq + e;
+                if (ch < g.K) y[int64_t(ch) * g.PQ + m] = acc[jb][e];
             }
-        }
     };
 
     float a0[KS][4];
@@ -160,14 +156,14 @@ __global__ void __launch_bounds__(256) conv_nchw_f32_tile_kernel(GemmArgs g) {
         read_block(a1);   // next block (a valid pixel-0 window past the end)
         f32x4 acc[TN];
 #pragma unroll
-        for (int jb = 0; jb < TN; ++jb) acc[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int jb = 0; jb < TN; ++jb) acc[jb] = bv[jb];
 #pragma unroll
         for (int st = 0; st < KS; ++st)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
 #pragma unroll
                 for (int jb = 0; jb < TN; ++jb)
-                    acc[jb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0[st][e], bf[jb][st][e], acc[jb], 0, 0, 0);
+                    acc[jb] = __builtin_amdgcn_mfma_f32_16x16x4f32(bf[jb][st][e], a0[st][e], acc[jb], 0, 0, 0);
         if (b != wave) store_block(prev, b - 4);
 #pragma unroll
         for (int jb = 0; jb < TN; ++jb) prev[jb] = acc[jb];
