@@ -52,7 +52,9 @@ class PlanInfo(ctypes.Structure):
                 ("ws_lowered_bytes", ctypes.c_uint64), ("im2win_bytes", ctypes.c_uint64),
                 ("im2col_bytes", ctypes.c_uint64), ("lowering_elided", ctypes.c_int32),
                 ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32), ("tile_k", ctypes.c_int32),
-                ("elem_bytes", ctypes.c_int32), ("kernel", ctypes.c_int32), ("kernel_variant", ctypes.c_int32)]
+                ("elem_bytes", ctypes.c_int32), ("kernel", ctypes.c_int32), ("kernel_variant", ctypes.c_int32),
+                ("ws_partial_offset", ctypes.c_uint64), ("ws_partial_bytes", ctypes.c_uint64),
+                ("ksplit", ctypes.c_int32)]
 
 
 class TuneResult(ctypes.Structure):

@@ -193,10 +193,12 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force) {
         }
     } else if (dma_ok) {
         // BN covers the output channels up to 128; BM = 256 where that still
-        // gives two workgroups per CU, else 128.
+        // gives two workgroups per CU, else 128 -- for 16-bit operands with
+        // 64-deep stages (two of them), which a sweep over the 3x3 and 1x1
+        // layers put ahead of four 32-deep ones.
         d.kernel = KERN_DMA;
-        d.variant = p.K <= 32 ? 0 : (p.K <= 64 ? 1 : 2);
-        if (d.variant == 2 && (d.M / 256) * ((p.K + 127) / 128) >= 512) d.variant = 3;
+        d.variant = p.K <= 32 ? 0 : (p.K <= 64 ? 1 : (p.dtype == CONV_F32 ? 2 : 6));
+        if (d.variant >= 2 && (d.M / 256) * ((p.K + 127) / 128) >= 512) d.variant = 3;
         // Taps sharing an input row (S >= 3), enough 512 x 128 tiles to give
         // most CUs one, and output channels filling whole 128-wide tiles:
         // the register-streamed strip kernel (a sweep over the kernel-size
@@ -223,13 +225,16 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force) {
                 break;
             }
     }
-    // Forced choice "<kernel>:<variant>" with kernel one of the names in
-    // kKernelFamilies, applied where that kernel takes this convolution.
+    // Forced choice "<kernel>:<variant>[:<ksplit>]" with kernel one of the
+    // names in kKernelFamilies, applied where that kernel takes this
+    // convolution (ksplit: the pipelined DMA kernel's contraction split).
+    int force_ks = 0;
     if (const char* v = force) {
         const char* colon = std::strchr(v, ':');
         if (colon) {
             const std::string name(v, colon - v);
             const int i = std::atoi(colon + 1);
+            if (const char* c2 = std::strchr(colon + 1, ':')) force_ks = std::atoi(c2 + 1);
             if (name == "reg" && !nchw_ok && i >= 0 && i < count_of(kRegVariants)) {
                 d.kernel = KERN_REG;
                 d.variant = i;
@@ -265,6 +270,31 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force) {
             }
         }
     }
+    // Split contraction for the pipelined DMA kernel, in two: when the
+    // output tiles leave most CUs idle (at most 128 of them) or the
+    // contraction is very long (4096 elements and more) while there are fewer
+    // than two tiles per CU, and the contraction has at least 16 tiles.  A
+    // sweep over 3x3 and 1x1 layers found more splits, or splits of shorter
+    // contractions, slower than none: the fp32 partials cost a write and a
+    // read of ksplit*M*K*4 bytes.  Every split non-empty.
+    d.ksplit = 1;
+    if (d.kernel == KERN_DMA) {
+        const TileVariant& tv = kDmaVariants[d.variant];
+        const int64_t bk = p.dtype == CONV_F32 ? tv.bk / 2 : tv.bk;
+        const int64_t kc = implicit ? d.Kg : d.Kl;
+        const int64_t nkt = (kc + bk - 1) / bk;
+        const int64_t tiles = ((d.M + tv.bm - 1) / tv.bm) * ((p.K + tv.bn - 1) / tv.bn);
+        int64_t ks = 1;
+        if (force_ks > 0) {
+            ks = force_ks < 8 ? force_ks : 8;
+        } else if (tiles > 0 && tiles < 512 && nkt >= 16 && (tiles <= 128 || kc >= 4096)) {
+            ks = 2;
+        }
+        if (ks > nkt) ks = nkt;
+        while (ks > 1 && (ks - 1) * ((nkt + ks - 1) / ks) >= nkt) --ks;
+        d.ksplit = int32_t(ks < 1 ? 1 : ks);
+    }
+
     d.tile_rows = 0;
     if (d.kernel == KERN_NCHW_TILE) {
         d.tile_rows = int32_t(nchw_tile_rows(kNchwTileVariants[d.variant]));
@@ -308,6 +338,14 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force) {
                                    kTile16Variants[d.variant].ks
                              : uint64_t(kpad) * d.Kg * e;
         d.ws_bytes = p.N == 0 ? 0 : d.bytes_filter;
+    }
+
+    // The split contraction's fp32 partials go last in the workspace.
+    d.off_part = 0;
+    d.bytes_part = d.ksplit > 1 ? uint64_t(d.ksplit) * uint64_t(d.M) * uint64_t(p.K) * 4 : 0;
+    if (d.bytes_part && p.N > 0) {
+        d.off_part = round_up(d.ws_bytes, kWsAlign);
+        d.ws_bytes = d.off_part + d.bytes_part;
     }
 
     // NCHW staging tile: whole strip columns of R*C values per LDS row.
@@ -370,7 +408,12 @@ conv_status_t plan_lstm(const conv_params_t& p, int64_t c_x, conv_desc& d) {
     if (d.bytes_low / 16 > 0xffffffffull) return CONV_ERR_UNSUPPORTED;
     d.lstm_cx = c_x;
     d.kernel = KERN_DMA;
-    d.variant = -1;   // the dedicated ConvLSTM tile (kLstmVariant)
+    d.variant = -1;   // the dedicated ConvLSTM tile (kLstmVariant): no split contraction
+    if (d.ksplit > 1) {
+        d.ws_bytes = d.off_part;
+        d.off_part = d.bytes_part = 0;
+    }
+    d.ksplit = 1;
     d.tile_m = kLstmVariant.bm;
     d.tile_n = kLstmVariant.bn;
     d.tile_k = kLstmVariant.bk / 2;
@@ -689,6 +732,9 @@ conv_status_t conv_plan_info(conv_desc_t d, conv_plan_info_t* info) {
     i.elem_bytes = d->elem;
     i.kernel = d->kernel;
     i.kernel_variant = d->variant;
+    i.ws_partial_offset = d->off_part;
+    i.ws_partial_bytes = d->bytes_part;
+    i.ksplit = d->ksplit;
     *info = i;
     return CONV_OK;
 }
@@ -711,7 +757,7 @@ conv_status_t conv_lower_input(conv_desc_t d, const void* x, void* ws, void* str
     return run_lower(*d, x, ws, static_cast<hipStream_t>(stream));
 }
 
-conv_status_t conv_contract(conv_desc_t d, const void* x, const void* w, const void* bias, void* y, const void* ws,
+conv_status_t conv_contract(conv_desc_t d, const void* x, const void* w, const void* bias, void* y, void* ws,
                             void* stream) {
     if (!desc_ok(d) || d->lstm_cx) return CONV_ERR_INVALID_ARG;
     if (d->p.N == 0) return CONV_OK;

@@ -127,6 +127,10 @@ struct conv_desc {
     int32_t tile_m, tile_n, tile_k;
     int32_t tile_rows;  // fp32 NCHW small-window kernel: output rows per workgroup
     int64_t lstm_cx;    // ConvLSTM step descriptor: input channels taken from x (0: a plain convolution)
+    // Split contraction (pipelined DMA kernel): ksplit ranges of the
+    // contraction per output tile, fp32 partials [ksplit][M*K] in ws at off_part.
+    int32_t ksplit;
+    uint64_t off_part, bytes_part;
     // NCHW staging (0 = use the element-wise kernel)
     int32_t stage_chunk, stage_ld;
 };

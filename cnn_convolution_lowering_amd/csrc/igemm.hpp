@@ -55,6 +55,10 @@ struct GemmArgs {
     const void* c_prev;
     void* c_out;
     int32_t lstm_kh;
+    // Split contraction: ksplit > 1 workgroups per output tile (blockIdx.y),
+    // each storing fp32 partial sums in the output layout at part + z*M*K.
+    int32_t ksplit;
+    void* part;
     // window loaders: the convolution itself
     int32_t C, H, W, R, S;
     int32_t sh, sw, ph, pw, dh, dw;

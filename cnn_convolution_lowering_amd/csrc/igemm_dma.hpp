@@ -323,6 +323,21 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 8 / (WGM * WGN)) conv_gemm_dma
     la.init(g, m0, tid);
     lb.init(g, n0, tid);
 
+    // Split contraction (ksplit > 1): workgroup z = blockIdx.y takes the
+    // contraction tiles [z*per, min(nkt, (z+1)*per)); the loaders start there.
+    // An empty range stores zeros.
+    const int nkt_all = (g.Kc + BK - 1) / BK;
+    int nkt = nkt_all;
+    if (g.ksplit > 1) {
+        const int per = (nkt_all + g.ksplit - 1) / g.ksplit;
+        const int kt0 = int(blockIdx.y) * per;
+        nkt = nkt_all - kt0 < per ? nkt_all - kt0 : per;
+        for (int i = 0; i < kt0; ++i) {
+            la.next(g);
+            lb.next(g);
+        }
+    }
+
     const uint32_t lds0 = lds_offset(smem);
     // Issue one tile's loads into stage `st`: load j of wave w covers LDS chunk
     // slots [j*NT + w*64, +64) of the A (then B) region.
@@ -345,7 +360,6 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 8 / (WGM * WGN)) conv_gemm_dma
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int nkt = (g.Kc + BK - 1) / BK;
 #pragma unroll
     for (int st = 0; st < STAGES - 1; ++st)
         if (st < nkt) issue(st);
@@ -397,8 +411,74 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 8 / (WGM * WGN)) conv_gemm_dma
     if constexpr (EPI == 1) {
         static_assert(sizeof(T) == 4 && !NHWC_OUT && BN == 64 && WGN == 1, "ConvLSTM epilogue tile");
         lstm_store_tile<WM, TM, TN>(g, acc, m0, n0, wm, lane);
+    } else if (g.ksplit > 1) {
+        // this split's fp32 partial sums, no bias, in the output layout
+        GemmArgs h = g;
+        h.y = static_cast<float*>(g.part) + int64_t(blockIdx.y) * g.M * g.K;
+        h.bias = nullptr;
+        store_tile<float, BM, BN, WM, WN, TM, TN, NHWC_OUT>(h, acc, m0, n0, wm, wn, lane);
     } else {
         store_tile<T, BM, BN, WM, WN, TM, TN, NHWC_OUT>(g, acc, m0, n0, wm, wn, lane);
+    }
+}
+
+// Sum of the split contraction's partials, in split order (deterministic),
+// plus the bias, rounded to the storage type: y[i] = round(sum_z part[z][i] +
+// bias[k(i)]), k(i) = i % K (NPQK) or (i / PQ) % K (NKPQ).  Four consecutive
+// elements per thread.
+struct SplitReduceArgs {
+    const float* part;
+    const void* bias;
+    void* y;
+    int64_t total;   // M*K
+    int32_t K, PQ, ksplit, nhwc;
+};
+
+template <typename T>
+__global__ void __launch_bounds__(256) splitk_reduce_kernel(SplitReduceArgs a) {
+    const T* __restrict__ bias = static_cast<const T*>(a.bias);
+    T* __restrict__ y = static_cast<T*>(a.y);
+    const bool vec = (a.total & 3) == 0;   // every split's slice 16-byte aligned
+    for (int64_t i0 = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 4; i0 < a.total;
+         i0 += int64_t(gridDim.x) * 256 * 4) {
+        float v[4] = {0.f, 0.f, 0.f, 0.f};
+        if (vec) {
+            for (int z = 0; z < a.ksplit; ++z) {
+                const f32x4 s = __builtin_bit_cast(f32x4, load16(a.part + z * a.total + i0));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] += s[e];
+            }
+        } else {
+            for (int z = 0; z < a.ksplit; ++z)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (i0 + e < a.total) v[e] += a.part[z * a.total + i0 + e];
+        }
+        T out[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int64_t i = i0 + e;
+            const int k = int(a.nhwc ? i % a.K : (i / a.PQ) % a.K);
+            out[e] = from_f32<T>(v[e] + (bias ? to_f32(bias[k]) : 0.f));
+        }
+        if (vec) {
+            if constexpr (sizeof(T) == 4) {
+                store16(y + i0, u32x4{__float_as_uint(out[0]), __float_as_uint(out[1]), __float_as_uint(out[2]),
+                                      __float_as_uint(out[3])});
+            } else {
+                union {
+                    u32x2 u;
+                    T e[4];
+                } pk;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) pk.e[e] = out[e];
+                *reinterpret_cast<u32x2*>(y + i0) = pk.u;
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (i0 + e < a.total) y[i0 + e] = out[e];
+        }
     }
 }
 

@@ -125,6 +125,12 @@ typedef struct {
      * copy in MFMA fragment order;
      * kernel_variant indexes that kernel's compiled tile shapes */
     int32_t kernel, kernel_variant;
+    /* split contraction (kernel 1 only): ksplit workgroups share each output
+     * tile, each over a contiguous range of the contraction, their fp32
+     * partial sums [ksplit][N*P*Q*K] in the output layout at
+     * ws_partial_offset; 1 = no split (ws_partial_bytes 0) */
+    uint64_t ws_partial_offset, ws_partial_bytes;
+    int32_t ksplit;
 } conv_plan_info_t;
 
 /* Validate *p and build a descriptor.  Host only: no HIP call is made, so it
@@ -175,9 +181,12 @@ conv_status_t conv_lower_input(conv_desc_t d, const void* x, void* ws, void* str
 /* Stage 3: the MFMA contraction over the lowered operand and packed filter
  * with the fused epilogue y = round(acc + bias[k]).  Reads ws written by
  * stages 1 and 2; reads x in place when the lowering is elided and w in place
- * when the pack is a no-op. */
+ * when the pack is a no-op.  When the plan splits the contraction
+ * (conv_plan_info_t.ksplit > 1) it also writes the fp32 partial sums into
+ * ws's partial area and then enqueues their reduction (sum in split order,
+ * plus bias, rounded once). */
 conv_status_t conv_contract(conv_desc_t d, const void* x, const void* w, const void* bias, void* y,
-                            const void* ws, void* stream);
+                            void* ws, void* stream);
 
 /* ---------------------------------------------------------------- ConvLSTM step
  * "GPU-Accelerating MSCRED with CUDA, im2col, GEMM, and a Custom PyTorch

@@ -41,8 +41,9 @@ def test_exports_every_header_function():
 def test_struct_sizes_match_header():
     # conv_params_t: 7 int64 + 6 int32 + 3 enums (int) -> 92 bytes, padded to 96
     assert ctypes.sizeof(cl.ConvParams) == 96
-    # conv_plan_info_t: 7 int64 + 7 uint64 + 7 int32 -> 140, padded to 144
-    assert ctypes.sizeof(cl.PlanInfo) == 144
+    # conv_plan_info_t: 7 int64 + 7 uint64 + 7 int32 (140, padded to 144),
+    # then 2 uint64 + 1 int32 -> 164, padded to 168
+    assert ctypes.sizeof(cl.PlanInfo) == 168
 
 
 @pytest.mark.parametrize("field,value", [
@@ -176,7 +177,10 @@ def test_workspace_formula(layout, dtype, algo):
         assert info["ws_lowered_bytes"] == low
         assert info["ws_lowered_offset"] % 256 == 0
         assert c.workspace_bytes >= info["ws_filter_bytes"] + low
-        if low:
+        if info["ksplit"] > 1:   # split contraction: the fp32 partials go last
+            assert info["ws_partial_offset"] >= info["ws_lowered_offset"] + low
+            assert c.workspace_bytes == info["ws_partial_offset"] + info["ws_partial_bytes"]
+        elif low:
             assert c.workspace_bytes == info["ws_lowered_offset"] + low
 
 
@@ -220,7 +224,10 @@ def test_implicit_needs_no_workspace(layout, dtype):
     for (C, R, S, st, pd) in [(3, 7, 7, 2, 3), (32, 3, 3, 2, 0), (128, 1, 1, 1, 0), (5, 2, 3, 1, 1)]:
         c = cl.Conv2d(4, C, 20, 20, 16, R, S, stride=st, padding=pd, layout=layout, dtype=dtype, algo="implicit")
         assert c.info["ws_lowered_bytes"] == 0 and c.info["lowering_elided"] == 1
-        assert c.workspace_bytes == c.info["ws_filter_bytes"]
+        # besides the filter copy, a split contraction's fp32 partials (not lowered input)
+        part = c.info["ws_partial_bytes"]
+        assert part == (c.info["ksplit"] * c.info["M"] * 16 * 4 if c.info["ksplit"] > 1 else 0)
+        assert c.workspace_bytes == (c.info["ws_partial_offset"] + part if part else c.info["ws_filter_bytes"])
         elem = {"f32": 4, "f16": 2, "bf16": 2}[dtype]
         if c.info["kernel"] == 8:
             assert layout == "nhwc" and dtype != "f32" and C * st % 2 == 0
@@ -228,7 +235,7 @@ def test_implicit_needs_no_workspace(layout, dtype):
             assert 0 < c.info["ws_filter_bytes"] <= 64 * 8 * 4 * ((chunks + 3) // 4) * elem
         else:
             assert c.info["ws_filter_bytes"] <= 32 * C * R * S * elem
-            if C % 16:
+            if C % 16 and not part:
                 assert c.workspace_bytes == 0
 
 
@@ -305,3 +312,42 @@ def test_tune_argument_checks_on_the_host():
     empty = cl.Conv2d(0, 16, 8, 8, 16, 3, 3, padding=1, layout="nchw", dtype="f32")
     assert lib.conv_tune(empty.handle, None, None, None, None, None, 0, 3, None, ctypes.byref(res)) == 0
     assert (res.kernel, res.kernel_variant) == (empty.info["kernel"], empty.info["kernel_variant"])
+
+def test_split_contraction_plan(monkeypatch):
+    """The pipelined kernel splits the contraction in two when the output
+    tiles leave most CUs idle or the contraction is very long; the fp32
+    partials take ksplit*M*K*4 bytes after the other workspace parts,
+    256-byte aligned, and a forced split is honoured (within the contraction
+    tiles, every split non-empty)."""
+    monkeypatch.delenv("CONVLOWER_KERNEL", raising=False)
+    for a in [(128, 512, 7, 7, 512, 3, 3, 1), (8, 192, 20, 20, 96, 3, 3, 1)]:   # 4608-long; 25 tiles
+        c = cl.Conv2d(*a[:7], padding=a[7], layout="nhwc", dtype="bf16", algo="implicit")
+        i = c.info
+        assert i["kernel"] == 1 and i["ksplit"] == 2, a
+        assert i["ws_lowered_bytes"] == 0 and i["ws_partial_bytes"] == 2 * i["M"] * a[4] * 4
+        assert i["ws_partial_offset"] % 256 == 0
+        assert i["ws_partial_offset"] >= i["ws_filter_offset"] + i["ws_filter_bytes"]
+        assert c.workspace_bytes == i["ws_partial_offset"] + i["ws_partial_bytes"]
+    # plenty of output tiles, a contraction of moderate length over 196 tiles,
+    # or a short contraction: no split
+    for a in [(32, 128, 64, 64, 128, 3, 3, 1), (128, 1024, 14, 14, 256, 1, 1, 0), (2, 32, 8, 8, 32, 1, 1, 0),
+              (64, 256, 14, 14, 256, 3, 3, 1)]:
+        for algo in ("implicit", "im2win", "im2col"):
+            c = cl.Conv2d(*a[:7], padding=a[7], layout="nhwc", dtype="f16", algo=algo)
+            assert c.info["ksplit"] == 1 and c.info["ws_partial_bytes"] == 0, (a, algo)
+    # im2win keeps its lowered part and adds the partials after it
+    c = cl.Conv2d(8, 192, 20, 20, 96, 3, 3, padding=1, layout="nhwc", dtype="f16", algo="im2win")
+    i = c.info
+    if i["ksplit"] > 1:
+        assert i["ws_partial_offset"] >= i["ws_lowered_offset"] + i["ws_lowered_bytes"]
+    # forced: honoured, clamped to the contraction tiles
+    monkeypatch.setenv("CONVLOWER_KERNEL", "dma:1:3")
+    c = cl.Conv2d(2, 64, 17, 17, 72, 3, 3, padding=1, layout="nhwc", dtype="f16", algo="implicit")
+    assert c.info["ksplit"] == 3 and c.info["ws_partial_bytes"] == 3 * c.info["M"] * 72 * 4
+    monkeypatch.setenv("CONVLOWER_KERNEL", "dma:1:8")
+    c = cl.Conv2d(2, 16, 9, 9, 24, 1, 1, layout="nhwc", dtype="f16", algo="implicit")   # one contraction tile
+    assert c.info["ksplit"] == 1 and c.info["ws_partial_bytes"] == 0
+    # the ConvLSTM step never splits
+    monkeypatch.delenv("CONVLOWER_KERNEL", raising=False)
+    cell = cl.ConvLSTMCell(4, 32, 32, 30, 30, 3, 3, padding=1, algo="im2win")
+    assert cell.info["ksplit"] == 1 and cell.info["ws_partial_bytes"] == 0

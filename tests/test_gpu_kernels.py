@@ -185,6 +185,47 @@ def test_small_window_kernel_integer_exact(dev, monkeypatch):
     assert ran >= 2
 
 
+# (dtype, layout, algo, shape, forced "dma:<variant>:<ksplit>"): ragged pixel
+# and channel tiles, contraction ranges that do not split evenly, NHWC and
+# NCHW outputs, fused and lowered operands
+SPLIT_CASES = [
+    ("f16", "nhwc", "implicit", (2, 64, 17, 17, 72, 3, 3, (1, 1), (1, 1), (1, 1)), "dma:1:2"),
+    ("bf16", "nhwc", "implicit", (3, 96, 9, 9, 40, 3, 3, (1, 1), (2, 2), (2, 2)), "dma:0:3"),
+    ("f16", "nhwc", "im2win", (2, 64, 17, 17, 130, 3, 3, (2, 1), (1, 1), (1, 1)), "dma:2:4"),
+    ("f32", "nchw", "im2col", (2, 16, 13, 11, 33, 3, 3, (1, 1), (1, 1), (1, 1)), "dma:1:3"),
+    ("f32", "nhwc", "implicit", (2, 32, 10, 10, 48, 3, 3, (1, 1), (1, 1), (1, 1)), "dma:1:2"),
+    ("bf16", "nhwc", "implicit", (4, 256, 7, 7, 256, 3, 3, (1, 1), (1, 1), (1, 1)), "dma:2:5"),
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=lambda c: "%s-%s-%s-%s" % (c[0], c[1], c[2], c[4]))
+def test_split_contraction_parity(dev, monkeypatch, case):
+    """Contraction split over several workgroups per output tile: fp32
+    partials in the workspace, summed in split order with the bias by the
+    reduction kernel.  Parity against the oracle with and without a bias, and
+    the same bits on a second run (the sum order is fixed)."""
+    dt, lay, algo, (N, C, H, W, K, R, S, st, pd, dl), forced = case
+    monkeypatch.setenv("CONVLOWER_KERNEL", forced)
+    d = cl.Conv2d(N, C, H, W, K, R, S, stride=st, padding=pd, dilation=dl, layout=lay, dtype=dt, algo=algo)
+    ks = int(forced.split(":")[2])
+    assert d.info["kernel"] == 1 and d.info["ksplit"] == ks, d.info
+    assert d.info["ws_partial_bytes"] == ks * d.info["M"] * K * 4
+    g = torch.Generator().manual_seed(91)
+    x = (torch.rand(N, C, H, W, generator=g) * 2 - 1).to(TORCH_DT[dt])
+    w = (torch.randn(K, C, R, S, generator=g) / np.sqrt(C * R * S)).to(TORCH_DT[dt])
+    b = (torch.randn(K, generator=g) * 0.1).to(TORCH_DT[dt])
+    xl, wl = _perm(x, lay), _perm(w, lay)
+    xd, wd = xl.to(dev), wl.to(dev)
+    for bias in (b, None):
+        print("split case %s %s %s %s %s bias=%s" % (dt, lay, algo, case[3], forced, bias is not None), flush=True)
+        y1 = d.forward(xd, wd, None if bias is None else bias.to(dev))
+        y2 = d.forward(xd, wd, None if bias is None else bias.to(dev))
+        torch.cuda.synchronize()
+        assert torch.equal(y1.cpu().view(-1).view(torch.uint8), y2.cpu().view(-1).view(torch.uint8))
+        ref, yabs = oracle.conv2d(xl, wl, bias, layout=lay, stride=st, padding=pd, dilation=dl, with_abs=True)
+        assert_parity(to_f64(y1.cpu()), ref, yabs, dt, "split %s" % forced)
+
+
 @pytest.mark.parametrize("case", [
     ("f32", "nchw", (64, 32, 30, 30, 64, 3, 3, (2, 2), (0, 0), (1, 1))),
     ("f32", "nchw", (16, 3, 30, 30, 32, 3, 3, (1, 1), (1, 1), (1, 1))),
