@@ -333,6 +333,49 @@ def load_traffic(kernel_key: str):
     return rec.get("bytes_per_launch")
 
 
+def gemm_calibration(dev):
+    """torch.matmul (hipBLASLt) on A[M x C*R*S] @ B[C*R*S x K] for every layer
+    of the 16-bit workloads -- the contraction of each convolution without its
+    window gather -- and on 8192^3, 20 timed calls each after 3 warm-up calls;
+    one JSON line per product."""
+    import torch
+    import cnn_convolution_lowering_amd as cl
+    from cnn_convolution_lowering_amd.workloads import workload_spec
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16}
+    shapes = []
+    for name in ("c3", "c4", "c5"):
+        spec = workload_spec(name)
+        H = W = None
+        for L in spec.layers:
+            if L.H is not None:
+                H, W = L.H, L.W
+            c = cl.Conv2d(spec.N, L.C, H, W, L.K, L.R, L.S, stride=L.stride, padding=L.padding,
+                          layout=spec.layout, dtype=spec.dtype, algo="implicit")
+            shapes.append(("%s %s" % (name, L.label), spec.dtype, c.info["M"], L.K, L.C * L.R * L.S))
+            if spec.chained:
+                H, W = c.P, c.Q
+    shapes += [("square 8192", dt, 8192, 8192, 8192) for dt in ("f16", "bf16")]
+    for label, dt, M, N, K in shapes:
+        g = torch.Generator(device=dev).manual_seed(7)
+        a = torch.randn(M, K, device=dev, generator=g).to(tdt[dt])
+        b = torch.randn(K, N, device=dev, generator=g).to(tdt[dt])
+        for _ in range(3):
+            c = a @ b
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(20):
+            c = a @ b
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 20
+        tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+        print(json.dumps({"gemm": label, "dtype": dt, "M": M, "N": N, "K": K, "ms": round(ms, 4),
+                          "tflops": round(tf, 1), "frac_of_peak": round(tf / PEAK_TFLOPS[dt], 3)}), flush=True)
+        del a, b, c
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -352,6 +395,10 @@ def main(argv=None):
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (5 times), to scale "
                          "the HBM byte counters of a profiler against a transfer of known size")
+    ap.add_argument("--gemm-calibration", action="store_true",
+                    help="only time the vendor GEMM (torch.matmul, hipBLASLt) on the plain M x K x C*R*S "
+                         "products of the 16-bit workloads' layers and on an 8192^3 product: what the "
+                         "library reaches on this GPU, for context next to the MFMA peak")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -377,6 +424,8 @@ def main(argv=None):
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_per_launch": n, "launches": 5}))
         return 0
+    if args.gemm_calibration:
+        return gemm_calibration(dev)
     if args.workload == "lstm":
         if args.algo == "implicit":
             args.algo = "im2win"   # the ConvLSTM step reads x and h through the lowering

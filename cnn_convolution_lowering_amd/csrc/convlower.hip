@@ -199,12 +199,13 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force) {
         d.kernel = KERN_DMA;
         d.variant = p.K <= 32 ? 0 : (p.K <= 64 ? 1 : (p.dtype == CONV_F32 ? 2 : 6));
         if (d.variant >= 2 && (d.M / 256) * ((p.K + 127) / 128) >= 512) d.variant = 3;
-        // Taps sharing an input row (S >= 3), enough 512 x 128 tiles to give
+        // Taps sharing an input row (S >= 5), enough 512 x 128 tiles to give
         // most CUs one, and output channels filling whole 128-wide tiles:
         // the register-streamed strip kernel (a sweep over the kernel-size
-        // layers put it ahead from 3 x 3 up).
+        // layers put it level with the 256 x 128 pipelined tiles at 5 x 5 and
+        // ahead from 7 x 7 up; at 3 x 3 the pipelined tiles are faster).
         const StripVariant& rb = kStripRbVariants[5];
-        if (p.S >= 3 && p.K % 128 == 0 && (d.M / rb.bm) * (p.K / rb.bn) >= 192 && strip_fits(rb)) {
+        if (p.S >= 5 && p.K % 128 == 0 && (d.M / rb.bm) * (p.K / rb.bn) >= 192 && strip_fits(rb)) {
             d.kernel = KERN_STRIP_RB;
             d.variant = 5;
         }
