@@ -272,12 +272,12 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force) {
         }
     }
     // Split contraction for the pipelined DMA kernel, in two: when the
-    // output tiles leave most CUs idle (at most 128 of them) or the
+    // output tiles leave three CUs in four idle (at most 64 of them) or the
     // contraction is very long (4096 elements and more) while there are fewer
     // than two tiles per CU, and the contraction has at least 16 tiles.  A
-    // sweep over 3x3 and 1x1 layers found more splits, or splits of shorter
-    // contractions, slower than none: the fp32 partials cost a write and a
-    // read of ksplit*M*K*4 bytes.  Every split non-empty.
+    // sweep over 3x3 and 1x1 layers found more splits, or splits with ~100
+    // tiles and shorter contractions, slower than none: the fp32 partials
+    // cost a write and a read of ksplit*M*K*4 bytes.  Every split non-empty.
     d.ksplit = 1;
     if (d.kernel == KERN_DMA) {
         const TileVariant& tv = kDmaVariants[d.variant];
@@ -288,7 +288,7 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force) {
         int64_t ks = 1;
         if (force_ks > 0) {
             ks = force_ks < 8 ? force_ks : 8;
-        } else if (tiles > 0 && tiles < 512 && nkt >= 16 && (tiles <= 128 || kc >= 4096)) {
+        } else if (tiles > 0 && tiles < 512 && nkt >= 16 && (tiles <= 64 || kc >= 4096)) {
             ks = 2;
         }
         if (ks > nkt) ks = nkt;
