@@ -59,7 +59,7 @@ class PlanInfo(ctypes.Structure):
 
 class TuneResult(ctypes.Structure):
     _fields_ = [("candidates", ctypes.c_int32), ("kernel", ctypes.c_int32), ("kernel_variant", ctypes.c_int32),
-                ("default_ms", ctypes.c_float), ("best_ms", ctypes.c_float)]
+                ("default_ms", ctypes.c_float), ("best_ms", ctypes.c_float), ("ksplit", ctypes.c_int32)]
 
 
 _lib = None

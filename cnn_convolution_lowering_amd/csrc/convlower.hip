@@ -795,6 +795,7 @@ conv_status_t conv_tune(conv_desc_t d, const void* x, const void* w, const void*
     *result = conv_tune_result_t{};
     result->kernel = d->kernel;
     result->kernel_variant = d->variant;
+    result->ksplit = d->ksplit;
     if (d->p.N == 0) return CONV_OK;
     const hipStream_t st = static_cast<hipStream_t>(stream);
     conv_status_t s;
@@ -832,19 +833,29 @@ conv_status_t conv_tune(conv_desc_t d, const void* x, const void* w, const void*
     result->default_ms = best_ms;
     int n = 1;
     for (const KernelFamily& f : kKernelFamilies) {
+        // the pipelined kernel also without and with a split contraction (2, 4)
+        const int nks = f.kernel == KERN_DMA ? 3 : 1;
         for (int v = 0; v < f.variants && s == CONV_OK; ++v) {
-            char force[32];
-            std::snprintf(force, sizeof(force), "%s:%d", f.name, v);
-            conv_desc c{};
-            c.p = d->p;
-            if (plan(d->p, c, force) != CONV_OK || c.kernel != f.kernel || c.variant != v) continue;
-            if (c.ws_bytes > ws_bytes || (c.kernel == d->kernel && c.variant == d->variant)) continue;
-            float ms = 0.f;
-            s = time_plan(c, &ms);
-            ++n;
-            if (s == CONV_OK && ms < best_ms) {
-                best = c;
-                best_ms = ms;
+            for (int si = 0; si < nks && s == CONV_OK; ++si) {
+                char force[32];
+                if (f.kernel == KERN_DMA)
+                    std::snprintf(force, sizeof(force), "%s:%d:%d", f.name, v, 1 << si);
+                else
+                    std::snprintf(force, sizeof(force), "%s:%d", f.name, v);
+                conv_desc c{};
+                c.p = d->p;
+                if (plan(d->p, c, force) != CONV_OK || c.kernel != f.kernel || c.variant != v) continue;
+                if (f.kernel == KERN_DMA && c.ksplit != (1 << si)) continue;   // clamped: same as another candidate
+                if (c.ws_bytes > ws_bytes ||
+                    (c.kernel == d->kernel && c.variant == d->variant && c.ksplit == d->ksplit))
+                    continue;
+                float ms = 0.f;
+                s = time_plan(c, &ms);
+                ++n;
+                if (s == CONV_OK && ms < best_ms) {
+                    best = c;
+                    best_ms = ms;
+                }
             }
         }
     }
@@ -857,6 +868,7 @@ conv_status_t conv_tune(conv_desc_t d, const void* x, const void* w, const void*
     result->candidates = n;
     result->kernel = d->kernel;
     result->kernel_variant = d->variant;
+    result->ksplit = d->ksplit;
     result->best_ms = best_ms;
     return CONV_OK;
 }

@@ -230,14 +230,16 @@ conv_status_t conv_lstm_step(conv_desc_t d, const void* x, const void* h_prev, c
  * MSCRED ...", section "CUDA Kernel Design"; the im2win abstract) without
  * fixing a rule.  conv_tune times, on the caller's tensors, the descriptor's
  * current plan and every other compiled contraction kernel and tile variant
- * that takes its convolution and whose workspace fits ws_bytes, and keeps the
- * fastest in d. */
+ * that takes its convolution and whose workspace fits ws_bytes (the pipelined
+ * kernel's variants each without a split contraction and with 2 and 4
+ * splits), and keeps the fastest in d. */
 typedef struct {
     int32_t candidates;       /* plans timed, the current one included */
     int32_t kernel;           /* the plan kept (conv_plan_info_t numbering) */
     int32_t kernel_variant;
     float default_ms;         /* ms per conv2d_fwd-equivalent call, the plan d had on entry */
     float best_ms;            /* ms per call of the plan kept */
+    int32_t ksplit;           /* its split contraction (conv_plan_info_t.ksplit) */
 } conv_tune_result_t;
 
 /* Tune d (not a ConvLSTM descriptor) with reps timed calls per candidate, on

@@ -312,6 +312,7 @@ def test_tune_argument_checks_on_the_host():
     empty = cl.Conv2d(0, 16, 8, 8, 16, 3, 3, padding=1, layout="nchw", dtype="f32")
     assert lib.conv_tune(empty.handle, None, None, None, None, None, 0, 3, None, ctypes.byref(res)) == 0
     assert (res.kernel, res.kernel_variant) == (empty.info["kernel"], empty.info["kernel_variant"])
+    assert res.ksplit == empty.info["ksplit"] == 1
 
 def test_split_contraction_plan(monkeypatch):
     """The pipelined kernel splits the contraction in two when the output

@@ -232,6 +232,7 @@ def test_split_contraction_parity(dev, monkeypatch, case):
     ("f16", "nhwc", (4, 128, 32, 32, 128, 3, 3, (1, 1), (1, 1), (1, 1))),
     ("bf16", "nhwc", (8, 64, 14, 14, 96, 3, 3, (1, 1), (1, 1), (1, 1))),
     ("bf16", "nhwc", (8, 3, 64, 64, 64, 7, 7, (2, 2), (3, 3), (1, 1))),
+    ("bf16", "nhwc", (8, 192, 20, 20, 96, 3, 3, (1, 1), (1, 1), (1, 1))),
 ], ids=lambda c: "%s-%s" % c[:2])
 def test_tune_keeps_a_correct_plan(dev, monkeypatch, case):
     """conv_tune times the candidates and keeps the fastest; the kept plan
@@ -249,7 +250,8 @@ def test_tune_keeps_a_correct_plan(dev, monkeypatch, case):
     print("tune %s %s %s" % (dt, lay, case[2]), flush=True)
     r = d.tune(xd, wd, bd, ws=ws, reps=3)
     assert r["candidates"] >= 2 and r["best_ms"] <= r["default_ms"]
-    assert (r["kernel"], r["kernel_variant"]) == (d.info["kernel"], d.info["kernel_variant"])
+    assert (r["kernel"], r["kernel_variant"], r["ksplit"]) == (d.info["kernel"], d.info["kernel_variant"],
+                                                             d.info["ksplit"])
     assert d.workspace_bytes <= ws.numel()
     y = d.forward(xd, wd, bd, ws=ws)
     torch.cuda.synchronize()
