@@ -66,7 +66,7 @@ template <typename T, int BM, int BN, int BK, int WGM, int WGN, int STAGES, bool
 void launch_dma_core(const conv_desc& d, GemmArgs g, hipStream_t st) {
     g.tiles_n = int32_t((d.p.K + BN - 1) / BN);
     const uint64_t tiles_m = (uint64_t(d.M) + BM - 1) / BM;
-    const dim3 blocks(uint32_t(tiles_m * g.tiles_n), uint32_t(WIDE || EPI || g.ksplit < 1 ? 1 : g.ksplit));
+    const dim3 blocks(uint32_t(tiles_m * g.tiles_n), uint32_t(EPI || g.ksplit < 1 ? 1 : g.ksplit));
     constexpr int NT = 64 * WGM * WGN;
     if constexpr (WIDE)
         conv_gemm_wide_kernel<T, BM, BN, BK, WGM, WGN, STAGES, ASrc, BSrc><<<blocks, NT, 0, st>>>(g);
@@ -110,6 +110,18 @@ void launch_dma_tile(const conv_desc& d, const GemmArgs& g, hipStream_t st) {
         if (nhwc) launch_dma_core<T, BM, BN, BK, WGM, WGN, STAGES, false, true, A, B>(d, g, st);
         else launch_dma_core<T, BM, BN, BK, WGM, WGN, STAGES, false, false, A, B>(d, g, st);
     }
+}
+
+// The split contraction's reduction (after the contraction on the same
+// stream); nothing without a split.
+template <typename T>
+void launch_split_reduce(const conv_desc& d, const GemmArgs& g, const void* bias, void* y, hipStream_t st) {
+    if (d.ksplit <= 1) return;
+    SplitReduceArgs a{static_cast<const float*>(g.part), bias, y, d.M * d.p.K, int32_t(d.p.K),
+                      int32_t(d.P * d.Q), d.ksplit, d.p.layout == CONV_NHWC ? 1 : 0};
+    const uint64_t work = (uint64_t(a.total) + 1023) / 1024;
+    const uint32_t rblocks = uint32_t(work < 256 * 16 ? (work ? work : 1) : 256 * 16);
+    splitk_reduce_kernel<T><<<rblocks, 256, 0, st>>>(a);
 }
 
 template <typename T>
@@ -226,13 +238,7 @@ void launch_gemm(const conv_desc& d, const void* x, const void* w, const void* b
             default: break;
         }
 #undef CONVLOWER_DMA_CASE
-        if (d.ksplit > 1) {
-            SplitReduceArgs a{static_cast<const float*>(g.part), bias, y, d.M * d.p.K, int32_t(d.p.K),
-                              int32_t(d.P * d.Q), d.ksplit, d.p.layout == CONV_NHWC ? 1 : 0};
-            const uint64_t work = (uint64_t(a.total) + 1023) / 1024;
-            const uint32_t rblocks = uint32_t(work < 256 * 16 ? (work ? work : 1) : 256 * 16);
-            splitk_reduce_kernel<T><<<rblocks, 256, 0, st>>>(a);
-        }
+        launch_split_reduce<T>(d, g, bias, y, st);
         return;
     }
     if (d.kernel == KERN_NCHW_TILE) {
@@ -395,6 +401,7 @@ void launch_gemm(const conv_desc& d, const void* x, const void* w, const void* b
                 default: break;
             }
 #undef CONVLOWER_WIDE_CASE
+            launch_split_reduce<T>(d, g, bias, y, st);
         }
         return;
     }

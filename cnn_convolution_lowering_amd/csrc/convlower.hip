@@ -278,9 +278,11 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force) {
     // sweep over 3x3 and 1x1 layers found more splits, or splits with ~100
     // tiles and shorter contractions, slower than none: the fp32 partials
     // cost a write and a read of ksplit*M*K*4 bytes.  Every split non-empty.
+    // (The wide-tile kernel splits only when forced, or when conv_tune keeps
+    // such a plan.)
     d.ksplit = 1;
-    if (d.kernel == KERN_DMA) {
-        const TileVariant& tv = kDmaVariants[d.variant];
+    if (d.kernel == KERN_DMA || d.kernel == KERN_WIDE) {
+        const TileVariant& tv = d.kernel == KERN_DMA ? kDmaVariants[d.variant] : kWideVariants[d.variant];
         const int64_t bk = p.dtype == CONV_F32 ? tv.bk / 2 : tv.bk;
         const int64_t kc = implicit ? d.Kg : d.Kl;
         const int64_t nkt = (kc + bk - 1) / bk;
@@ -288,7 +290,7 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force) {
         int64_t ks = 1;
         if (force_ks > 0) {
             ks = force_ks < 8 ? force_ks : 8;
-        } else if (tiles > 0 && tiles < 512 && nkt >= 16 && (tiles <= 64 || kc >= 4096)) {
+        } else if (d.kernel == KERN_DMA && tiles > 0 && tiles < 512 && nkt >= 16 && (tiles <= 64 || kc >= 4096)) {
             ks = 2;
         }
         if (ks > nkt) ks = nkt;
@@ -833,19 +835,21 @@ conv_status_t conv_tune(conv_desc_t d, const void* x, const void* w, const void*
     result->default_ms = best_ms;
     int n = 1;
     for (const KernelFamily& f : kKernelFamilies) {
-        // the pipelined kernel also without and with a split contraction (2, 4)
-        const int nks = f.kernel == KERN_DMA ? 3 : 1;
+        // the pipelined and wide-tile kernels also without and with a split
+        // contraction (2, 4)
+        const bool splits = f.kernel == KERN_DMA || f.kernel == KERN_WIDE;
+        const int nks = splits ? 3 : 1;
         for (int v = 0; v < f.variants && s == CONV_OK; ++v) {
             for (int si = 0; si < nks && s == CONV_OK; ++si) {
                 char force[32];
-                if (f.kernel == KERN_DMA)
+                if (splits)
                     std::snprintf(force, sizeof(force), "%s:%d:%d", f.name, v, 1 << si);
                 else
                     std::snprintf(force, sizeof(force), "%s:%d", f.name, v);
                 conv_desc c{};
                 c.p = d->p;
                 if (plan(d->p, c, force) != CONV_OK || c.kernel != f.kernel || c.variant != v) continue;
-                if (f.kernel == KERN_DMA && c.ksplit != (1 << si)) continue;   // clamped: same as another candidate
+                if (splits && c.ksplit != (1 << si)) continue;   // clamped: same as another candidate
                 if (c.ws_bytes > ws_bytes ||
                     (c.kernel == d->kernel && c.variant == d->variant && c.ksplit == d->ksplit))
                     continue;

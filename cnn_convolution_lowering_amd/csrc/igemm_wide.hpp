@@ -76,7 +76,8 @@ struct Mfma32<__bf16> {
 // Fused epilogue for 32 x 32 fragments fed (filter, pixel): acc[i][j][e] is
 // output pixel m0 + wm*WM + i*32 + lane%32, channel
 // n0 + wn*WN + j*32 + 8*(e/4) + 4*(lane/32) + e%4, so each group of four e is
-// four consecutive channels of one NPQK row (one 8-byte store).
+// four consecutive channels of one NPQK row (one 8-byte store; 16 bytes for
+// the fp32 partial sums of a split contraction).
 template <typename T, int WM, int WN, int TM, int TN>
 __device__ __forceinline__ void store_tile32_nhwc(const GemmArgs& g, const f32x16 (&acc)[TM][TN], int64_t m0, int n0,
                                                   int wm, int wn, int lane) {
@@ -97,13 +98,18 @@ __device__ __forceinline__ void store_tile32_nhwc(const GemmArgs& g, const f32x1
                 for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e] + ((bias && k + e < g.K) ? to_f32(bias[k + e]) : 0.f);
                 T* dst = y + m * g.K + k;
                 if (k + 3 < g.K && (g.K & 3) == 0) {
-                    union {
-                        u32x2 u;
-                        T e[4];
-                    } pk;
+                    if constexpr (sizeof(T) == 4) {   // fp32 partial sums of a split contraction
+                        store16(dst, u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                                           __float_as_uint(v[3])});
+                    } else {
+                        union {
+                            u32x2 u;
+                            T e[4];
+                        } pk;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) pk.e[e] = from_f32<T>(v[e]);
-                    *reinterpret_cast<u32x2*>(dst) = pk.u;
+                        for (int e = 0; e < 4; ++e) pk.e[e] = from_f32<T>(v[e]);
+                        *reinterpret_cast<u32x2*>(dst) = pk.u;
+                    }
                 } else {
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
@@ -152,6 +158,20 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) conv_gemm_wide_kernel(GemmA
     BSrc lb;
     la.init(g, m0, tid);
     lb.init(g, n0, tid);
+    // Split contraction (ksplit > 1): workgroup z = blockIdx.y takes the
+    // contraction tiles [z*per, min(nkt, (z+1)*per)); the sources start
+    // there.  An empty range stores zeros.
+    const int nkt_all = (g.Kc + BK - 1) / BK;
+    int nkt_split = nkt_all;
+    if (g.ksplit > 1) {
+        const int per = (nkt_all + g.ksplit - 1) / g.ksplit;
+        const int kt0 = int(blockIdx.y) * per;
+        nkt_split = nkt_all - kt0 < per ? nkt_all - kt0 : per;
+        for (int i = 0; i < kt0; ++i) {
+            la.next(g);
+            lb.next(g);
+        }
+    }
 
     const uint32_t lds0 = lds_offset(smem);
     auto issue = [&](int st) {
@@ -221,7 +241,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) conv_gemm_wide_kernel(GemmA
             for (int j = 0; j < TN; ++j) acc[i][j] = Mfma32<T>::run(fb[j], fa[i], acc[i][j]);
     };
 
-    const int nkt = (g.Kc + BK - 1) / BK;
+    const int nkt = nkt_split;
 #pragma unroll
     for (int st = 0; st < STAGES - 1; ++st)
         if (st < nkt) issue(st);
@@ -300,7 +320,15 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) conv_gemm_wide_kernel(GemmA
         });
     }
 
-    store_tile32_nhwc<T, WM, WN, TM, TN>(g, acc, m0, n0, wm, wn, lane);
+    if (g.ksplit > 1) {
+        // this split's fp32 partial sums, no bias
+        GemmArgs h = g;
+        h.y = static_cast<float*>(g.part) + int64_t(blockIdx.y) * g.M * g.K;
+        h.bias = nullptr;
+        store_tile32_nhwc<float, WM, WN, TM, TN>(h, acc, m0, n0, wm, wn, lane);
+    } else {
+        store_tile32_nhwc<T, WM, WN, TM, TN>(g, acc, m0, n0, wm, wn, lane);
+    }
 }
 
 }  // namespace convlower

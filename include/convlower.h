@@ -125,7 +125,7 @@ typedef struct {
      * copy in MFMA fragment order;
      * kernel_variant indexes that kernel's compiled tile shapes */
     int32_t kernel, kernel_variant;
-    /* split contraction (kernel 1 only): ksplit workgroups share each output
+    /* split contraction (kernels 1 and 2): ksplit workgroups share each output
      * tile, each over a contiguous range of the contraction, their fp32
      * partial sums [ksplit][N*P*Q*K] in the output layout at
      * ws_partial_offset; 1 = no split (ws_partial_bytes 0) */
@@ -231,8 +231,8 @@ conv_status_t conv_lstm_step(conv_desc_t d, const void* x, const void* h_prev, c
  * fixing a rule.  conv_tune times, on the caller's tensors, the descriptor's
  * current plan and every other compiled contraction kernel and tile variant
  * that takes its convolution and whose workspace fits ws_bytes (the pipelined
- * kernel's variants each without a split contraction and with 2 and 4
- * splits), and keeps the fastest in d. */
+ * and wide-tile kernels' variants each without a split contraction and with 2
+ * and 4 splits), and keeps the fastest in d. */
 typedef struct {
     int32_t candidates;       /* plans timed, the current one included */
     int32_t kernel;           /* the plan kept (conv_plan_info_t numbering) */

@@ -195,6 +195,9 @@ SPLIT_CASES = [
     ("f32", "nchw", "im2col", (2, 16, 13, 11, 33, 3, 3, (1, 1), (1, 1), (1, 1)), "dma:1:3"),
     ("f32", "nhwc", "implicit", (2, 32, 10, 10, 48, 3, 3, (1, 1), (1, 1), (1, 1)), "dma:1:2"),
     ("bf16", "nhwc", "implicit", (4, 256, 7, 7, 256, 3, 3, (1, 1), (1, 1), (1, 1)), "dma:2:5"),
+    ("f16", "nhwc", "implicit", (2, 64, 17, 17, 72, 3, 3, (1, 1), (1, 1), (1, 1)), "wide:5:2"),
+    ("bf16", "nhwc", "implicit", (3, 96, 9, 9, 300, 3, 3, (1, 1), (2, 2), (2, 2)), "wide:2:3"),
+    ("bf16", "nhwc", "implicit", (8, 128, 7, 7, 256, 3, 3, (1, 1), (1, 1), (1, 1)), "wide:0:8"),
 ]
 
 
@@ -208,7 +211,7 @@ def test_split_contraction_parity(dev, monkeypatch, case):
     monkeypatch.setenv("CONVLOWER_KERNEL", forced)
     d = cl.Conv2d(N, C, H, W, K, R, S, stride=st, padding=pd, dilation=dl, layout=lay, dtype=dt, algo=algo)
     ks = int(forced.split(":")[2])
-    assert d.info["kernel"] == 1 and d.info["ksplit"] == ks, d.info
+    assert d.info["kernel"] == KERNELS[forced.split(":")[0]][0] and d.info["ksplit"] == ks, d.info
     assert d.info["ws_partial_bytes"] == ks * d.info["M"] * K * 4
     g = torch.Generator().manual_seed(91)
     x = (torch.rand(N, C, H, W, generator=g) * 2 - 1).to(TORCH_DT[dt])
