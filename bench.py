@@ -336,12 +336,14 @@ def load_traffic(kernel_key: str):
 def gemm_calibration(dev):
     """torch.matmul (hipBLASLt) on A[M x C*R*S] @ B[C*R*S x K] for every layer
     of the 16-bit workloads -- the contraction of each convolution without its
-    window gather -- and on 8192^3, 20 timed calls each after 3 warm-up calls;
+    window gather -- and on 8192^3 in fp16, bf16 and fp32, 20 timed calls each
+    after 3 warm-up calls;
     one JSON line per product."""
     import torch
     import cnn_convolution_lowering_amd as cl
     from cnn_convolution_lowering_amd.workloads import workload_spec
-    tdt = {"f16": torch.float16, "bf16": torch.bfloat16}
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}
+    torch.backends.cuda.matmul.allow_tf32 = False   # full fp32 products
     shapes = []
     for name in ("c3", "c4", "c5"):
         spec = workload_spec(name)
@@ -354,7 +356,7 @@ def gemm_calibration(dev):
             shapes.append(("%s %s" % (name, L.label), spec.dtype, c.info["M"], L.K, L.C * L.R * L.S))
             if spec.chained:
                 H, W = c.P, c.Q
-    shapes += [("square 8192", dt, 8192, 8192, 8192) for dt in ("f16", "bf16")]
+    shapes += [("square 8192", dt, 8192, 8192, 8192) for dt in ("f16", "bf16", "f32")]
     for label, dt, M, N, K in shapes:
         g = torch.Generator(device=dev).manual_seed(7)
         a = torch.randn(M, K, device=dev, generator=g).to(tdt[dt])
@@ -397,8 +399,9 @@ def main(argv=None):
                          "the HBM byte counters of a profiler against a transfer of known size")
     ap.add_argument("--gemm-calibration", action="store_true",
                     help="only time the vendor GEMM (torch.matmul, hipBLASLt) on the plain M x K x C*R*S "
-                         "products of the 16-bit workloads' layers and on an 8192^3 product: what the "
-                         "library reaches on this GPU, for context next to the MFMA peak")
+                         "products of the 16-bit workloads' layers and on 8192^3 products (fp16, bf16, "
+                         "fp32): what the library reaches on this GPU, a measured peak next to the "
+                         "published one")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
