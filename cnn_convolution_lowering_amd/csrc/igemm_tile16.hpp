@@ -1,5 +1,5 @@
 // 16-bit NHWC implicit contraction for small windows (few input channels,
-// K <= 16*TN): the stem layers whose cost is writing their output.
+// K <= 16*TN*SPLIT): the stem layers whose cost is writing their output.
 //
 // "Enabling Memory-efficient Im2win Convolution with Multi-precision Support
 // on GPU CUDA and Tensor Cores" (abstract): every window is read from one
@@ -10,19 +10,23 @@
 // touches are copied, zero-padded, into LDS once (4-byte LDS-DMA loads
 // straight from x) and every pixel's window is read from there as whole
 // runs.  Workgroups are persistent (a few per CU) and double-buffer the
-// staging: the next tile's rows load while this tile is contracted.  The contraction over one filter row is that run,
-// preceded by `lead` zero-weight elements so that it starts on a 4-byte
-// boundary, padded with zero weights to whole 8-element chunks (one MFMA
-// lane group's share of a 32-deep step); filter row r owns chunks
-// r*cpr .. r*cpr+cpr-1.  Only (C*sw) even and (W*C) even are needed for
-// every run and every staged word to stay 4-byte aligned.
+// staging: the next tile's rows load while this tile is contracted.
+//
+// The contraction over one filter row is that run, preceded by `lead`
+// zero-weight elements so that it starts on a 4-byte boundary, padded with
+// zero weights to whole 8-element chunks (one MFMA lane group's share of a
+// 32-deep step); filter row r owns chunks r*cpr .. r*cpr+cpr-1.  Only (C*sw)
+// even and (W*C) even are needed for every run and every staged word to
+// stay 4-byte aligned.
 //
 // Roles are swapped against the other contraction kernels: the filter is
 // the MFMA A operand (16 output channels by 32 contraction elements, kept in
 // registers for the kernel's life, loaded from a copy already in fragment
-// order), the pixels are B, so each lane's accumulators hold 4*TN channels
-// of one pixel (NHWC-contiguous: two 16-byte stores per pixel at TN = 4).
-// v_mfma_f32_16x16x32_{f16,bf16}, fp32 accumulation.
+// order), the pixels are B, so each lane's accumulators hold 4*TN
+// consecutive channels of one pixel.  A 16-pixel block leaves through a
+// per-wave LDS buffer so that consecutive lanes store consecutive 16-byte
+// pieces of the block's NHWC run.  v_mfma_f32_16x16x32_{f16,bf16}, fp32
+// accumulation.
 #pragma once
 
 #include "igemm_dma.hpp"
