@@ -70,6 +70,8 @@ SHAPES_TILE16 = [
     (1, 6, 9, 50, 16, 3, 3, (2, 1), (0, 1), (1, 1)),
     (3, 3, 11, 10, 8, 2, 4, (1, 2), (0, 1), (1, 1)),
     (256, 2, 42, 12, 16, 3, 3, (2, 2), (1, 1), (1, 1)),
+    (2, 1, 30, 28, 16, 5, 5, (2, 2), (2, 2), (1, 1)),
+    (2, 4, 21, 19, 64, 3, 3, (1, 1), (1, 1), (1, 1)),
 ]
 # (kernel, dtype, layout, algo, shapes)
 PLANS = [
@@ -171,6 +173,8 @@ def test_small_window_kernel_integer_exact(dev, monkeypatch):
     xl, wl = _perm(x, "nhwc"), _perm(w, "nhwc")
     ref = oracle.conv2d(xl, wl, b, layout="nhwc", stride=2, padding=3)
     want = torch.from_numpy(ref).to(torch.float32).to(torch.bfloat16)
+    ref0 = oracle.conv2d(xl, wl, None, layout="nhwc", stride=2, padding=3)
+    want0 = torch.from_numpy(ref0).to(torch.float32).to(torch.bfloat16)
     ran = 0
     for v in range(KERNELS["tile16"][1]):
         monkeypatch.setenv("CONVLOWER_KERNEL", "tile16:%d" % v)
@@ -179,8 +183,10 @@ def test_small_window_kernel_integer_exact(dev, monkeypatch):
             continue
         print("int case tile16:%d" % v, flush=True)
         y = d.forward(xl.to(dev), wl.to(dev), b.to(dev))
+        y0 = d.forward(xl.to(dev), wl.to(dev), None)   # no bias: the accumulators start at zero
         torch.cuda.synchronize()
         assert torch.equal(y.cpu().view(torch.int16), want.view(torch.int16)), v
+        assert torch.equal(y0.cpu().view(torch.int16), want0.view(torch.int16)), v
         ran += 1
     assert ran >= 2
 
