@@ -515,10 +515,19 @@ def main(argv=None):
     for i, l in enumerate(layers):
         info = l["desc"].info
         lay_ms = sum(v for (j, _), v in brk.items() if j == i)
+        # compulsory traffic B_min = x + w + b + y once, and the layer's bound
+        p, eb = l["desc"].params, info["elem_bytes"]
+        b_min = (p.N * p.C * p.H * p.W + p.K * p.C * p.R * p.S + p.K + p.N * p.K * l["desc"].P * l["desc"].Q) * eb
+        mfma_bound = l["flops"] / (peak_f * 1e12) >= b_min / (PEAK_HBM_GBS * 1e9)
+        gbs = b_min / (lay_ms * 1e-3) / 1e9 if lay_ms else None
+        tfs = l["flops"] / (lay_ms * 1e-3) / 1e12 if lay_ms else None
         per_layer.append({
             "layer": l["spec"].label, "gflop": l["flops"] / 1e9,
             "kernels_ms": {st: round(brk[(i, st)], 5) for st in STAGES if (i, st) in brk},
-            "tflops_isolated": l["flops"] / (lay_ms * 1e-3) / 1e12 if lay_ms else None,
+            "tflops_isolated": tfs,
+            "bound": "mfma" if mfma_bound else "hbm",
+            "frac_of_peak": (tfs / peak_f if mfma_bound else gbs / PEAK_HBM_GBS) if lay_ms else None,
+            "b_min_bytes": b_min, "b_min_gbs_isolated": gbs,
             "ws_lowered_bytes": info["ws_lowered_bytes"], "im2col_bytes": info["im2col_bytes"],
             "ws_vs_im2col": info["ws_lowered_bytes"] / info["im2col_bytes"],
             "tile": [info["tile_m"], info["tile_n"], info["tile_k"]]})
