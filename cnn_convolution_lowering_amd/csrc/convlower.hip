@@ -26,7 +26,8 @@ namespace {
 
 constexpr uint32_t kDescMagic = 0x636f6e76u;   // marks a live descriptor
 constexpr uint64_t kWsAlign = 256;             // workspace sub-buffer alignment (bytes)
-constexpr int kStageLdsBytes = 32 * 1024;      // NCHW staging tile budget per block
+constexpr int kStageLdsBytes = 32 * 1024;      // band lowering: staged tile budget per block
+constexpr int64_t kBandItems = 2048;           // band lowering: items to aim for (8 per CU)
 
 }  // namespace
 
@@ -86,7 +87,7 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force) {
     d.im2col_bytes = uint64_t(d.M) * d.Kg * e;
     const uint64_t col_bytes = uint64_t(d.M) * d.Kl * e;
     const uint64_t low_vec = (p.algo == CONV_ALGO_IM2WIN ? d.im2win_bytes : col_bytes) / 16;
-    if (!d.elided && low_vec > 0xffffffffull) return CONV_ERR_UNSUPPORTED;
+    if (!d.elided && low_vec > 0x7fffffffull) return CONV_ERR_UNSUPPORTED;
     if (d.P * d.Q > 0 && (d.W_used * d.RCp / d.vec + 255) / 256 > 65535) return CONV_ERR_UNSUPPORTED;
 
     d.off_filter = 0;
@@ -351,26 +352,45 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force) {
         d.ws_bytes = d.off_part + d.bytes_part;
     }
 
-    // NCHW staging tile: whole strip columns of R*C values per LDS row.
-    d.stage_chunk = 0;
-    d.stage_ld = 0;
-    if (!nhwc) {
-        const int64_t ld = p.R * p.C + 1;     // odd pitch spreads the column-major writes over banks
-        const int64_t cols_fit = kStageLdsBytes / (ld * d.elem);
-        if (p.algo == CONV_ALGO_IM2WIN) {
-            if (cols_fit >= 1) {
-                d.stage_chunk = int32_t(cols_fit < d.W_used ? cols_fit : d.W_used);
-                d.stage_ld = int32_t(ld);
-            }
-        } else {
-            // output columns per block: (chunk-1)*sw + (S-1)*dw + 1 strip columns must fit
-            const int64_t span = (p.S - 1) * int64_t(p.dil_w) + 1;
-            if (cols_fit >= span) {
-                int64_t qc = (cols_fit - span) / p.stride_w + 1;
-                if (qc > d.Q) qc = d.Q;
-                d.stage_chunk = int32_t(qc);
-                d.stage_ld = int32_t(ld);
-            }
+    // Band lowering: the most output rows per item whose staged tile fits
+    // kStageLdsBytes, at most P / ceil(kBandItems / N) rows so that the grid
+    // has about kBandItems items; when one full-width row does not fit
+    // (NCHW), one row and the most output columns that fit.
+    d.band_items = 0;
+    d.band_g = d.band_cw = d.band_br = d.band_tw = d.band_wl = d.band_cs = d.band_lds = 0;
+    if ((!nhwc || !c_vec) && !d.elided && p.N > 0 && d.P > 0 && d.Q > 0) {
+        const bool win = p.algo == CONV_ALGO_IM2WIN;
+        const int64_t full = win ? d.W_used : d.Q;
+        const int64_t span = (p.S - 1) * int64_t(p.dil_w) + 1;
+        auto tw_of = [&](int64_t cw) { return win ? cw : (cw - 1) * p.stride_w + span; };
+        auto br_of = [&](int64_t g) { return (g - 1) * p.stride_h + (p.R - 1) * int64_t(p.dil_h) + 1; };
+        // NCHW rows get an odd pitch, which spreads a wave's column reads over banks.
+        auto wl_of = [&](int64_t cw) { return nhwc ? p.W * p.C : (tw_of(cw) | 1); };
+        // NCHW channel pitch: odd too, or a wave reading every 4th channel meets few banks.
+        auto cs_of = [&](int64_t g, int64_t cw) { return nhwc ? br_of(g) * wl_of(cw) : (br_of(g) * wl_of(cw)) | 1; };
+        auto lds_of = [&](int64_t g, int64_t cw) { return (nhwc ? 1 : p.C) * cs_of(g, cw) * int64_t(d.elem); };
+        const int64_t bands_wanted = (kBandItems + p.N - 1) / p.N;
+        const int64_t g_cap = bands_wanted > 1 ? std::max<int64_t>(1, d.P / bands_wanted) : d.P;
+        int64_t g = 0, cw = full;
+        if (lds_of(1, full) <= kStageLdsBytes) {
+            g = 1;
+            while (g < g_cap && lds_of(g + 1, full) <= kStageLdsBytes) ++g;
+        } else if (!nhwc) {
+            // (tw | 1) <= max_wl keeps C * ((br * wl) | 1) within the budget
+            const int64_t max_wl = (kStageLdsBytes / (p.C * int64_t(d.elem)) - 1) / br_of(1);
+            cw = win ? max_wl - 1 : (max_wl - 1 - span) / p.stride_w + 1;
+            if (max_wl >= 2 && cw >= 1 && tw_of(cw) >= 1 && lds_of(1, cw) <= kStageLdsBytes) g = 1;
+        }
+        const int64_t items = g ? p.N * ((d.P + g - 1) / g) * ((full + cw - 1) / cw) : 0;
+        if (g && items <= lim) {
+            d.band_items = items;
+            d.band_g = int32_t(g);
+            d.band_cw = int32_t(cw);
+            d.band_br = int32_t(br_of(g));
+            d.band_tw = int32_t(nhwc ? p.W * p.C : tw_of(cw));
+            d.band_wl = int32_t(wl_of(cw));
+            d.band_cs = int32_t(cs_of(g, cw));
+            d.band_lds = int32_t(lds_of(g, cw));
         }
     }
     return CONV_OK;
@@ -439,6 +459,12 @@ conv_status_t check_dev(const void* ptr, size_t align) {
     return CONV_OK;
 }
 
+// NHWC band staging moves 16-byte vectors when every x row starts on one.
+bool band_vload(const conv_desc& d, const void* x) {
+    return d.band_items && d.p.layout == CONV_NHWC && (int64_t(d.p.W) * d.p.C * d.elem) % 16 == 0 &&
+           reinterpret_cast<uintptr_t>(x) % 16 == 0;
+}
+
 LowerArgs lower_args(const conv_desc& d, const void* x, void* out) {
     LowerArgs a;
     a.x = x;
@@ -460,10 +486,28 @@ LowerArgs lower_args(const conv_desc& d, const void* x, void* out) {
     a.W_used = int32_t(d.W_used);
     a.RCp = int32_t(d.RCp);
     a.Kl = int32_t(d.Kl);
-    a.chunk = d.stage_chunk;
-    a.lds_ld = d.stage_ld;
     a.x2 = nullptr;
     a.C1 = int32_t(d.p.C);
+    auto fd = [](int64_t v) { return make_fastdiv(uint32_t(v > 1 ? v : 1)); };
+    const bool win = d.p.algo == CONV_ALGO_IM2WIN;
+    const int64_t vpc = (win ? d.RCp : d.Kl) / d.vec;
+    const int64_t full = win ? d.W_used : d.Q;
+    a.G = d.band_g;
+    a.CW = d.band_items ? d.band_cw : int32_t(full);
+    a.BR = d.band_br;
+    a.WL = d.band_wl;
+    a.CS = d.band_cs;
+    a.TW = band_vload(d, x) ? d.band_tw / d.vec : d.band_tw;
+    a.fd_cb = fd(d.band_items ? (full + d.band_cw - 1) / d.band_cw : 1);
+    a.fd_pb = fd(d.band_items ? (d.P + d.band_g - 1) / d.band_g : 1);
+    a.fd_tw = fd(a.TW);
+    a.fd_br = fd(d.band_br);
+    a.fd_row = fd(int64_t(a.CW) * vpc);
+    a.fd_vpc = fd(vpc);
+    a.fd_cpv = fd(d.RCp / d.vec);
+    a.fd_c = fd(d.p.C);
+    a.fd_p = fd(d.P);
+    a.fd_q = fd(d.Q);
     return a;
 }
 
@@ -514,46 +558,64 @@ void launch_pack(const conv_desc& d, const void* w, void* out, hipStream_t st) {
         pack_filter_kernel<T, false><<<blocks, 256, 0, st>>>(a);
 }
 
+// Band lowering of one item per block (band_items > 0).
 template <typename T>
-void launch_lower(const conv_desc& d, const void* x, void* out, hipStream_t st) {
-    constexpr int VEC = Vec<T>::n;
-    const LowerArgs a = lower_args(d, x, out);
-    const bool nhwc = d.p.layout == CONV_NHWC;
-    const bool c_vec = d.p.C % VEC == 0;
-    if (d.p.algo == CONV_ALGO_IM2WIN) {
-        if (nhwc) {
-            const uint32_t vps = uint32_t(d.W_used * d.RCp / VEC);
-            dim3 grid(uint32_t(d.p.N * d.P), (vps + 255) / 256);
-            if (c_vec)
-                im2win_nhwc_kernel<T, true><<<grid, 256, 0, st>>>(a);
-            else
-                im2win_nhwc_kernel<T, false><<<grid, 256, 0, st>>>(a);
-        } else if (d.stage_chunk > 0) {
-            dim3 grid(uint32_t(d.p.N * d.P), uint32_t((d.W_used + d.stage_chunk - 1) / d.stage_chunk));
-            const size_t lds = size_t(d.stage_chunk) * d.stage_ld * sizeof(T);
-            im2win_nchw_kernel<T><<<grid, 256, lds, st>>>(a);
-        } else {
-            const uint64_t total = d.im2win_bytes / 16;
-            lower_generic_kernel<T, false, false><<<grid_stride_blocks(total), 256, 0, st>>>(a, uint32_t(total));
-        }
+void launch_band(const conv_desc& d, const LowerArgs& a, bool vload, hipStream_t st) {
+    const bool col = d.p.algo != CONV_ALGO_IM2WIN;
+    const dim3 grid(uint32_t(d.band_items));
+    const size_t lds = size_t(d.band_lds);
+    if (d.p.layout == CONV_NCHW) {
+        if (col)
+            lower_nchw_band_kernel<T, true><<<grid, 256, lds, st>>>(a);
+        else
+            lower_nchw_band_kernel<T, false><<<grid, 256, lds, st>>>(a);
+    } else if (vload) {
+        if (col)
+            lower_nhwc_band_kernel<T, true, true><<<grid, 256, lds, st>>>(a);
+        else
+            lower_nhwc_band_kernel<T, false, true><<<grid, 256, lds, st>>>(a);
     } else {
-        const uint64_t total = uint64_t(d.M) * d.Kl / VEC;
-        if (nhwc) {
-            if (c_vec)
-                im2col_nhwc_kernel<T, true><<<grid_stride_blocks(total), 256, 0, st>>>(a, uint32_t(total));
-            else
-                im2col_nhwc_kernel<T, false><<<grid_stride_blocks(total), 256, 0, st>>>(a, uint32_t(total));
-        } else if (d.stage_chunk > 0) {
-            dim3 grid(uint32_t(d.p.N * d.P), uint32_t((d.Q + d.stage_chunk - 1) / d.stage_chunk));
-            const int64_t cols = int64_t(d.stage_chunk - 1) * d.p.stride_w + (d.p.S - 1) * int64_t(d.p.dil_w) + 1;
-            const size_t lds = size_t(cols) * d.stage_ld * sizeof(T);
-            im2col_nchw_kernel<T><<<grid, 256, lds, st>>>(a);
-        } else {
-            lower_generic_kernel<T, false, true><<<grid_stride_blocks(total), 256, 0, st>>>(a, uint32_t(total));
-        }
+        if (col)
+            lower_nhwc_band_kernel<T, true, false><<<grid, 256, lds, st>>>(a);
+        else
+            lower_nhwc_band_kernel<T, false, false><<<grid, 256, lds, st>>>(a);
     }
 }
 
+template <typename T>
+void launch_lower_args(const conv_desc& d, const LowerArgs& a, hipStream_t st) {
+    constexpr int VEC = Vec<T>::n;
+    const bool nhwc = d.p.layout == CONV_NHWC;
+    const bool win = d.p.algo == CONV_ALGO_IM2WIN;
+    const uint64_t total = (win ? d.im2win_bytes : uint64_t(d.M) * d.Kl * d.elem) / 16;
+    if (nhwc && d.p.C % VEC == 0) {
+        if (win) {
+            const uint32_t vps = uint32_t(d.W_used * d.RCp / VEC);
+            dim3 grid(uint32_t(d.p.N * d.P), (vps + 256 * LOWER_U - 1) / (256 * LOWER_U));
+            im2win_nhwc_vec_kernel<T><<<grid, 256, 0, st>>>(a);
+        } else {
+            const uint32_t blocks = grid_stride_blocks((total + LOWER_U - 1) / LOWER_U);
+            im2col_nhwc_vec_kernel<T><<<blocks, 256, 0, st>>>(a, uint32_t(total));
+        }
+    } else if (d.band_items > 0) {
+        launch_band<T>(d, a, band_vload(d, a.x), st);
+    } else if (nhwc) {
+        if (win)
+            lower_generic_kernel<T, true, false><<<grid_stride_blocks(total), 256, 0, st>>>(a, uint32_t(total));
+        else
+            lower_generic_kernel<T, true, true><<<grid_stride_blocks(total), 256, 0, st>>>(a, uint32_t(total));
+    } else {
+        if (win)
+            lower_generic_kernel<T, false, false><<<grid_stride_blocks(total), 256, 0, st>>>(a, uint32_t(total));
+        else
+            lower_generic_kernel<T, false, true><<<grid_stride_blocks(total), 256, 0, st>>>(a, uint32_t(total));
+    }
+}
+
+template <typename T>
+void launch_lower(const conv_desc& d, const void* x, void* out, hipStream_t st) {
+    launch_lower_args<T>(d, lower_args(d, x, out), st);
+}
 
 template <template <typename> class F, typename... Args>
 void by_dtype(conv_dtype_t dt, Args&&... args) {
@@ -615,24 +677,7 @@ conv_status_t run_lstm(const conv_desc& d, const void* x, const void* h_prev, co
     LowerArgs a = lower_args(d, x, static_cast<char*>(ws) + d.off_low);
     a.x2 = h_prev;
     a.C1 = int32_t(d.lstm_cx);
-    if (d.p.algo == CONV_ALGO_IM2WIN) {
-        if (d.stage_chunk > 0) {
-            dim3 grid(uint32_t(d.p.N * d.P), uint32_t((d.W_used + d.stage_chunk - 1) / d.stage_chunk));
-            im2win_nchw_kernel<float><<<grid, 256, size_t(d.stage_chunk) * d.stage_ld * 4, st>>>(a);
-        } else {
-            const uint64_t total = d.im2win_bytes / 16;
-            lower_generic_kernel<float, false, false><<<grid_stride_blocks(total), 256, 0, st>>>(a, uint32_t(total));
-        }
-    } else {
-        const uint64_t total = uint64_t(d.M) * d.Kl / 4;
-        if (d.stage_chunk > 0) {
-            dim3 grid(uint32_t(d.p.N * d.P), uint32_t((d.Q + d.stage_chunk - 1) / d.stage_chunk));
-            const int64_t cols = int64_t(d.stage_chunk - 1) * d.p.stride_w + (d.p.S - 1) * int64_t(d.p.dil_w) + 1;
-            im2col_nchw_kernel<float><<<grid, 256, size_t(cols) * d.stage_ld * 4, st>>>(a);
-        } else {
-            lower_generic_kernel<float, false, true><<<grid_stride_blocks(total), 256, 0, st>>>(a, uint32_t(total));
-        }
-    }
+    launch_lower_args<float>(d, a, st);
     conv_status_t s = launch_status();
     if (s != CONV_OK) return s;
     launch_lstm_gemm(d, bias, c_prev, h_out, c_out, ws, st);

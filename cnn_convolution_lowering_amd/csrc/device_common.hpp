@@ -25,6 +25,28 @@ __device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cas
 
 __device__ __forceinline__ void store16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
+// Unsigned division by a divisor fixed at launch, as multiply-high, add and
+// shift: the round-up multiplier of Granlund and Montgomery, "Division by
+// Invariant Integers using Multiplication" (PLDI 1994), section 4.  With
+// l = ceil(log2 d) and m = floor(2^32 * (2^l - d) / d) + 1, floor(n / d) =
+// (mulhi(m, n) + n) >> l for every n < 2^32; the sum is formed in 32 bits,
+// which is exact while n < 2^31 (mulhi(m, n) < n).  Dividends here are
+// element and item indices checked on the host to stay below 2^31.
+struct FastDiv {
+    uint32_t d, m, l;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {   // host side, d >= 1
+    uint32_t l = 0;
+    while ((uint64_t(1) << l) < d) ++l;
+    const uint64_t m = ((uint64_t(1) << 32) * ((uint64_t(1) << l) - d)) / d + 1;
+    return {d, uint32_t(m), l};
+}
+
+__host__ __device__ inline uint32_t fdiv(uint32_t n, FastDiv f) {
+    return (uint32_t((uint64_t(n) * f.m) >> 32) + n) >> f.l;
+}
+
 // Pack VEC elements into one 16-byte vector (used where a vector is gathered
 // element by element).
 template <typename T>

@@ -131,8 +131,12 @@ struct conv_desc {
     // contraction per output tile, fp32 partials [ksplit][M*K] in ws at off_part.
     int32_t ksplit;
     uint64_t off_part, bytes_part;
-    // NCHW staging (0 = use the element-wise kernel)
-    int32_t stage_chunk, stage_ld;
+    // Band lowering (NCHW input, or NHWC with C not a whole number of
+    // vectors): output rows (band_g) and output columns (band_cw) per item,
+    // staged input rows and columns, LDS row and channel pitch (elements) and
+    // tile bytes.  band_items == 0: the element-wise kernel.
+    int64_t band_items;
+    int32_t band_g, band_cw, band_br, band_tw, band_wl, band_cs, band_lds;
 };
 
 namespace convlower {

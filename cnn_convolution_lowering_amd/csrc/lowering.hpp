@@ -33,13 +33,26 @@ struct LowerArgs {
     int32_t W_used;   // strip columns per (n, p)
     int32_t RCp;      // R*C padded to whole vectors
     int32_t Kl;       // S*RCp
-    int32_t chunk;    // strip columns (im2win NCHW) or output columns (im2col NCHW) per block
-    int32_t lds_ld;   // LDS row pitch (elements) of the NCHW staging tile
     // NCHW input split over two tensors (a ConvLSTM step's x and h): channels
     // c < C1 come from x (C1 per image), the rest from x2 (C - C1 per image).
     // C1 == C and x2 == nullptr for an ordinary convolution.
     const void* x2;
     int32_t C1;
+    // Band kernels: an item is (image, band of G output rows, chunk of CW
+    // output columns -- strip columns for im2win, q for im2col); it stages
+    // BR input rows of TW tile columns at LDS row pitch WL elements (and,
+    // NCHW, channel pitch CS elements).
+    int32_t G, CW, BR, TW, WL, CS;
+    FastDiv fd_cb;    // column chunks per band
+    FastDiv fd_pb;    // bands per image
+    FastDiv fd_tw;    // staging: elements (NCHW) or vectors (NHWC) per staged row
+    FastDiv fd_br;    // staging: rows per channel (NCHW)
+    FastDiv fd_row;   // output vectors per output row of the band: CW * fd_vpc.d
+    FastDiv fd_vpc;   // output vectors per output column: RCp/VEC (im2win) or Kl/VEC (im2col)
+    FastDiv fd_cpv;   // RCp/VEC
+    FastDiv fd_c;     // C
+    FastDiv fd_p;     // P
+    FastDiv fd_q;     // Q
 };
 
 // x element (n, c, h, w) in either layout, zero outside the image.
@@ -54,166 +67,288 @@ __device__ __forceinline__ T x_at(const LowerArgs& a, const T* __restrict__ x, i
 }
 
 // ---------------------------------------------------------------------------
-// im2win, NHWC input: one thread per 16-byte vector of the strip.  When C is a
-// whole number of vectors, a vector of the strip is a vector of one x row, so
-// the copy is 16-byte load -> 16-byte store; otherwise it gathers elements.
-// grid.x = N*P strips, grid.y = ceil(W_used*RCp/VEC / 256).
-template <typename T, bool C_VEC>
-__global__ void __launch_bounds__(256) im2win_nhwc_kernel(LowerArgs a) {
+// im2win and im2col, NHWC input with C a whole number of 16-byte vectors: a
+// vector of the lowered row is a vector of one x row, so the copy is 16-byte
+// load -> 16-byte store.  Each thread moves LOWER_U vectors LOWER_U*256 apart,
+// all loads issued before the first store; outside the image the load reads
+// a clamped in-image address and the value is replaced by zeros, so no load
+// is conditional.
+constexpr int LOWER_U = 4;
+
+// Lowered vector v of strip (n, p): strip column j, elements t0.. of R*C.
+template <typename T>
+__device__ __forceinline__ const T* nhwc_src(const LowerArgs& a, const T* x, int n, int p, int wcol, int t0,
+                                             bool& in) {
+    const int r = int(fdiv(uint32_t(t0), a.fd_c));
+    const int c0 = t0 - r * a.C;
+    const int h = p * a.sh - a.ph + r * a.dh;
+    in = h >= 0 && h < a.H && wcol >= 0 && wcol < a.W;
+    const int hc = min(max(h, 0), a.H - 1), wc = min(max(wcol, 0), a.W - 1);
+    return x + ((int64_t(n) * a.H + hc) * a.W + wc) * a.C + c0;
+}
+
+// grid.x = N*P strips, grid.y = ceil(W_used*RCp/VEC / (256*LOWER_U)).
+template <typename T>
+__global__ void __launch_bounds__(256) im2win_nhwc_vec_kernel(LowerArgs a) {
     constexpr int VEC = Vec<T>::n;
     const int strip = blockIdx.x;
-    const int cpv = a.RCp / VEC;                 // vectors per strip column
-    const int v = blockIdx.y * 256 + threadIdx.x;
-    if (v >= a.W_used * cpv) return;
-    const int n = strip / a.P, p = strip - (strip / a.P) * a.P;
-    const int j = v / cpv;
-    const int t0 = (v - j * cpv) * VEC;
-    const int wcol = j - a.pw;
+    const int n = int(fdiv(uint32_t(strip), a.fd_p)), p = strip - n * a.P;
+    const uint32_t vps = uint32_t(a.W_used) * a.fd_cpv.d;   // vectors per strip
     const T* __restrict__ x = static_cast<const T*>(a.x);
-    T* out = static_cast<T*>(a.out) + (int64_t(strip) * a.W_used * a.RCp + int64_t(v) * VEC);
-    if (C_VEC) {
-        const int r = t0 / a.C, c0 = t0 - (t0 / a.C) * a.C;
-        const int h = p * a.sh - a.ph + r * a.dh;
-        u32x4 val = zero4();
-        if (h >= 0 && h < a.H && wcol >= 0 && wcol < a.W)
-            val = load16(x + ((int64_t(n) * a.H + h) * a.W + wcol) * a.C + c0);
-        store16(out, val);
+    T* out = static_cast<T*>(a.out) + int64_t(strip) * a.W_used * a.RCp;
+    u32x4 val[LOWER_U];
+    bool live[LOWER_U];
+#pragma unroll
+    for (int u = 0; u < LOWER_U; ++u) {
+        const uint32_t v = (blockIdx.y * LOWER_U + u) * 256 + threadIdx.x;
+        live[u] = v < vps;
+        const uint32_t vv = live[u] ? v : 0;
+        const int j = int(fdiv(vv, a.fd_cpv));
+        const int t0 = int(vv - uint32_t(j) * a.fd_cpv.d) * VEC;
+        bool in;
+        const T* src = nhwc_src<T>(a, x, n, p, j - a.pw, t0, in);
+        val[u] = load16(src);
+        if (!in) val[u] = zero4();
+    }
+#pragma unroll
+    for (int u = 0; u < LOWER_U; ++u) {
+        const uint32_t v = (blockIdx.y * LOWER_U + u) * 256 + threadIdx.x;
+        if (live[u]) store16(out + int64_t(v) * VEC, val[u]);
+    }
+}
+
+// Grid-stride over the M*Kl/VEC vectors of Col (checked on the host to stay
+// below 2^31), LOWER_U vectors per thread and pass.
+template <typename T>
+__global__ void __launch_bounds__(256) im2col_nhwc_vec_kernel(LowerArgs a, uint32_t total_vec) {
+    constexpr int VEC = Vec<T>::n;
+    const T* __restrict__ x = static_cast<const T*>(a.x);
+    T* out = static_cast<T*>(a.out);
+    const uint32_t step = gridDim.x * 256u * LOWER_U;
+    for (uint32_t base = blockIdx.x * 256u * LOWER_U + threadIdx.x; base < total_vec; base += step) {
+        u32x4 val[LOWER_U];
+#pragma unroll
+        for (int u = 0; u < LOWER_U; ++u) {
+            const uint32_t v0 = base + u * 256u;
+            const uint32_t v = v0 < total_vec ? v0 : 0;
+            const uint32_t m = fdiv(v, a.fd_vpc);                  // Col row (n, p, q)
+            const uint32_t kv = v - m * a.fd_vpc.d;
+            const uint32_t s = fdiv(kv, a.fd_cpv);
+            const int t0 = int(kv - s * a.fd_cpv.d) * VEC;
+            const uint32_t np = fdiv(m, a.fd_q);
+            const int q = int(m - np * a.fd_q.d);
+            const int n = int(fdiv(np, a.fd_p)), p = int(np) - n * a.P;
+            bool in;
+            const T* src = nhwc_src<T>(a, x, n, p, q * a.sw - a.pw + int(s) * a.dw, t0, in);
+            val[u] = load16(src);
+            if (!in) val[u] = zero4();
+        }
+#pragma unroll
+        for (int u = 0; u < LOWER_U; ++u) {
+            const uint32_t v = base + u * 256u;
+            if (v < total_vec) store16(out + int64_t(v) * VEC, val[u]);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Band lowering, for the layouts where a lowered vector is not a vector of
+// x: NCHW input (a strip column gathers one element from each of R*C rows)
+// and NHWC input whose C is not a whole number of vectors.  An item is an
+// image n, a band of G output rows from p0 = pb*G and a chunk of CW output
+// columns.  The block first copies the input the item reads into LDS with
+// coalesced loads (zeros outside the image), then writes the item's lowered
+// rows as whole 16-byte vectors, consecutive lanes on consecutive vectors,
+// gathering each vector's elements from LDS.  grid.x = items; dynamic LDS is
+// the staged tile.
+
+// Item -> (n, pb, cb).
+__device__ __forceinline__ void band_item(const LowerArgs& a, int& n, int& pb, int& cb) {
+    const uint32_t item = blockIdx.x;
+    const uint32_t ib = fdiv(item, a.fd_cb);
+    cb = int(item - ib * a.fd_cb.d);
+    n = int(fdiv(ib, a.fd_pb));
+    pb = int(ib) - n * int(a.fd_pb.d);
+}
+
+// Output vector v of the item -> (pp = output row in the band, col = output
+// column in the chunk, s = kernel column (im2col), tv = vector in RCp).
+template <bool COL>
+__device__ __forceinline__ void band_vector(const LowerArgs& a, uint32_t v, int& pp, int& col, int& s, int& tv) {
+    pp = int(fdiv(v, a.fd_row));
+    const uint32_t rem = v - uint32_t(pp) * a.fd_row.d;
+    col = int(fdiv(rem, a.fd_vpc));
+    const uint32_t kv = rem - uint32_t(col) * a.fd_vpc.d;
+    if (COL) {
+        s = int(fdiv(kv, a.fd_cpv));
+        tv = int(kv) - s * int(a.fd_cpv.d);
     } else {
+        s = 0;
+        tv = int(kv);
+    }
+}
+
+// NCHW: the tile is tile[c][hh][jj] (row pitch WL, channel pitch CS, both
+// odd, so that a wave's reads of every k-th channel spread over banks): input
+// row h = p0*sh - ph + hh of channel c, strip column j0 + jj (x column
+// j0 + jj - pw), where j0 is the chunk's first strip column.  BR = (G-1)*sh
+// + (R-1)*dh + 1 rows; TW = CW strip columns (im2win) or (CW-1)*sw +
+// (S-1)*dw + 1 (im2col).
+template <typename T, bool COL>
+__global__ void __launch_bounds__(256) lower_nchw_band_kernel(LowerArgs a) {
+    constexpr int VEC = Vec<T>::n;
+    constexpr int U = 8;
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
+    T* tile = reinterpret_cast<T*>(lds_raw);
+    int n, pb, cb;
+    band_item(a, n, pb, cb);
+    const int p0 = pb * a.G;
+    const int hlo = p0 * a.sh - a.ph;
+    const int j0 = COL ? cb * a.CW * a.sw : cb * a.CW;
+    const T* __restrict__ x = static_cast<const T*>(a.x);
+    const T* __restrict__ x2 = static_cast<const T*>(a.x2);
+    const int64_t plane = int64_t(a.H) * a.W;
+    const T* xn = x + int64_t(n) * a.C1 * plane;
+    const T* x2n = x2 + int64_t(n) * (a.C - a.C1) * plane - int64_t(a.C1) * plane;   // indexed by c >= C1
+    const uint32_t stage_total = uint32_t(a.C) * a.BR * a.TW;
+    for (uint32_t base = threadIdx.x; base < stage_total; base += 256 * U) {
+        T val[U];
+        int dst[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t i0 = base + u * 256;
+            const uint32_t i = i0 < stage_total ? i0 : 0;
+            const uint32_t row = fdiv(i, a.fd_tw);
+            const int jj = int(i - row * a.fd_tw.d);
+            const int c = int(fdiv(row, a.fd_br));
+            const int hh = int(row) - c * a.BR;
+            const int h = hlo + hh, w = j0 + jj - a.pw;
+            const bool in = h >= 0 && h < a.H && w >= 0 && w < a.W;
+            const int hc = min(max(h, 0), a.H - 1), wc = min(max(w, 0), a.W - 1);
+            const T* src = (c < a.C1 ? xn : x2n) + int64_t(c) * plane + hc * a.W + wc;
+            val[u] = *src;
+            if (!in) val[u] = T(0);
+            dst[u] = i0 < stage_total ? c * a.CS + hh * a.WL + jj : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (dst[u] >= 0) tile[dst[u]] = val[u];
+    }
+    __syncthreads();
+    const int RC = a.R * a.C;
+    const int cstride = a.CS;
+    const uint32_t out_total = uint32_t(a.G) * a.fd_row.d;
+    for (uint32_t v = threadIdx.x; v < out_total; v += 256) {
+        int pp, col, s, tv;
+        band_vector<COL>(a, v, pp, col, s, tv);
+        const int p = p0 + pp;
+        const int gcol = cb * a.CW + col;
+        if (p >= a.P || gcol >= (COL ? a.Q : a.W_used)) continue;
+        const int tcol = COL ? col * a.sw + s * a.dw : col;
+        const int t0 = tv * VEC;
+        int r = int(fdiv(uint32_t(t0), a.fd_c));
+        int c = t0 - r * a.C;
+        const T* trow = tile + pp * a.sh * a.WL + tcol;
         Pack16<T> pk;
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
-            const int t = t0 + e;
-            T val = T(0);
-            if (t < a.R * a.C) {
-                const int r = t / a.C, c = t - (t / a.C) * a.C;
-                val = x_at<T, true>(a, x, n, c, p * a.sh - a.ph + r * a.dh, wcol);
+            pk.e[e] = t0 + e < RC ? trow[c * cstride + r * a.dh * a.WL] : T(0);
+            if (++c == a.C) {
+                c = 0;
+                ++r;
             }
-            pk.e[e] = val;
         }
+        T* out = static_cast<T*>(a.out) +
+                 (COL ? ((int64_t(n) * a.P + p) * a.Q + gcol) * a.Kl + (s * a.RCp + t0)
+                      : ((int64_t(n) * a.P + p) * a.W_used + gcol) * a.RCp + t0);
         store16(out, pk.v);
     }
 }
 
-// ---------------------------------------------------------------------------
-// NCHW input: x rows are contiguous along w, the strip is contiguous along
-// (r, c) inside a column, so stage through LDS: read coalesced along w into a
-// [column][r*C + c] tile, then write whole 16-byte strip vectors.
-// Tile rows [j0, j0 + ncols) of strip (n, p); LDS pitch a.lds_ld elements.
-template <typename T>
-__device__ __forceinline__ void stage_strip_nchw(const LowerArgs& a, T* tile, int n, int p, int j0, int ncols) {
-    const T* __restrict__ x = static_cast<const T*>(a.x);
-    const int RC = a.R * a.C;
-    const int total = ncols * RC;
-    for (int idx = threadIdx.x; idx < total; idx += blockDim.x) {
-        const int jj = idx % ncols;
-        const int rc = idx / ncols;
-        const int c = rc % a.C, r = rc / a.C;
-        const int h = p * a.sh - a.ph + r * a.dh;
-        tile[jj * a.lds_ld + rc] = x_at<T, false>(a, x, n, c, h, j0 + jj - a.pw);
-    }
-}
-
-// grid.x = N*P strips, grid.y = ceil(W_used / chunk); dynamic LDS = chunk*lds_ld elements.
-template <typename T>
-__global__ void __launch_bounds__(256) im2win_nchw_kernel(LowerArgs a) {
+// NHWC with C not a whole number of vectors: the tile is BR whole x rows,
+// tile[hh][w*C + c] at pitch WL = W*C elements (row h = p0*sh - ph + hh,
+// zeros outside the image); a column outside the image gives a zero vector.
+// VLOAD: W*C*sizeof(T) and x are 16-byte aligned, so the staging moves
+// 16-byte vectors (fd_tw counts vectors per row); otherwise elements.
+template <typename T, bool COL, bool VLOAD>
+__global__ void __launch_bounds__(256) lower_nhwc_band_kernel(LowerArgs a) {
     constexpr int VEC = Vec<T>::n;
+    constexpr int U = VLOAD ? 8 : 16;
     extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
     T* tile = reinterpret_cast<T*>(lds_raw);
-    const int strip = blockIdx.x;
-    const int n = strip / a.P, p = strip - (strip / a.P) * a.P;
-    const int j0 = blockIdx.y * a.chunk;
-    const int ncols = min(a.chunk, a.W_used - j0);
-    stage_strip_nchw<T>(a, tile, n, p, j0, ncols);
+    int n, pb, cb;
+    band_item(a, n, pb, cb);
+    const int p0 = pb * a.G;
+    const int hlo = p0 * a.sh - a.ph;
+    const T* __restrict__ xn = static_cast<const T*>(a.x) + int64_t(n) * a.H * a.WL;
+    const uint32_t stage_total = uint32_t(a.BR) * a.fd_tw.d;
+    for (uint32_t base = threadIdx.x; base < stage_total; base += 256 * U) {
+        if (VLOAD) {
+            u32x4 val[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t i0 = base + u * 256;
+                const uint32_t i = i0 < stage_total ? i0 : 0;
+                const int hh = int(fdiv(i, a.fd_tw));
+                const int cv = int(i - uint32_t(hh) * a.fd_tw.d);
+                const int h = hlo + hh;
+                const int hc = min(max(h, 0), a.H - 1);
+                val[u] = load16(xn + int64_t(hc) * a.WL + cv * VEC);
+                if (h < 0 || h >= a.H) val[u] = zero4();
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t i = base + u * 256;
+                if (i < stage_total) store16(tile + int64_t(i) * VEC, val[u]);
+            }
+        } else {
+            T val[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t i0 = base + u * 256;
+                const uint32_t i = i0 < stage_total ? i0 : 0;
+                const int hh = int(fdiv(i, a.fd_tw));
+                const int h = hlo + hh;
+                const int hc = min(max(h, 0), a.H - 1);
+                val[u] = xn[int64_t(hc) * a.WL + (int(i) - hh * a.WL)];
+                if (h < 0 || h >= a.H) val[u] = T(0);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t i = base + u * 256;
+                if (i < stage_total) tile[i] = val[u];
+            }
+        }
+    }
     __syncthreads();
     const int RC = a.R * a.C;
-    const int cpv = a.RCp / VEC;
-    T* out = static_cast<T*>(a.out) + (int64_t(strip) * a.W_used + j0) * a.RCp;
-    for (int idx = threadIdx.x; idx < ncols * cpv; idx += blockDim.x) {
-        const int jj = idx / cpv, tv = idx - (idx / cpv) * cpv;
+    const uint32_t out_total = uint32_t(a.G) * a.fd_row.d;
+    for (uint32_t v = threadIdx.x; v < out_total; v += 256) {
+        int pp, col, s, tv;
+        band_vector<COL>(a, v, pp, col, s, tv);
+        const int p = p0 + pp;
+        if (p >= a.P) continue;
+        const int wcol = COL ? col * a.sw - a.pw + s * a.dw : col - a.pw;
+        const int t0 = tv * VEC;
         Pack16<T> pk;
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            const int t = tv * VEC + e;
-            pk.e[e] = t < RC ? tile[jj * a.lds_ld + t] : T(0);
-        }
-        store16(out + int64_t(jj) * a.RCp + tv * VEC, pk.v);
-    }
-}
-
-// ---------------------------------------------------------------------------
-// im2col, NHWC input: one thread per 16-byte vector of Col; grid-stride over
-// M*Kl/VEC vectors (checked on the host to fit 32 bits).
-template <typename T, bool C_VEC>
-__global__ void __launch_bounds__(256) im2col_nhwc_kernel(LowerArgs a, uint32_t total_vec) {
-    constexpr int VEC = Vec<T>::n;
-    const T* __restrict__ x = static_cast<const T*>(a.x);
-    const uint32_t vpr = a.Kl / VEC;   // vectors per Col row
-    const uint32_t cpv = a.RCp / VEC;
-    const uint32_t PQ = uint32_t(a.P) * a.Q;
-    for (uint32_t v = blockIdx.x * 256u + threadIdx.x; v < total_vec; v += gridDim.x * 256u) {
-        const uint32_t m = v / vpr, kv = v - (v / vpr) * vpr;
-        const uint32_t s = kv / cpv;
-        const int t0 = int(kv - s * cpv) * VEC;
-        const uint32_t n = m / PQ, pq = m - (m / PQ) * PQ;
-        const int p = int(pq / a.Q), q = int(pq - (pq / a.Q) * a.Q);
-        const int wcol = q * a.sw - a.pw + int(s) * a.dw;
-        T* out = static_cast<T*>(a.out) + int64_t(v) * VEC;
-        if (C_VEC) {
-            const int r = t0 / a.C, c0 = t0 - (t0 / a.C) * a.C;
-            const int h = p * a.sh - a.ph + r * a.dh;
-            u32x4 val = zero4();
-            if (h >= 0 && h < a.H && wcol >= 0 && wcol < a.W)
-                val = load16(x + ((int64_t(n) * a.H + h) * a.W + wcol) * a.C + c0);
-            store16(out, val);
-        } else {
-            Pack16<T> pk;
+        pk.v = zero4();
+        if (wcol >= 0 && wcol < a.W) {
+            int r = int(fdiv(uint32_t(t0), a.fd_c));
+            int c = t0 - r * a.C;
+            const T* trow = tile + pp * a.sh * a.WL + wcol * a.C;
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
-                const int t = t0 + e;
-                T val = T(0);
-                if (t < a.R * a.C) {
-                    const int r = t / a.C, c = t - (t / a.C) * a.C;
-                    val = x_at<T, true>(a, x, int(n), c, p * a.sh - a.ph + r * a.dh, wcol);
+                pk.e[e] = t0 + e < RC ? trow[r * a.dh * a.WL + c] : T(0);
+                if (++c == a.C) {
+                    c = 0;
+                    ++r;
                 }
-                pk.e[e] = val;
             }
-            store16(out, pk.v);
         }
-    }
-}
-
-// im2col, NCHW input: a block stages the strip columns its output columns
-// [q0, q0 + chunk) need for one (n, p), then writes those Col rows.
-// grid.x = N*P, grid.y = ceil(Q / chunk); dynamic LDS = cols*lds_ld elements
-// with cols = (chunk-1)*sw + (S-1)*dw + 1.
-template <typename T>
-__global__ void __launch_bounds__(256) im2col_nchw_kernel(LowerArgs a) {
-    constexpr int VEC = Vec<T>::n;
-    extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
-    T* tile = reinterpret_cast<T*>(lds_raw);
-    const int strip = blockIdx.x;
-    const int n = strip / a.P, p = strip - (strip / a.P) * a.P;
-    const int q0 = blockIdx.y * a.chunk;
-    const int nq = min(a.chunk, a.Q - q0);
-    const int j0 = q0 * a.sw;
-    const int ncols = (nq - 1) * a.sw + (a.S - 1) * a.dw + 1;
-    stage_strip_nchw<T>(a, tile, n, p, j0, ncols);
-    __syncthreads();
-    const int RC = a.R * a.C;
-    const int cpv = a.RCp / VEC;
-    const int vpr = a.Kl / VEC;
-    T* out = static_cast<T*>(a.out) + (int64_t(strip) * a.Q + q0) * a.Kl;
-    for (int idx = threadIdx.x; idx < nq * vpr; idx += blockDim.x) {
-        const int qq = idx / vpr, kv = idx - (idx / vpr) * vpr;
-        const int s = kv / cpv, tv = kv - (kv / cpv) * cpv;
-        const int jj = qq * a.sw + s * a.dw;
-        Pack16<T> pk;
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            const int t = tv * VEC + e;
-            pk.e[e] = t < RC ? tile[jj * a.lds_ld + t] : T(0);
-        }
-        store16(out + int64_t(qq) * a.Kl + kv * VEC, pk.v);
+        T* out = static_cast<T*>(a.out) +
+                 (COL ? ((int64_t(n) * a.P + p) * a.Q + col) * a.Kl + (s * a.RCp + t0)
+                      : ((int64_t(n) * a.P + p) * a.W_used + col) * a.RCp + t0);
+        store16(out, pk.v);
     }
 }
 

@@ -145,7 +145,13 @@ def _bits(t):
 @pytest.mark.parametrize("lay", ["nchw", "nhwc"])
 @pytest.mark.parametrize("shape", [(2, 3, 9, 11, 8, 3, 3, (1, 1), (1, 1), (1, 1)),
                                    (1, 16, 7, 12, 5, 3, 2, (2, 3), (2, 1), (1, 2)),
-                                   (2, 8, 10, 10, 4, 2, 5, (1, 2), (0, 2), (2, 1))])
+                                   (2, 8, 10, 10, 4, 2, 5, (1, 2), (0, 2), (2, 1)),
+                                   # enough images for bands of several output rows, the last band ragged
+                                   (1100, 3, 13, 11, 4, 3, 3, (1, 1), (1, 1), (1, 1)),
+                                   (2100, 5, 13, 9, 4, 3, 2, (2, 1), (1, 0), (1, 2)),
+                                   # NCHW rows too wide for one staged tile: chunks of output columns
+                                   (1, 64, 12, 200, 4, 3, 3, (1, 1), (1, 1), (1, 1)),
+                                   (2, 40, 9, 150, 4, 4, 5, (2, 3), (1, 2), (1, 2))])
 def test_lowered_layouts_exact(dev, dt, lay, shape):
     N, C, H, W, K, R, S, st, pd, dl = shape
     g = torch.Generator().manual_seed(9)
