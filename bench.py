@@ -168,7 +168,12 @@ def kernel_symbol(l, stage):
             return "pack_filter_frag_kernel"
         return {6: "pack_filter_frag_f32_kernel", 8: "pack_filter_tile16_kernel"}.get(info["kernel"],
                                                                                     "pack_filter_kernel")
-    return "%s_%s_kernel" % (d.algo, d.layout)
+    # NHWC with C a whole number of 16-byte vectors: the direct vector copy;
+    # otherwise the band kernel (the element-wise fallback, for a one-column
+    # tile beyond the LDS budget, occurs in none of the workloads).
+    if d.layout == "nhwc" and d.params.C % (16 // info["elem_bytes"]) == 0:
+        return "%s_nhwc_vec_kernel" % d.algo
+    return "lower_%s_band_kernel" % d.layout
 
 
 def cpu_baseline(wl, budget_s=10.0):
