@@ -151,7 +151,12 @@ def _bits(t):
                                    (2100, 5, 13, 9, 4, 3, 2, (2, 1), (1, 0), (1, 2)),
                                    # NCHW rows too wide for one staged tile: chunks of output columns
                                    (1, 64, 12, 200, 4, 3, 3, (1, 1), (1, 1), (1, 1)),
-                                   (2, 40, 9, 150, 4, 4, 5, (2, 3), (1, 2), (1, 2))])
+                                   (2, 40, 9, 150, 4, 4, 5, (2, 3), (1, 2), (1, 2)),
+                                   # one-column tiles beyond the LDS budget: the element-wise
+                                   # kernel (NCHW C*R large; NHWC C=3 rows of 3000 columns),
+                                   # and NCHW column chunks with a ragged last chunk
+                                   (1, 2048, 6, 6, 4, 5, 5, (1, 1), (1, 1), (1, 1)),
+                                   (1, 3, 9, 3000, 4, 7, 7, (1, 1), (0, 3), (1, 1))])
 def test_lowered_layouts_exact(dev, dt, lay, shape):
     N, C, H, W, K, R, S, st, pd, dl = shape
     g = torch.Generator().manual_seed(9)
