@@ -205,11 +205,10 @@ __global__ void __launch_bounds__(256) lower_nchw_band_kernel(LowerArgs a) {
     const int p0 = pb * a.G;
     const int hlo = p0 * a.sh - a.ph;
     const int j0 = COL ? cb * a.CW * a.sw : cb * a.CW;
-    const T* __restrict__ x = static_cast<const T*>(a.x);
-    const T* __restrict__ x2 = static_cast<const T*>(a.x2);
     const int64_t plane = int64_t(a.H) * a.W;
-    const T* xn = x + int64_t(n) * a.C1 * plane;
-    const T* x2n = x2 + int64_t(n) * (a.C - a.C1) * plane - int64_t(a.C1) * plane;   // indexed by c >= C1
+    const T* xn = static_cast<const T*>(a.x) + int64_t(n) * a.C1 * plane;
+    // channels c >= C1 (a second input only): plane c - C1 of image n there
+    const T* x2n = a.x2 ? static_cast<const T*>(a.x2) + int64_t(n) * (a.C - a.C1) * plane : xn;
     const uint32_t stage_total = uint32_t(a.C) * a.BR * a.TW;
     for (uint32_t base = threadIdx.x; base < stage_total; base += 256 * U) {
         T val[U];
@@ -225,7 +224,7 @@ __global__ void __launch_bounds__(256) lower_nchw_band_kernel(LowerArgs a) {
             const int h = hlo + hh, w = j0 + jj - a.pw;
             const bool in = h >= 0 && h < a.H && w >= 0 && w < a.W;
             const int hc = min(max(h, 0), a.H - 1), wc = min(max(w, 0), a.W - 1);
-            const T* src = (c < a.C1 ? xn : x2n) + int64_t(c) * plane + hc * a.W + wc;
+            const T* src = (c < a.C1 ? xn + int64_t(c) * plane : x2n + int64_t(c - a.C1) * plane) + hc * a.W + wc;
             val[u] = *src;
             if (!in) val[u] = T(0);
             dst[u] = i0 < stage_total ? c * a.CS + hh * a.WL + jj : -1;
