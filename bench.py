@@ -410,8 +410,8 @@ def main(argv=None):
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
-        print("bench.py: this build measures one GPU; --gpus %d is not supported (the path shards over "
-              "images with no exchange, see the design notes)" % args.gpus, file=sys.stderr)
+        print("bench.py: measures one GPU; --gpus %d is not supported (the convolution would shard over "
+              "images, each GPU running the same path on its share with no exchange)" % args.gpus, file=sys.stderr)
         return 2
 
     import torch
