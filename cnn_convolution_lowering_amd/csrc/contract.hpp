@@ -235,6 +235,7 @@ void launch_gemm(const conv_desc& d, const void* x, const void* w, const void* b
             CONVLOWER_DMA_CASE(4)
             CONVLOWER_DMA_CASE(5)
             CONVLOWER_DMA_CASE(6)
+            CONVLOWER_DMA_CASE(7)
             default: break;
         }
 #undef CONVLOWER_DMA_CASE

@@ -196,9 +196,11 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force) {
         // BN covers the output channels up to 128; BM = 256 where that still
         // gives two workgroups per CU, else 128 -- for 16-bit operands with
         // 64-deep stages (two of them), which a sweep over the 3x3 and 1x1
-        // layers put ahead of four 32-deep ones.
+        // layers put ahead of four 32-deep ones, and eight waves: with fewer
+        // tiles than two per CU, two waves per SIMD on one tile beat one
+        // (4-12 % on the 3x3 and 1x1 layers of a few hundred tiles).
         d.kernel = KERN_DMA;
-        d.variant = p.K <= 32 ? 0 : (p.K <= 64 ? 1 : (p.dtype == CONV_F32 ? 2 : 6));
+        d.variant = p.K <= 32 ? 0 : (p.K <= 64 ? 1 : (p.dtype == CONV_F32 ? 2 : 7));
         if (d.variant >= 2 && (d.M / 256) * ((p.K + 127) / 128) >= 512) d.variant = 3;
         // Taps sharing an input row (S >= 5), enough 512 x 128 tiles to give
         // most CUs one, and output channels filling whole 128-wide tiles:
