@@ -467,6 +467,15 @@ bool band_vload(const conv_desc& d, const void* x) {
            reinterpret_cast<uintptr_t>(x) % 16 == 0;
 }
 
+// NCHW band staging moves 16-byte vectors when one chunk spans every column
+// and every channel plane of x (and of the second input) starts on one.
+bool band_vload_nchw(const conv_desc& d, const void* x, const void* x2) {
+    const int64_t full = d.p.algo == CONV_ALGO_IM2WIN ? d.W_used : d.Q;
+    return d.band_items && d.p.layout == CONV_NCHW && d.band_cw == full &&
+           (int64_t(d.p.H) * d.p.W * d.elem) % 16 == 0 && reinterpret_cast<uintptr_t>(x) % 16 == 0 &&
+           reinterpret_cast<uintptr_t>(x2) % 16 == 0;
+}
+
 LowerArgs lower_args(const conv_desc& d, const void* x, void* out) {
     LowerArgs a;
     a.x = x;
@@ -510,6 +519,8 @@ LowerArgs lower_args(const conv_desc& d, const void* x, void* out) {
     a.fd_c = fd(d.p.C);
     a.fd_p = fd(d.P);
     a.fd_q = fd(d.Q);
+    a.fd_nv = fd((int64_t(d.band_br) * d.p.W + d.vec - 1) / d.vec + 1);
+    a.fd_w = fd(d.p.W);
     return a;
 }
 
@@ -567,10 +578,15 @@ void launch_band(const conv_desc& d, const LowerArgs& a, bool vload, hipStream_t
     const dim3 grid(uint32_t(d.band_items));
     const size_t lds = size_t(d.band_lds);
     if (d.p.layout == CONV_NCHW) {
-        if (col)
-            lower_nchw_band_kernel<T, true><<<grid, 256, lds, st>>>(a);
+        const bool v = band_vload_nchw(d, a.x, a.x2);
+        if (col && v)
+            lower_nchw_band_kernel<T, true, true><<<grid, 256, lds, st>>>(a);
+        else if (col)
+            lower_nchw_band_kernel<T, true, false><<<grid, 256, lds, st>>>(a);
+        else if (v)
+            lower_nchw_band_kernel<T, false, true><<<grid, 256, lds, st>>>(a);
         else
-            lower_nchw_band_kernel<T, false><<<grid, 256, lds, st>>>(a);
+            lower_nchw_band_kernel<T, false, false><<<grid, 256, lds, st>>>(a);
     } else if (vload) {
         if (col)
             lower_nhwc_band_kernel<T, true, true><<<grid, 256, lds, st>>>(a);

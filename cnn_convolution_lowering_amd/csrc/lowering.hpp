@@ -53,6 +53,8 @@ struct LowerArgs {
     FastDiv fd_c;     // C
     FastDiv fd_p;     // P
     FastDiv fd_q;     // Q
+    FastDiv fd_nv;    // NCHW vector staging: 16-byte vectors per channel's band of rows (bound)
+    FastDiv fd_w;     // W
 };
 
 // x element (n, c, h, w) in either layout, zero outside the image.
@@ -194,7 +196,12 @@ __device__ __forceinline__ void band_vector(const LowerArgs& a, uint32_t v, int&
 // j0 + jj - pw), where j0 is the chunk's first strip column.  BR = (G-1)*sh
 // + (R-1)*dh + 1 rows; TW = CW strip columns (im2win) or (CW-1)*sw +
 // (S-1)*dw + 1 (im2col).
-template <typename T, bool COL>
+// VLOAD (one chunk spans every column, and every channel plane starts on a
+// 16-byte boundary): the band's rows inside the image are one contiguous run
+// of each plane, so the tile is zeroed and then filled from 16-byte loads of
+// those runs (fd_nv.d vectors cover a run from any start); otherwise element
+// loads with the zeros outside the image selected in.
+template <typename T, bool COL, bool VLOAD>
 __global__ void __launch_bounds__(256) lower_nchw_band_kernel(LowerArgs a) {
     constexpr int VEC = Vec<T>::n;
     constexpr int U = 8;
@@ -210,7 +217,48 @@ __global__ void __launch_bounds__(256) lower_nchw_band_kernel(LowerArgs a) {
     // channels c >= C1 (a second input only): plane c - C1 of image n there
     const T* x2n = a.x2 ? static_cast<const T*>(a.x2) + int64_t(n) * (a.C - a.C1) * plane : xn;
     const uint32_t stage_total = uint32_t(a.C) * a.BR * a.TW;
-    for (uint32_t base = threadIdx.x; base < stage_total; base += 256 * U) {
+    if (VLOAD) {
+        for (uint32_t i = threadIdx.x; i < stage_total; i += 256) {
+            const uint32_t row = fdiv(i, a.fd_tw);
+            const int c = int(fdiv(row, a.fd_br));
+            tile[c * a.CS + (int(row) - c * a.BR) * a.WL + int(i - row * a.fd_tw.d)] = T(0);
+        }
+        __syncthreads();
+        const int ha = max(hlo, 0), hb = min(hlo + a.BR, a.H);
+        const int fa = ha * a.W, fb = hb * a.W;   // the run of each plane, elements
+        const int va = fa / VEC;                  // its first vector
+        const uint32_t vtotal = uint32_t(a.C) * a.fd_nv.d;
+        for (uint32_t base = threadIdx.x; base < vtotal; base += 256 * 4) {
+            u32x4 val[4];
+            int f0[4], c4[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint32_t i0 = base + u * 256;
+                const uint32_t i = i0 < vtotal ? i0 : 0;
+                const int c = int(fdiv(i, a.fd_nv));
+                const int v = va + int(i - uint32_t(c) * a.fd_nv.d);
+                const bool live = i0 < vtotal && v * VEC < fb;
+                const T* plane_c = c < a.C1 ? xn + int64_t(c) * plane : x2n + int64_t(c - a.C1) * plane;
+                val[u] = load16(plane_c + (live ? v * VEC : 0));   // not live: the plane's first vector
+                f0[u] = live ? v * VEC : -1;
+                c4[u] = c;
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                if (f0[u] < 0) continue;
+                Pack16<T> pk;
+                pk.v = val[u];
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    const int f = f0[u] + e;
+                    const int h = int(fdiv(uint32_t(f), a.fd_w));
+                    const int jj = f - h * a.W + a.pw;
+                    if (f >= fa && f < fb && jj < a.TW) tile[c4[u] * a.CS + (h - hlo) * a.WL + jj] = pk.e[e];
+                }
+            }
+        }
+    }
+    for (uint32_t base = threadIdx.x; !VLOAD && base < stage_total; base += 256 * U) {
         T val[U];
         int dst[U];
 #pragma unroll

@@ -152,6 +152,11 @@ def _bits(t):
                                    # NCHW rows too wide for one staged tile: chunks of output columns
                                    (1, 64, 12, 200, 4, 3, 3, (1, 1), (1, 1), (1, 1)),
                                    (2, 40, 9, 150, 4, 4, 5, (2, 3), (1, 2), (1, 2)),
+                                   # NCHW planes on 16-byte boundaries, one chunk across: staged
+                                   # with 16-byte loads (bands of one and of several rows)
+                                   (3, 5, 12, 12, 4, 3, 3, (1, 1), (1, 1), (1, 1)),
+                                   (1100, 3, 12, 12, 4, 3, 3, (1, 1), (1, 1), (1, 1)),
+                                   (2, 16, 8, 10, 4, 2, 3, (2, 1), (3, 0), (1, 2)),
                                    # one-column tiles beyond the LDS budget: the element-wise
                                    # kernel (NCHW C*R large; NHWC C=3 rows of 3000 columns),
                                    # and NCHW column chunks with a ragged last chunk
