@@ -218,13 +218,24 @@ __global__ void __launch_bounds__(256) lower_nchw_band_kernel(LowerArgs a) {
     const T* x2n = a.x2 ? static_cast<const T*>(a.x2) + int64_t(n) * (a.C - a.C1) * plane : xn;
     const uint32_t stage_total = uint32_t(a.C) * a.BR * a.TW;
     if (VLOAD) {
-        for (uint32_t i = threadIdx.x; i < stage_total; i += 256) {
-            const uint32_t row = fdiv(i, a.fd_tw);
-            const int c = int(fdiv(row, a.fd_br));
-            tile[c * a.CS + (int(row) - c * a.BR) * a.WL + int(i - row * a.fd_tw.d)] = T(0);
-        }
-        __syncthreads();
         const int ha = max(hlo, 0), hb = min(hlo + a.BR, a.H);
+        // Zeros where the vector pass below writes nothing (so no barrier
+        // between them): every column of the tile rows outside the image --
+        // rows outside [lo, hi) -- and, in the rows inside, the columns left
+        // of the image ([0, zl)) and right of it ([zr, TW)).
+        const int lo = min(ha - hlo, a.BR), hi = max(hb - hlo, lo);
+        const int nout = a.BR - (hi - lo);
+        for (int i = threadIdx.x; i < a.C * nout * a.TW; i += 256) {
+            const int c = i / (nout * a.TW), rem = i - c * nout * a.TW;
+            const int r = rem / a.TW, jj = rem - r * a.TW;
+            tile[c * a.CS + (r < lo ? r : r - lo + hi) * a.WL + jj] = T(0);
+        }
+        const int zl = min(a.pw, a.TW), zr = min(a.pw + a.W, a.TW), zc = zl + a.TW - zr;
+        for (int i = threadIdx.x; i < a.C * (hi - lo) * zc; i += 256) {
+            const int c = i / ((hi - lo) * zc), rem = i - c * (hi - lo) * zc;
+            const int r = rem / zc, k = rem - r * zc;
+            tile[c * a.CS + (lo + r) * a.WL + (k < zl ? k : zr + k - zl)] = T(0);
+        }
         const int fa = ha * a.W, fb = hb * a.W;   // the run of each plane, elements
         const int va = fa / VEC;                  // its first vector
         const uint32_t vtotal = uint32_t(a.C) * a.fd_nv.d;
