@@ -468,11 +468,13 @@ bool band_vload(const conv_desc& d, const void* x) {
 }
 
 // NCHW band staging moves 16-byte vectors when one chunk spans every column
-// and every channel plane of x (and of the second input) starts on one.
+// and every channel plane of x (and of the second input) starts on one; its
+// offsets within a plane are 32-bit.
 bool band_vload_nchw(const conv_desc& d, const void* x, const void* x2) {
     const int64_t full = d.p.algo == CONV_ALGO_IM2WIN ? d.W_used : d.Q;
-    return d.band_items && d.p.layout == CONV_NCHW && d.band_cw == full &&
-           (int64_t(d.p.H) * d.p.W * d.elem) % 16 == 0 && reinterpret_cast<uintptr_t>(x) % 16 == 0 &&
+    const int64_t plane = int64_t(d.p.H) * d.p.W;
+    return d.band_items && d.p.layout == CONV_NCHW && d.band_cw == full && (plane * d.elem) % 16 == 0 &&
+           plane < (int64_t(1) << 31) - 64 && reinterpret_cast<uintptr_t>(x) % 16 == 0 &&
            reinterpret_cast<uintptr_t>(x2) % 16 == 0;
 }
 

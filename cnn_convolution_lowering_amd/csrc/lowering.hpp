@@ -283,7 +283,8 @@ __global__ void __launch_bounds__(256) lower_nchw_band_kernel(LowerArgs a) {
             const int h = hlo + hh, w = j0 + jj - a.pw;
             const bool in = h >= 0 && h < a.H && w >= 0 && w < a.W;
             const int hc = min(max(h, 0), a.H - 1), wc = min(max(w, 0), a.W - 1);
-            const T* src = (c < a.C1 ? xn + int64_t(c) * plane : x2n + int64_t(c - a.C1) * plane) + hc * a.W + wc;
+            const T* src =
+                (c < a.C1 ? xn + int64_t(c) * plane : x2n + int64_t(c - a.C1) * plane) + int64_t(hc) * a.W + wc;
             val[u] = *src;
             if (!in) val[u] = T(0);
             dst[u] = i0 < stage_total ? c * a.CS + hh * a.WL + jj : -1;
