@@ -501,7 +501,8 @@ LowerArgs lower_args(const conv_desc& d, const void* x, void* out) {
     a.Kl = int32_t(d.Kl);
     a.x2 = nullptr;
     a.C1 = int32_t(d.p.C);
-    auto fd = [](int64_t v) { return make_fastdiv(uint32_t(v > 1 ? v : 1)); };
+    // (divisors the chosen kernel does not use may exceed 32 bits: clamped, never zero)
+    auto fd = [](int64_t v) { return make_fastdiv(uint32_t(std::min<int64_t>(std::max<int64_t>(v, 1), INT32_MAX))); };
     const bool win = d.p.algo == CONV_ALGO_IM2WIN;
     const int64_t vpc = (win ? d.RCp : d.Kl) / d.vec;
     const int64_t full = win ? d.W_used : d.Q;
