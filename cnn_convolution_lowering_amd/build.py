@@ -12,6 +12,10 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libconvlower.so")
 SOURCES = [os.path.join(CSRC, f) for f in
            ("convlower.hip", "contract_f32.hip", "contract_f16.hip", "contract_bf16.hip")]
+# The peak microbenchmarks (include/convpeak.h): a library of their own, so
+# that nothing on the convolution path links them.
+PEAK_LIB = os.path.join(PKG, "libconvpeak.so")
+PEAK_SOURCE = os.path.join(CSRC, "peak.hip")
 
 # Packed-fp32 instructions are kept out of every kernel: hipcc forms them from
 # plain float code on its own, and they are not needed here.
@@ -34,6 +38,11 @@ def build_library(verbose: bool = False) -> str:
     tag = "%d" % os.getpid()
     compile_flags = [f for f in HIPCC_FLAGS if f != "-shared"]
     jobs = []
+    peak_tmp = PEAK_LIB + ".tmp" + tag
+    peak_cmd = [hipcc()] + HIPCC_FLAGS + ["-I", INCLUDE, PEAK_SOURCE, "-o", peak_tmp]
+    if verbose:
+        print(" ".join(peak_cmd), flush=True)
+    peak_proc = subprocess.Popen(peak_cmd)
     for src in SOURCES:
         obj = os.path.join(objdir, os.path.splitext(os.path.basename(src))[0] + "." + tag + ".o")
         cmd = [hipcc()] + compile_flags + ["-I", INCLUDE, "-c", src, "-o", obj]
@@ -41,8 +50,11 @@ def build_library(verbose: bool = False) -> str:
             print(" ".join(cmd), flush=True)
         jobs.append((subprocess.Popen(cmd), obj, cmd))
     failed = [cmd for proc, _, cmd in jobs if proc.wait() != 0]
+    if peak_proc.wait() != 0:
+        failed.append(peak_cmd)
     if failed:
         raise subprocess.CalledProcessError(1, failed[0])
+    os.replace(peak_tmp, PEAK_LIB)
     tmp = LIB + ".tmp" + tag
     cmd = [hipcc()] + HIPCC_FLAGS + [obj for _, obj, _ in jobs] + ["-o", tmp]
     if verbose:
