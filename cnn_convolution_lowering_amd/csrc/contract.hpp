@@ -62,7 +62,7 @@ void launch_gemm_tile(const conv_desc& d, const GemmArgs& g, hipStream_t st) {
 }
 
 template <typename T, int BM, int BN, int BK, int WGM, int WGN, int STAGES, bool WIDE, bool NHWC_OUT, class ASrc,
-          class BSrc, int EPI = 0>
+          class BSrc, int EPI = 0, bool EARLY = false>
 void launch_dma_core(const conv_desc& d, GemmArgs g, hipStream_t st) {
     g.tiles_n = int32_t((d.p.K + BN - 1) / BN);
     const uint64_t tiles_m = (uint64_t(d.M) + BM - 1) / BM;
@@ -71,7 +71,7 @@ void launch_dma_core(const conv_desc& d, GemmArgs g, hipStream_t st) {
     if constexpr (WIDE)
         conv_gemm_wide_kernel<T, BM, BN, BK, WGM, WGN, STAGES, ASrc, BSrc><<<blocks, NT, 0, st>>>(g);
     else
-        conv_gemm_dma_kernel<T, BM, BN, BK, WGM, WGN, STAGES, NHWC_OUT, ASrc, BSrc, EPI><<<blocks, NT, 0, st>>>(g);
+        conv_gemm_dma_kernel<T, BM, BN, BK, WGM, WGN, STAGES, NHWC_OUT, ASrc, BSrc, EPI, EARLY><<<blocks, NT, 0, st>>>(g);
 }
 
 template <typename T, int BM, int BN, int WGM, int WGN, int STRIP, int BST>
@@ -85,7 +85,7 @@ void launch_strip(const conv_desc& d, GemmArgs g, hipStream_t st) {
 // Pick the DMA sources for the descriptor and launch one tile shape of the
 // pipelined kernel (WIDE: the one-wave-per-SIMD schedule, implicit NHWC
 // windows with C a multiple of BK only -- checked when planning).
-template <typename T, int BM, int BN, int BK, int WGM, int WGN, int STAGES, bool WIDE>
+template <typename T, int BM, int BN, int BK, int WGM, int WGN, int STAGES, bool WIDE, bool EARLY = false>
 void launch_dma_tile(const conv_desc& d, const GemmArgs& g, hipStream_t st) {
     constexpr int NT = 64 * WGM * WGN;
     using B = DmaRows<T, BN, BK, false, false, NT>;
@@ -97,18 +97,18 @@ void launch_dma_tile(const conv_desc& d, const GemmArgs& g, hipStream_t st) {
     } else if (d.p.algo == CONV_ALGO_IMPLICIT) {
         // NHWC with C a whole number of vectors (checked when planning)
         if (d.p.C % BK == 0)
-            launch_dma_core<T, BM, BN, BK, WGM, WGN, STAGES, false, true, DmaWindowNHWCBlocked<T, BM, BK, NT>, B>(
+            launch_dma_core<T, BM, BN, BK, WGM, WGN, STAGES, false, true, DmaWindowNHWCBlocked<T, BM, BK, NT>, B, 0, EARLY>(
                 d, g, st);
         else
-            launch_dma_core<T, BM, BN, BK, WGM, WGN, STAGES, false, true, DmaWindowNHWC<T, BM, BK, NT>, B>(d, g, st);
+            launch_dma_core<T, BM, BN, BK, WGM, WGN, STAGES, false, true, DmaWindowNHWC<T, BM, BK, NT>, B, 0, EARLY>(d, g, st);
     } else if (!d.elided && d.p.algo == CONV_ALGO_IM2WIN) {
         using A = DmaRows<T, BM, BK, true, true, NT>;
-        if (nhwc) launch_dma_core<T, BM, BN, BK, WGM, WGN, STAGES, false, true, A, B>(d, g, st);
-        else launch_dma_core<T, BM, BN, BK, WGM, WGN, STAGES, false, false, A, B>(d, g, st);
+        if (nhwc) launch_dma_core<T, BM, BN, BK, WGM, WGN, STAGES, false, true, A, B, 0, EARLY>(d, g, st);
+        else launch_dma_core<T, BM, BN, BK, WGM, WGN, STAGES, false, false, A, B, 0, EARLY>(d, g, st);
     } else {
         using A = DmaRows<T, BM, BK, true, false, NT>;
-        if (nhwc) launch_dma_core<T, BM, BN, BK, WGM, WGN, STAGES, false, true, A, B>(d, g, st);
-        else launch_dma_core<T, BM, BN, BK, WGM, WGN, STAGES, false, false, A, B>(d, g, st);
+        if (nhwc) launch_dma_core<T, BM, BN, BK, WGM, WGN, STAGES, false, true, A, B, 0, EARLY>(d, g, st);
+        else launch_dma_core<T, BM, BN, BK, WGM, WGN, STAGES, false, false, A, B, 0, EARLY>(d, g, st);
     }
 }
 
@@ -224,7 +224,7 @@ void launch_gemm(const conv_desc& d, const void* x, const void* w, const void* b
 #define CONVLOWER_DMA_CASE(I)                                                                     \
     case I: {                                                                                     \
         constexpr TileVariant v = kDmaVariants[I];                                                \
-        launch_dma_tile<T, v.bm, v.bn, v.bk / DIV, v.wgm, v.wgn, v.stages, false>(d, g, st); \
+        launch_dma_tile<T, v.bm, v.bn, v.bk / DIV, v.wgm, v.wgn, v.stages, false, v.early != 0>(d, g, st); \
         break;                                                                                    \
     }
         switch (d.variant) {
@@ -236,6 +236,10 @@ void launch_gemm(const conv_desc& d, const void* x, const void* w, const void* b
             CONVLOWER_DMA_CASE(5)
             CONVLOWER_DMA_CASE(6)
             CONVLOWER_DMA_CASE(7)
+            CONVLOWER_DMA_CASE(8)
+            CONVLOWER_DMA_CASE(9)
+            CONVLOWER_DMA_CASE(10)
+            CONVLOWER_DMA_CASE(11)
             default: break;
         }
 #undef CONVLOWER_DMA_CASE

@@ -23,9 +23,12 @@ enum KernelId : int32_t {
 
 // One compiled tile shape: BM x BN output tile, BK-deep LDS stages (in 16-bit
 // elements; fp32 uses BK/2, the same bytes per row), WGM x WGN waves, STAGES
-// LDS stages (0 for the register-staged kernel).
+// LDS stages (0 for the register-staged kernel).  early (pipelined kernel):
+// the loads of tile kt+STAGES-1 are issued right after the barrier of tile
+// kt, before its MFMAs, instead of after them -- one more tile's MFMA time
+// to cover their latency.
 struct TileVariant {
-    int bm, bn, bk, wgm, wgn, stages;
+    int bm, bn, bk, wgm, wgn, stages, early;
 };
 
 constexpr TileVariant kRegVariants[] = {
@@ -34,6 +37,7 @@ constexpr TileVariant kRegVariants[] = {
 constexpr TileVariant kDmaVariants[] = {
     {128, 32, 32, 4, 1, 4}, {128, 64, 32, 2, 2, 4}, {128, 128, 32, 2, 2, 4}, {256, 128, 32, 2, 2, 3},
     {256, 128, 32, 4, 2, 4}, {256, 256, 32, 4, 2, 3}, {128, 128, 64, 2, 2, 2}, {128, 128, 64, 4, 2, 2},
+    {128, 128, 64, 4, 2, 2, 1}, {128, 128, 64, 2, 2, 2, 1}, {256, 128, 64, 4, 2, 2, 1}, {64, 128, 64, 2, 2, 2, 1},
 };
 // The ConvLSTM step's contraction: 64 packed gate rows per tile, one wave
 // across them (the cell update needs all four gates of a hidden channel).

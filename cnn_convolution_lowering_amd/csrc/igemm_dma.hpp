@@ -19,7 +19,11 @@
 //                  still be in flight) -> barrier (every wave's part of tile kt
 //                  is visible, and every wave has finished reading the stage
 //                  of tile kt-1) -> MFMAs on tile kt -> issue tile
-//                  kt+STAGES-1 into the stage of tile kt-1.
+//                  kt+STAGES-1 into the stage of tile kt-1
+// or, with EARLY, the issue of tile kt+STAGES-1 right after the barrier and
+// before the MFMAs on tile kt, which gives the loads STAGES-1 tiles' worth
+// of MFMA time instead of STAGES-2 (the number of loads in flight at each
+// wait is the same in both orders).
 //
 // LDS tiles use the same row swizzle as conv_gemm_kernel (swz_chunk).  Since a
 // DMA writes LDS in lane order, the swizzle is applied on the global side:
@@ -286,7 +290,7 @@ struct DmaRows {
 // EPI 0: bias add and store; 1: the ConvLSTM cell update (fp32 NCHW, BN = 64
 // with WGN = 1).
 template <typename T, int BM, int BN, int BK, int WGM, int WGN, int STAGES, bool NHWC_OUT, class ASrc, class BSrc,
-          int EPI = 0>
+          int EPI = 0, bool EARLY = false>
 __global__ void __launch_bounds__(64 * WGM * WGN, 8 / (WGM * WGN)) conv_gemm_dma_kernel(GemmArgs g) {
     constexpr int NT = 64 * WGM * WGN;
     constexpr int NW = WGM * WGN;
@@ -377,6 +381,12 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 8 / (WGM * WGN)) conv_gemm_dma
             wait_vmcnt<0>();
         }
         lds_barrier();
+        // EARLY: the stage of tile kt-1 is free once every wave has passed this
+        // barrier (each finished its MFMAs on tile kt-1, which waited for their
+        // LDS reads), so the loads of tile kt+STAGES-1 can go out now.
+        if constexpr (EARLY) {
+            if (kt + STAGES - 1 < nkt) issue((kt + STAGES - 1) % STAGES);
+        }
         const T* sA = smem + (kt % STAGES) * STAGE_ELEMS;
         const T* sB = sA + BM * BK;
         // All fragment reads of a step are issued ahead of its MFMAs
@@ -405,7 +415,9 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 8 / (WGM * WGN)) conv_gemm_dma
         // The next tile's loads go out after this tile's MFMAs are issued, so
         // their address arithmetic overlaps the MFMAs in flight.  Their stage
         // was last read in iteration kt-1, which every wave has left (barrier).
-        if (kt + STAGES - 1 < nkt) issue((kt + STAGES - 1) % STAGES);
+        if constexpr (!EARLY) {
+            if (kt + STAGES - 1 < nkt) issue((kt + STAGES - 1) % STAGES);
+        }
     }
 
     if constexpr (EPI == 1) {
