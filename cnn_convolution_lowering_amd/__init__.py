@@ -77,6 +77,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     vp, i64p = ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64)
     sig = {
         "conv_create_desc": [ctypes.POINTER(ConvParams), ctypes.POINTER(vp)],
+        "conv_create_desc_forced": [ctypes.POINTER(ConvParams), ctypes.c_char_p, ctypes.POINTER(vp)],
         "conv_destroy_desc": [vp],
         "conv_workspace_size": [vp, ctypes.POINTER(ctypes.c_size_t)],
         "conv_output_dims": [vp, i64p, i64p],
@@ -87,7 +88,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "conv_contract": [vp, vp, vp, vp, vp, vp, vp],
         "conv_lstm_create_desc": [ctypes.POINTER(ConvParams), ctypes.c_int64, ctypes.POINTER(vp)],
         "conv_lstm_step": [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
-        "conv_tune": [vp, vp, vp, vp, vp, vp, ctypes.c_size_t, ctypes.c_int32, vp, ctypes.POINTER(TuneResult)],
+        "conv_tune": [vp, vp, vp, vp, vp, vp, ctypes.c_size_t, ctypes.c_int32, vp, ctypes.POINTER(vp),
+                      ctypes.POINTER(TuneResult)],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -135,10 +137,14 @@ def _dtype_name(t) -> str:
 
 
 class Conv2d:
-    """One convolution descriptor (a plan); immutable once created."""
+    """One convolution descriptor (a plan); immutable once created.
+
+    ``plan`` asks for a contraction kernel explicitly ("<kernel>:<variant>"
+    or "<kernel>:<variant>:<ksplit>", conv_create_desc_forced): for tests and
+    tuning; None is the library's default choice."""
 
     def __init__(self, N, C, H, W, K, R, S, *, stride=1, padding=0, dilation=1, layout="nchw",
-                 dtype="f32", algo="im2win"):
+                 dtype="f32", algo="im2win", plan: Optional[str] = None, _handle=None):
         self.lib = load_library()
         sh, sw = _pair(stride)
         ph, pw = _pair(padding)
@@ -149,8 +155,17 @@ class Conv2d:
                                  LAYOUTS[layout], DTYPES[dtype], ALGOS[algo])
         self.layout, self.dtype, self.algo = layout, dtype, algo
         self.stride, self.padding, self.dilation = (sh, sw), (ph, pw), (dh, dw)
-        self._desc = ctypes.c_void_p()
-        _check(self.lib.conv_create_desc(ctypes.byref(self.params), ctypes.byref(self._desc)), "conv_create_desc")
+        self.plan = plan
+        if _handle is not None:
+            self._desc = _handle          # a descriptor conv_tune made for this object
+        else:
+            self._desc = ctypes.c_void_p()
+            if plan is None:
+                _check(self.lib.conv_create_desc(ctypes.byref(self.params), ctypes.byref(self._desc)),
+                       "conv_create_desc")
+            else:
+                _check(self.lib.conv_create_desc_forced(ctypes.byref(self.params), plan.encode(),
+                                                        ctypes.byref(self._desc)), "conv_create_desc_forced")
         info = PlanInfo()
         _check(self.lib.conv_plan_info(self._desc, ctypes.byref(info)), "conv_plan_info")
         self.info: Dict[str, int] = {name: getattr(info, name) for name, _ in PlanInfo._fields_}
@@ -235,8 +250,9 @@ class Conv2d:
 
     def tune(self, x, w, bias=None, y=None, ws=None, reps=5, stream=None):
         """conv_tune: time every kernel / tile variant that takes this
-        convolution (within the workspace given) and keep the fastest.
-        Returns the result as a dict; refreshes ``info``."""
+        convolution (within the workspace given) and return (result dict, a
+        new Conv2d holding the fastest plan).  This object is not changed, so
+        a descriptor shared through ``descriptor()`` keeps its plan."""
         self._tensor(x, self.x_shape(), "x")
         self._tensor(w, self.w_shape(), "w")
         self._tensor(bias, (self.params.K,), "bias")
@@ -244,14 +260,15 @@ class Conv2d:
         ws = self._ws(ws, x.device)
         ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
         res = TuneResult()
+        handle = ctypes.c_void_p()
         _check(self.lib.conv_tune(self._desc, self._ptr(x), self._ptr(w), self._ptr(bias), self._ptr(y),
                                   self._ptr(ws), ws_bytes, int(reps), self._stream(stream, x.device),
-                                  ctypes.byref(res)), "conv_tune")
-        info = PlanInfo()
-        _check(self.lib.conv_plan_info(self._desc, ctypes.byref(info)), "conv_plan_info")
-        self.info = {name: getattr(info, name) for name, _ in PlanInfo._fields_}
-        self.workspace_bytes = int(self.info["ws_bytes"])
-        return {name: getattr(res, name) for name, _ in TuneResult._fields_}
+                                  ctypes.byref(handle), ctypes.byref(res)), "conv_tune")
+        p = self.params
+        tuned = Conv2d(p.N, p.C, p.H, p.W, p.K, p.R, p.S, stride=self.stride, padding=self.padding,
+                       dilation=self.dilation, layout=self.layout, dtype=self.dtype, algo=self.algo,
+                       _handle=handle)
+        return {name: getattr(res, name) for name, _ in TuneResult._fields_}, tuned
 
     def pack_filter(self, w, ws, stream=None):
         self._tensor(w, self.w_shape(), "w")
@@ -338,8 +355,9 @@ _cache: Dict[tuple, Conv2d] = {}
 
 
 def descriptor(x_shape, w_shape, *, stride=1, padding=0, dilation=1, layout="nchw", dtype="f32",
-               algo="im2win") -> Conv2d:
-    """A cached descriptor for the given shapes and parameters."""
+               algo="im2win", plan: Optional[str] = None) -> Conv2d:
+    """A cached descriptor for the given shapes, parameters and plan request
+    (descriptors are immutable, so sharing one is safe)."""
     if layout == "nchw":
         N, C, H, W = x_shape
         K, C2, R, S = w_shape
@@ -350,11 +368,11 @@ def descriptor(x_shape, w_shape, *, stride=1, padding=0, dilation=1, layout="nch
         raise ValueError("layout must be 'nchw' or 'nhwc'")
     if C != C2:
         raise ValueError("x has %d channels, w has %d" % (C, C2))
-    key = (N, C, H, W, K, R, S, _pair(stride), _pair(padding), _pair(dilation), layout, dtype, algo)
+    key = (N, C, H, W, K, R, S, _pair(stride), _pair(padding), _pair(dilation), layout, dtype, algo, plan)
     d = _cache.get(key)
     if d is None:
         d = Conv2d(N, C, H, W, K, R, S, stride=stride, padding=padding, dilation=dilation, layout=layout,
-                   dtype=dtype, algo=algo)
+                   dtype=dtype, algo=algo, plan=plan)
         _cache[key] = d
     return d
 

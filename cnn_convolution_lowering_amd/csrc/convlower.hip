@@ -41,8 +41,8 @@ conv_status_t from_hip(hipError_t e) { return e == hipSuccess ? CONV_OK : CONV_E
 
 // ---------------------------------------------------------------- planning
 
-// force: "<kernel>:<variant>" (the tuning override), or nullptr for the
-// default choice.
+// force: "<kernel>:<variant>[:<ksplit>]" (conv_create_desc_forced, conv_tune),
+// or nullptr for the default choice.
 conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force) {
     if (p.N < 0 || p.C <= 0 || p.H <= 0 || p.W <= 0 || p.K <= 0 || p.R <= 0 || p.S <= 0) return CONV_ERR_INVALID_ARG;
     if (p.stride_h <= 0 || p.stride_w <= 0 || p.dil_h <= 0 || p.dil_w <= 0 || p.pad_h < 0 || p.pad_w < 0)
@@ -193,22 +193,23 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force) {
             }
         }
     } else if (dma_ok) {
-        // BN covers the output channels up to 128; BM = 256 where that still
-        // gives two workgroups per CU, else 128 -- for 16-bit operands with
-        // 64-deep stages (two of them), which a sweep over the 3x3 and 1x1
-        // layers put ahead of four 32-deep ones, and eight waves: with fewer
-        // tiles than two per CU, two waves per SIMD on one tile beat one
-        // (4-12 % on the 3x3 and 1x1 layers of a few hundred tiles).
+        // BN covers the output channels up to 128.  fp32: BM = 256 where that
+        // still gives two workgroups per CU, else 128.  16-bit: 128 x 128
+        // tiles over eight waves with two 64-deep stages, the next tile's
+        // loads issued before the MFMAs of the current one -- ahead of the
+        // same tile issuing after them (5-15 %), of three and four stages
+        // (their LDS leaves room for one workgroup per CU instead of two)
+        // and of 256 x 128 tiles, on the 3x3, 1x1 and kernel-size layers.
         d.kernel = KERN_DMA;
-        d.variant = p.K <= 32 ? 0 : (p.K <= 64 ? 1 : (p.dtype == CONV_F32 ? 2 : 7));
-        if (d.variant >= 2 && (d.M / 256) * ((p.K + 127) / 128) >= 512) d.variant = 3;
-        // Taps sharing an input row (S >= 5), enough 512 x 128 tiles to give
-        // most CUs one, and output channels filling whole 128-wide tiles:
-        // the register-streamed strip kernel (a sweep over the kernel-size
-        // layers put it level with the 256 x 128 pipelined tiles at 5 x 5 and
-        // ahead from 7 x 7 up; at 3 x 3 the pipelined tiles are faster).
+        d.variant = p.K <= 32 ? 0 : (p.K <= 64 ? 1 : (p.dtype == CONV_F32 ? 2 : 8));
+        if (d.variant == 2 && (d.M / 256) * ((p.K + 127) / 128) >= 512) d.variant = 3;
+        // Long filter rows (S >= 9), enough 512 x 128 tiles to give most CUs
+        // one, and output channels filling whole 128-wide tiles: the
+        // register-streamed strip kernel (measured on the kernel-size layers:
+        // ahead of the pipelined tiles at 11 x 11, level at 7 x 7, behind at
+        // 5 x 5 and 3 x 3).
         const StripVariant& rb = kStripRbVariants[5];
-        if (p.S >= 5 && p.K % 128 == 0 && (d.M / rb.bm) * (p.K / rb.bn) >= 192 && strip_fits(rb)) {
+        if (p.S >= 9 && p.K % 128 == 0 && (d.M / rb.bm) * (p.K / rb.bn) >= 192 && strip_fits(rb)) {
             d.kernel = KERN_STRIP_RB;
             d.variant = 5;
         }
@@ -711,18 +712,22 @@ conv_status_t run_lstm(const conv_desc& d, const void* x, const void* h_prev, co
 
 extern "C" {
 
-conv_status_t conv_create_desc(const conv_params_t* p, conv_desc_t* out) {
+conv_status_t conv_create_desc_forced(const conv_params_t* p, const char* force, conv_desc_t* out) {
     if (!p || !out) return CONV_ERR_NULL_PTR;
     *out = nullptr;
     conv_desc tmp{};
     tmp.p = *p;
-    conv_status_t s = plan(*p, tmp, std::getenv("CONVLOWER_KERNEL"));
+    conv_status_t s = plan(*p, tmp, force);
     if (s != CONV_OK) return s;
     conv_desc* d = new (std::nothrow) conv_desc(tmp);
     if (!d) return CONV_ERR_OOM;
     d->magic = kDescMagic;
     *out = d;
     return CONV_OK;
+}
+
+conv_status_t conv_create_desc(const conv_params_t* p, conv_desc_t* out) {
+    return conv_create_desc_forced(p, nullptr, out);
 }
 
 conv_status_t conv_lstm_create_desc(const conv_params_t* p, int64_t c_x, conv_desc_t* out) {
@@ -857,14 +862,24 @@ conv_status_t conv2d_fwd(conv_desc_t d, const void* x, const void* w, const void
 }
 
 conv_status_t conv_tune(conv_desc_t d, const void* x, const void* w, const void* bias, void* y, void* ws,
-                        size_t ws_bytes, int32_t reps, void* stream, conv_tune_result_t* result) {
+                        size_t ws_bytes, int32_t reps, void* stream, conv_desc_t* tuned,
+                        conv_tune_result_t* result) {
+    if (!tuned || !result) return CONV_ERR_NULL_PTR;
+    *tuned = nullptr;
     if (!desc_ok(d) || d->lstm_cx || reps < 1) return CONV_ERR_INVALID_ARG;
-    if (!result) return CONV_ERR_NULL_PTR;
     *result = conv_tune_result_t{};
     result->kernel = d->kernel;
     result->kernel_variant = d->variant;
     result->ksplit = d->ksplit;
-    if (d->p.N == 0) return CONV_OK;
+    // the kept plan goes into a new descriptor; d stays as it is
+    auto emit = [&](const conv_desc& c) -> conv_status_t {
+        conv_desc* nd = new (std::nothrow) conv_desc(c);
+        if (!nd) return CONV_ERR_OOM;
+        nd->magic = kDescMagic;
+        *tuned = nd;
+        return CONV_OK;
+    };
+    if (d->p.N == 0) return emit(*d);
     const hipStream_t st = static_cast<hipStream_t>(stream);
     conv_status_t s;
     if ((s = check_dev(x, 16)) != CONV_OK) return s;
@@ -932,13 +947,11 @@ conv_status_t conv_tune(conv_desc_t d, const void* x, const void* w, const void*
     (void)hipEventDestroy(e0);
     (void)hipEventDestroy(e1);
     if (s != CONV_OK) return s;
-    const uint32_t magic = d->magic;
-    *d = best;
-    d->magic = magic;
+    if ((s = emit(best)) != CONV_OK) return s;
     result->candidates = n;
-    result->kernel = d->kernel;
-    result->kernel_variant = d->variant;
-    result->ksplit = d->ksplit;
+    result->kernel = best.kernel;
+    result->kernel_variant = best.variant;
+    result->ksplit = best.ksplit;
     result->best_ms = best_ms;
     return CONV_OK;
 }

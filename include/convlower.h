@@ -27,15 +27,20 @@
  *    and ws must be 16-byte aligned; bias must be aligned to its element.
  *    y must not overlap x, w, bias or ws.
  *  - The library never allocates device memory, never copies between host
- *    and device and never synchronises.  Work is enqueued on `stream` (a
- *    hipStream_t; NULL = the default stream) and runs asynchronously; errors
- *    found on the host are returned before anything is enqueued, launch
- *    failures come back as CONV_ERR_HIP, and faults inside a kernel surface
- *    at the caller's next synchronisation.
+ *    and device and never synchronises -- with one exception, conv_tune,
+ *    which times candidate plans and therefore waits for its own timing
+ *    events.  Work is enqueued on `stream` (a hipStream_t; NULL = the
+ *    default stream) and runs asynchronously; errors found on the host are
+ *    returned before anything is enqueued, launch failures come back as
+ *    CONV_ERR_HIP, and faults inside a kernel surface at the caller's next
+ *    synchronisation.
  *  - There is no fallback: a case the kernels do not cover returns
  *    CONV_ERR_UNSUPPORTED and nothing runs.
- *  - A descriptor is immutable after creation; one descriptor may be used
- *    from several threads and streams at once if each call has its own ws.
+ *  - A descriptor is immutable after creation (conv_tune returns a new one);
+ *    one descriptor may be used from several threads and streams at once if
+ *    each call has its own ws.
+ *  - No entry point reads the process environment: a plan other than the
+ *    default is only ever asked for explicitly (conv_create_desc_forced).
  */
 #ifndef CONVLOWER_H
 #define CONVLOWER_H
@@ -133,30 +138,74 @@ typedef struct {
     int32_t ksplit;
 } conv_plan_info_t;
 
-/* Validate *p and build a descriptor.  Host only: no HIP call is made, so it
- * works without a GPU.  Errors: CONV_ERR_NULL_PTR (p or out NULL),
- * CONV_ERR_INVALID_ARG (N < 0, C/H/W/K/R/S <= 0, stride or dilation <= 0,
- * padding < 0, bad enum, or a kernel that does not fit the padded input, i.e.
- * P or Q <= 0), CONV_ERR_UNSUPPORTED (sizes beyond the 32-bit index ranges the
- * kernels use), CONV_ERR_OOM.  On success *out owns a descriptor the caller
- * must release with conv_destroy_desc. */
+/* Validate *p and build a descriptor.  "GPU-Accelerating MSCRED ...",
+ * section "Integrating the CUDA Implementation with PyTorch" (the extension
+ * checks tensor dimensions, data types, device placement and contiguity, and
+ * handles errors) and section "Transforming Conv2D into im2col and GEMM" (the
+ * sizes of the lowered matrix and of the output feature map follow from the
+ * convolution's parameters): all of that is decided here, once, on the host.
+ * Host only: no HIP call is made, so it works without a GPU.  Errors:
+ * CONV_ERR_NULL_PTR (p or out NULL), CONV_ERR_INVALID_ARG (N < 0,
+ * C/H/W/K/R/S <= 0, stride or dilation <= 0, padding < 0, bad enum, or a
+ * kernel that does not fit the padded input, i.e. P or Q <= 0),
+ * CONV_ERR_UNSUPPORTED (sizes beyond the 32-bit index ranges the kernels
+ * use), CONV_ERR_OOM.  On success *out owns a descriptor the caller must
+ * release with conv_destroy_desc. */
 conv_status_t conv_create_desc(const conv_params_t* p, conv_desc_t* out);
 
-/* Release a descriptor (NULL is accepted and ignored). */
+/* As conv_create_desc, with the contraction kernel named explicitly: plan is
+ * "<kernel>:<variant>" or "<kernel>:<variant>:<ksplit>" with kernel one of
+ * reg, dma, wide, nchw, strip, striprb, nchwstrip, nchwtile, tile16 (the
+ * numbering of conv_plan_info_t.kernel, in that order) and variant an index
+ * into that kernel's compiled tile shapes; ksplit (1-8) splits the
+ * contraction of the dma and wide kernels.  "GPU-Accelerating MSCRED ...",
+ * section "Engineering Challenges" (kernel configuration: thread-block
+ * dimensions and tile sizes change occupancy, memory access and work
+ * distribution, so they are measured, not assumed).  For tests and tuning: a
+ * plan that does not take this convolution, or a malformed string, leaves
+ * the default plan (conv_plan_info says which was kept).  plan == NULL is
+ * conv_create_desc.  Host only; errors as conv_create_desc. */
+conv_status_t conv_create_desc_forced(const conv_params_t* p, const char* plan, conv_desc_t* out);
+
+/* Release a descriptor (NULL is accepted and ignored; a pointer that is not a
+ * live descriptor returns CONV_ERR_INVALID_ARG).  "GPU-Accelerating MSCRED
+ * ...", section "Engineering Challenges" (memory management: what is
+ * allocated is released).  Host only. */
 conv_status_t conv_destroy_desc(conv_desc_t d);
 
 /* Bytes of device workspace conv2d_fwd needs for this descriptor (may be 0).
- * Host only. */
+ * "GPU-Accelerating MSCRED ...", section "Engineering Challenges" (the
+ * im2col transformation creates intermediate data whose allocation, reuse and
+ * release must be managed): the caller allocates this many bytes, may reuse
+ * them for any call with a descriptor that needs no more, and frees them;
+ * the library never allocates.  The figure is what the plan lowers (im2win
+ * strips: "Enabling Memory-efficient Im2win Convolution ...", abstract; or
+ * explicit im2col rows) plus any packed filter or split-contraction partial
+ * sums.  Host only. */
 conv_status_t conv_workspace_size(conv_desc_t d, size_t* bytes);
 
-/* Output extents P, Q (floor formula above).  Host only. */
+/* Output extents P, Q (floor formula above; "GPU-Accelerating MSCRED ...",
+ * section "Transforming Conv2D into im2col and GEMM": the product is
+ * reshaped into the output feature map).  Host only. */
 conv_status_t conv_output_dims(conv_desc_t d, int64_t* P, int64_t* Q);
 
-/* The descriptor's plan (see conv_plan_info_t).  Host only. */
+/* The descriptor's plan (see conv_plan_info_t): "GPU-Accelerating MSCRED
+ * ...", section "Engineering Challenges" (measuring the correct bottleneck:
+ * the choice a measurement is about must be visible).  Host only. */
 conv_status_t conv_plan_info(conv_desc_t d, conv_plan_info_t* info);
 
 /* The whole forward convolution: conv_pack_filter, conv_lower_input and
- * conv_contract enqueued in that order on `stream`.
+ * conv_contract enqueued in that order on `stream`.  "GPU-Accelerating MSCRED
+ * ...", section "Transforming Conv2D into im2col and GEMM" (overlapping input
+ * windows become the columns of a matrix that the reshaped filter matrix
+ * multiplies; the result is reshaped into the output feature map) and
+ * section "Global Memory and Shared Memory" (reusable tiles staged in on-chip
+ * memory); "Enabling Memory-efficient Im2win Convolution ...", abstract (the
+ * window layout, asynchronous data movement, fp32 and half-precision
+ * arithmetic).  Errors (all found before anything is enqueued):
+ * CONV_ERR_INVALID_ARG (not a live descriptor, or a ConvLSTM one),
+ * CONV_ERR_NULL_PTR, CONV_ERR_NOT_DEVICE_PTR, CONV_ERR_MISALIGNED; a launch
+ * failure returns CONV_ERR_HIP.
  *   x     input, N*C*H*W elements in the descriptor's layout
  *   w     filter, K*C*R*S elements (KCRS or KRSC)
  *   bias  K elements, or NULL for no bias
@@ -168,18 +217,28 @@ conv_status_t conv2d_fwd(conv_desc_t d, const void* x, const void* w, const void
                          void* ws, void* stream);
 
 /* Stage 1 of conv2d_fwd: reorder w into the packed contraction operand
- * Bp[k][s*RCp + r*C + c] in ws (zeros in the RCp padding).  A no-op for
- * CONV_ALGO_IMPLICIT and when the filter is already in that order (NHWC with
- * R == 1 or S == 1 and C a multiple of the 16-byte vector). */
+ * Bp[k][s*RCp + r*C + c] in ws (zeros in the RCp padding) -- the "reshaped
+ * filter matrix" of "GPU-Accelerating MSCRED ...", section "Transforming
+ * Conv2D into im2col and GEMM" -- or, for the register-streamed and
+ * small-window kernels, into the order their MFMAs consume it.  A no-op when
+ * the plan reads w in place (the fused path's pipelined kernels, and NHWC
+ * with R == 1 or S == 1 and C a multiple of the 16-byte vector).  Pointer
+ * rules and errors as conv2d_fwd. */
 conv_status_t conv_pack_filter(conv_desc_t d, const void* w, void* ws, void* stream);
 
-/* Stage 2: lower x into ws -- im2win strips or im2col rows, per the
- * descriptor's algorithm.  A no-op when the lowering is elided and for
- * CONV_ALGO_IMPLICIT. */
+/* Stage 2: lower x into ws -- im2win strips ("Enabling Memory-efficient
+ * Im2win Convolution ...", abstract) or im2col rows ("GPU-Accelerating MSCRED
+ * ...", section "Transforming Conv2D into im2col and GEMM": overlapping
+ * windows copied into an intermediate matrix), per the descriptor's
+ * algorithm.  A no-op when the lowering is elided and for
+ * CONV_ALGO_IMPLICIT.  Pointer rules and errors as conv2d_fwd. */
 conv_status_t conv_lower_input(conv_desc_t d, const void* x, void* ws, void* stream);
 
 /* Stage 3: the MFMA contraction over the lowered operand and packed filter
- * with the fused epilogue y = round(acc + bias[k]).  Reads ws written by
+ * with the fused epilogue y = round(acc + bias[k]) ("GPU-Accelerating MSCRED
+ * ...", sections "Transforming Conv2D into im2col and GEMM" -- the matrix
+ * product and the reshape into the output map -- and "Global Memory and
+ * Shared Memory" -- tiles reused from on-chip memory).  Reads ws written by
  * stages 1 and 2; reads x in place when the lowering is elided and w in place
  * when the pack is a no-op.  When the plan splits the contraction
  * (conv_plan_info_t.ksplit > 1) it also writes the fp32 partial sums into
@@ -242,19 +301,25 @@ typedef struct {
     int32_t ksplit;           /* its split contraction (conv_plan_info_t.ksplit) */
 } conv_tune_result_t;
 
-/* Tune d (not a ConvLSTM descriptor) with reps timed calls per candidate, on
- * `stream`, with the same pointer rules as conv2d_fwd; ws_bytes is the size
- * of ws (at least conv_workspace_size(d)).  Blocks the calling thread until
- * the timings are in.  On return y holds the output of the last candidate
- * run, d may need a different (never larger than ws_bytes) workspace --
- * query conv_workspace_size again -- and *result says what was kept.  d must
- * not be used by any other call while it is tuned; afterwards it is
- * immutable again.  Errors as conv2d_fwd, CONV_ERR_INVALID_ARG for reps < 1
- * or ws_bytes below the current workspace size. */
+/* Tune the plan of d (not a ConvLSTM descriptor) with reps timed calls per
+ * candidate, on `stream`, with the same pointer rules as conv2d_fwd; ws_bytes
+ * is the size of ws (at least conv_workspace_size(d)); only candidates whose
+ * workspace fits ws_bytes are timed.  The one entry point that synchronises:
+ * it blocks the calling thread until its timing events are in.  d itself is
+ * not changed (other users of it are unaffected); the plan kept is returned
+ * in *tuned, a new descriptor the caller releases with conv_destroy_desc --
+ * query its conv_workspace_size, which is never above ws_bytes.  On return y
+ * holds the output of the last candidate run and *result says what was kept.
+ * Errors as conv2d_fwd, CONV_ERR_NULL_PTR for a NULL tuned or result,
+ * CONV_ERR_INVALID_ARG for reps < 1 or ws_bytes below the current workspace
+ * size, CONV_ERR_OOM; on an error *tuned is NULL. */
 conv_status_t conv_tune(conv_desc_t d, const void* x, const void* w, const void* bias, void* y, void* ws,
-                        size_t ws_bytes, int32_t reps, void* stream, conv_tune_result_t* result);
+                        size_t ws_bytes, int32_t reps, void* stream, conv_desc_t* tuned,
+                        conv_tune_result_t* result);
 
-/* Static English text for a status code. */
+/* Static English text for a status code ("GPU-Accelerating MSCRED ...",
+ * section "Integrating the CUDA Implementation with PyTorch": error handling
+ * at the boundary).  Never NULL; "unknown status" for other values. */
 const char* conv_status_string(conv_status_t s);
 
 #ifdef __cplusplus

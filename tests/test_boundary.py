@@ -247,30 +247,34 @@ def test_elided_layers_use_no_lowering_workspace():
 
 
 def test_kernel_override_is_host_only_and_checked(monkeypatch):
-    """CONVLOWER_KERNEL forces a compiled kernel variant only where that kernel
-    takes the shape; otherwise (or when malformed) the planner's choice stays."""
-    def plan(**kw):
+    """conv_create_desc_forced takes a compiled kernel variant only where that
+    kernel takes the shape; otherwise (or when malformed) the planner's choice
+    stays.  conv_create_desc never reads the environment."""
+    def plan(force=None, **kw):
         args = dict(N=2, C=64, H=17, W=17, K=72, R=3, S=3, padding=1, layout="nhwc", dtype="f16", algo="implicit")
         args.update(kw)
         N, C, H, W, K, R, S = (args.pop(k) for k in ("N", "C", "H", "W", "K", "R", "S"))
-        d = cl.Conv2d(N, C, H, W, K, R, S, **args)
+        d = cl.Conv2d(N, C, H, W, K, R, S, plan=force, **args)
         return d.info["kernel"], d.info["kernel_variant"], d.info["tile_m"], d.info["tile_n"]
 
-    monkeypatch.delenv("CONVLOWER_KERNEL", raising=False)
     default = plan()
-    monkeypatch.setenv("CONVLOWER_KERNEL", "strip:0")
-    assert plan()[:3] == (4, 0, 512)
-    assert plan(R=1, S=1, padding=0)[0] != 4       # a single tap: nothing to share
-    assert plan(C=48)[0] != 4                       # C not a multiple of 32
-    assert plan(dtype="f32")[0] != 4                # 16-bit only
-    monkeypatch.setenv("CONVLOWER_KERNEL", "wide:2")
-    assert plan()[:4] == (2, 2, 256, 256)
-    monkeypatch.setenv("CONVLOWER_KERNEL", "nchw:1")
-    assert plan()[0] != 3                           # fp32 NCHW only
-    assert plan(layout="nchw", dtype="f32")[:2] == (3, 1)
-    for bad in ("strip", "strip:99", "bogus:1", ":", "dma:-1"):
-        monkeypatch.setenv("CONVLOWER_KERNEL", bad)
-        assert plan() == default
+    monkeypatch.setenv("CONVLOWER_KERNEL", "strip:0")      # the old override: ignored
+    assert plan() == default
+    monkeypatch.delenv("CONVLOWER_KERNEL")
+    assert plan("strip:0")[:3] == (4, 0, 512)
+    assert plan("strip:0", R=1, S=1, padding=0)[0] != 4       # a single tap: nothing to share
+    assert plan("strip:0", C=48)[0] != 4                       # C not a multiple of 32
+    assert plan("strip:0", dtype="f32")[0] != 4                # 16-bit only
+    assert plan("wide:2")[:4] == (2, 2, 256, 256)
+    assert plan("nchw:1")[0] != 3                              # fp32 NCHW only
+    assert plan("nchw:1", layout="nchw", dtype="f32")[:2] == (3, 1)
+    for bad in ("strip", "strip:99", "bogus:1", ":", "dma:-1", ""):
+        assert plan(bad) == default
+    # the cache of shared descriptors keeps forced and default plans apart
+    a = cl.descriptor((2, 17, 17, 64), (72, 3, 3, 64), padding=1, layout="nhwc", dtype="f16", algo="implicit")
+    b = cl.descriptor((2, 17, 17, 64), (72, 3, 3, 64), padding=1, layout="nhwc", dtype="f16", algo="implicit",
+                      plan="wide:2")
+    assert a is not b and a.info["kernel"] == default[0] and b.info["kernel"] == 2
 
 
 def test_lstm_descriptor_validation_and_entry_separation():
@@ -304,23 +308,32 @@ def test_tune_argument_checks_on_the_host():
     d = cl.Conv2d(2, 16, 8, 8, 16, 3, 3, padding=1, layout="nchw", dtype="f32")
     res = cl.TuneResult()
     fake = ctypes.c_void_p(1 << 20)
-    assert lib.conv_tune(d.handle, fake, fake, None, fake, fake, 1 << 30, 0, None, ctypes.byref(res)) == -1
-    assert lib.conv_tune(d.handle, fake, fake, None, fake, fake, 1 << 30, 3, None, None) == -3
+    out = ctypes.c_void_p(123)
+    assert lib.conv_tune(d.handle, fake, fake, None, fake, fake, 1 << 30, 0, None, ctypes.byref(out),
+                         ctypes.byref(res)) == -1
+    assert not out.value                                     # cleared on every error
+    assert lib.conv_tune(d.handle, fake, fake, None, fake, fake, 1 << 30, 3, None, ctypes.byref(out), None) == -3
+    assert lib.conv_tune(d.handle, fake, fake, None, fake, fake, 1 << 30, 3, None, None, ctypes.byref(res)) == -3
     cell = cl.ConvLSTMCell(2, 16, 16, 8, 8, 3, 3, padding=1)
-    assert lib.conv_tune(cell.handle if hasattr(cell, "handle") else cell._desc, fake, fake, None, fake, fake,
-                         1 << 30, 3, None, ctypes.byref(res)) == -1
+    assert lib.conv_tune(cell._desc, fake, fake, None, fake, fake, 1 << 30, 3, None, ctypes.byref(out),
+                         ctypes.byref(res)) == -1
     empty = cl.Conv2d(0, 16, 8, 8, 16, 3, 3, padding=1, layout="nchw", dtype="f32")
-    assert lib.conv_tune(empty.handle, None, None, None, None, None, 0, 3, None, ctypes.byref(res)) == 0
+    assert lib.conv_tune(empty.handle, None, None, None, None, None, 0, 3, None, ctypes.byref(out),
+                         ctypes.byref(res)) == 0
+    assert out.value and out.value != empty.handle.value     # a new descriptor, same plan
+    info = cl.PlanInfo()
+    assert lib.conv_plan_info(out, ctypes.byref(info)) == 0
     assert (res.kernel, res.kernel_variant) == (empty.info["kernel"], empty.info["kernel_variant"])
+    assert (info.kernel, info.kernel_variant) == (res.kernel, res.kernel_variant)
     assert res.ksplit == empty.info["ksplit"] == 1
+    assert lib.conv_destroy_desc(out) == 0
 
-def test_split_contraction_plan(monkeypatch):
+def test_split_contraction_plan():
     """The pipelined kernel splits the contraction in two when the output
     tiles leave most CUs idle or the contraction is very long; the fp32
     partials take ksplit*M*K*4 bytes after the other workspace parts,
     256-byte aligned, and a forced split is honoured (within the contraction
     tiles, every split non-empty)."""
-    monkeypatch.delenv("CONVLOWER_KERNEL", raising=False)
     for a in [(128, 512, 7, 7, 512, 3, 3, 1), (8, 192, 20, 20, 96, 3, 3, 1)]:   # 4608-long; 25 tiles
         c = cl.Conv2d(*a[:7], padding=a[7], layout="nhwc", dtype="bf16", algo="implicit")
         i = c.info
@@ -342,13 +355,40 @@ def test_split_contraction_plan(monkeypatch):
     if i["ksplit"] > 1:
         assert i["ws_partial_offset"] >= i["ws_lowered_offset"] + i["ws_lowered_bytes"]
     # forced: honoured, clamped to the contraction tiles
-    monkeypatch.setenv("CONVLOWER_KERNEL", "dma:1:3")
-    c = cl.Conv2d(2, 64, 17, 17, 72, 3, 3, padding=1, layout="nhwc", dtype="f16", algo="implicit")
+    c = cl.Conv2d(2, 64, 17, 17, 72, 3, 3, padding=1, layout="nhwc", dtype="f16", algo="implicit", plan="dma:1:3")
     assert c.info["ksplit"] == 3 and c.info["ws_partial_bytes"] == 3 * c.info["M"] * 72 * 4
-    monkeypatch.setenv("CONVLOWER_KERNEL", "dma:1:8")
-    c = cl.Conv2d(2, 16, 9, 9, 24, 1, 1, layout="nhwc", dtype="f16", algo="implicit")   # one contraction tile
+    c = cl.Conv2d(2, 16, 9, 9, 24, 1, 1, layout="nhwc", dtype="f16", algo="implicit", plan="dma:1:8")  # one tile
     assert c.info["ksplit"] == 1 and c.info["ws_partial_bytes"] == 0
     # the ConvLSTM step never splits
-    monkeypatch.delenv("CONVLOWER_KERNEL", raising=False)
     cell = cl.ConvLSTMCell(4, 32, 32, 30, 30, 3, 3, padding=1, algo="im2win")
     assert cell.info["ksplit"] == 1 and cell.info["ws_partial_bytes"] == 0
+
+
+def test_peak_library_exports_and_host_checks():
+    """libconvpeak.so (the measured-peak microbenchmarks) exports what
+    include/convpeak.h declares; its argument checks run on the host."""
+    import re
+    from cnn_convolution_lowering_amd import peak
+    if not os.path.exists(peak.PEAK_LIB_PATH):
+        pytest.skip("libconvpeak.so not built")
+    lib = peak.load_peak_library()
+    with open(peak.PEAK_HEADER_PATH) as f:
+        text = re.sub(r"/\*.*?\*/", " ", f.read(), flags=re.S)
+    names = set(re.findall(r"^\s*(?:const\s+)?[a-z0-9_]+\**\s+\**\s*(convpeak\w*)\s*\(", text, flags=re.M))
+    assert names == {"convpeak_mfma_flops_per_iter", "convpeak_mfma", "convpeak_wall_clock_khz", "convpeak_copy"}
+    for n in names:
+        assert hasattr(lib, n), n
+    # flops per loop iteration: the instruction's M*N*K*2 times the accumulators per iteration
+    assert lib.convpeak_mfma_flops_per_iter(0) == 2 * 16 * 16 * 4 * 8
+    assert lib.convpeak_mfma_flops_per_iter(1) == lib.convpeak_mfma_flops_per_iter(2) == 2 * 32 * 32 * 16 * 4
+    assert lib.convpeak_mfma_flops_per_iter(3) == lib.convpeak_mfma_flops_per_iter(4) == 2 * 16 * 16 * 32 * 8
+    assert lib.convpeak_mfma_flops_per_iter(5) == 0
+    fake = ctypes.c_void_p(1 << 20)
+    assert lib.convpeak_mfma(1, 0, 4, fake, None) == -1          # iters < 1
+    assert lib.convpeak_mfma(1, 10, 0, fake, None) == -1         # no blocks
+    assert lib.convpeak_mfma(9, 10, 4, fake, None) == -1         # unknown instruction
+    assert lib.convpeak_mfma(1, 10, 4, None, None) == -1         # no clock buffer
+    assert lib.convpeak_copy(fake, ctypes.c_void_p((1 << 20) + 4096), 24, None) == -1   # not a multiple of 16
+    assert lib.convpeak_copy(ctypes.c_void_p((1 << 20) + 8), fake, 32, None) == -1      # misaligned
+    assert lib.convpeak_copy(fake, ctypes.c_void_p((1 << 20) + 16), 64, None) == -1    # overlapping
+    assert lib.convpeak_copy(fake, ctypes.c_void_p(1 << 24), 0, None) == 0             # nothing to copy

@@ -1,7 +1,8 @@
 """GPU parity of every compiled contraction kernel and tile variant.
 
-The planner picks one kernel per shape; CONVLOWER_KERNEL="<kernel>:<variant>"
-forces another one that takes the shape.  Each variant runs here on shapes
+The planner picks one kernel per shape; conv_create_desc_forced with
+"<kernel>:<variant>" (the binding's plan=) asks for another one that takes
+the shape.  Each variant runs here on shapes
 with ragged pixel and channel tiles, strides, dilation and padding, against
 the fp64 reference, to the same per-element bound as the default path.
 """
@@ -21,7 +22,7 @@ from parity import TORCH_DT, assert_parity, to_f64
 pytestmark = pytest.mark.gpu
 
 # kernel name -> (plan_info kernel id, number of compiled variants)
-KERNELS = {"reg": (0, 3), "dma": (1, 8), "wide": (2, 9), "nchw": (3, 12), "strip": (4, 5), "striprb": (5, 7), "nchwstrip": (6, 10), "nchwtile": (7, 6), "tile16": (8, 11)}
+KERNELS = {"reg": (0, 3), "dma": (1, 12), "wide": (2, 9), "nchw": (3, 12), "strip": (4, 5), "striprb": (5, 7), "nchwstrip": (6, 10), "nchwtile": (7, 6), "tile16": (8, 11)}
 
 # (N, C, H, W, K, R, S, stride, pad, dilation)
 SHAPES_C32 = [
@@ -116,13 +117,13 @@ def _perm(t, lay):
 
 
 @pytest.mark.parametrize("case", _cases(), ids=lambda c: "%s%d-%s-%s-%s" % c[:5])
-def test_forced_kernel_parity(dev, monkeypatch, case):
+def test_forced_kernel_parity(dev, case):
     kind, v, dt, lay, algo, shapes = case
     kid = KERNELS[kind][0]
-    monkeypatch.setenv("CONVLOWER_KERNEL", "%s:%d" % (kind, v))
     ran = 0
     for si, (N, C, H, W, K, R, S, st, pd, dl) in enumerate(shapes):
-        d = cl.Conv2d(N, C, H, W, K, R, S, stride=st, padding=pd, dilation=dl, layout=lay, dtype=dt, algo=algo)
+        d = cl.Conv2d(N, C, H, W, K, R, S, stride=st, padding=pd, dilation=dl, layout=lay, dtype=dt, algo=algo,
+                      plan="%s:%d" % (kind, v))
         if d.info["kernel"] != kid or d.info["kernel_variant"] != v:
             continue      # this variant does not take the shape
         g = torch.Generator().manual_seed(300 + 17 * v + si)
@@ -140,7 +141,7 @@ def test_forced_kernel_parity(dev, monkeypatch, case):
     assert ran > 0, "no listed shape is taken by %s:%d" % (kind, v)
 
 
-def test_forced_kernel_integer_exact(dev, monkeypatch):
+def test_forced_kernel_integer_exact(dev):
     """Integer inputs through the strip and wide kernels: exact fp32 sums, so
     the result is the reference rounded once to fp16, bit for bit."""
     N, C, H, W, K, R, S = 2, 64, 12, 12, 96, 3, 3
@@ -151,9 +152,9 @@ def test_forced_kernel_integer_exact(dev, monkeypatch):
     xl, wl = _perm(x, "nhwc"), _perm(w, "nhwc")
     ref = oracle.conv2d(xl, wl, b, layout="nhwc", stride=1, padding=1)
     want = torch.from_numpy(ref).to(torch.float32).to(torch.float16)
-    for forced in ("strip:0", "strip:2", "strip:3", "wide:0", "wide:5", "striprb:0", "striprb:3", "striprb:4"):
-        monkeypatch.setenv("CONVLOWER_KERNEL", forced)
-        d = cl.Conv2d(N, C, H, W, K, R, S, padding=1, layout="nhwc", dtype="f16", algo="implicit")
+    for forced in ("strip:0", "strip:2", "strip:3", "wide:0", "wide:5", "striprb:0", "striprb:3", "striprb:4",
+                   "dma:8", "dma:9", "dma:10", "dma:11"):
+        d = cl.Conv2d(N, C, H, W, K, R, S, padding=1, layout="nhwc", dtype="f16", algo="implicit", plan=forced)
         assert d.info["kernel"] == KERNELS[forced.split(":")[0]][0], forced
         print("int case %s" % forced, flush=True)
         y = d.forward(xl.to(dev), wl.to(dev), b.to(dev))
@@ -161,7 +162,7 @@ def test_forced_kernel_integer_exact(dev, monkeypatch):
         assert torch.equal(y.cpu().view(torch.int16), want.view(torch.int16)), forced
 
 
-def test_small_window_kernel_integer_exact(dev, monkeypatch):
+def test_small_window_kernel_integer_exact(dev):
     """Integer inputs through the 16-bit NHWC small-window kernel (the stem
     shape at reduced size, every variant that takes it): exact fp32 sums, so
     the result is the reference rounded once, bit for bit."""
@@ -177,8 +178,8 @@ def test_small_window_kernel_integer_exact(dev, monkeypatch):
     want0 = torch.from_numpy(ref0).to(torch.float32).to(torch.bfloat16)
     ran = 0
     for v in range(KERNELS["tile16"][1]):
-        monkeypatch.setenv("CONVLOWER_KERNEL", "tile16:%d" % v)
-        d = cl.Conv2d(N, C, H, W, K, R, S, stride=2, padding=3, layout="nhwc", dtype="bf16", algo="implicit")
+        d = cl.Conv2d(N, C, H, W, K, R, S, stride=2, padding=3, layout="nhwc", dtype="bf16", algo="implicit",
+                      plan="tile16:%d" % v)
         if d.info["kernel"] != KERNELS["tile16"][0] or d.info["kernel_variant"] != v:
             continue
         print("int case tile16:%d" % v, flush=True)
@@ -204,18 +205,20 @@ SPLIT_CASES = [
     ("f16", "nhwc", "implicit", (2, 64, 17, 17, 72, 3, 3, (1, 1), (1, 1), (1, 1)), "wide:5:2"),
     ("bf16", "nhwc", "implicit", (3, 96, 9, 9, 300, 3, 3, (1, 1), (2, 2), (2, 2)), "wide:2:3"),
     ("bf16", "nhwc", "implicit", (8, 128, 7, 7, 256, 3, 3, (1, 1), (1, 1), (1, 1)), "wide:0:8"),
+    ("f16", "nhwc", "implicit", (3, 96, 9, 9, 300, 3, 3, (1, 1), (2, 2), (2, 2)), "dma:8:3"),
+    ("bf16", "nhwc", "implicit", (4, 256, 7, 7, 256, 3, 3, (1, 1), (1, 1), (1, 1)), "dma:9:2"),
 ]
 
 
 @pytest.mark.parametrize("case", SPLIT_CASES, ids=lambda c: "%s-%s-%s-%s" % (c[0], c[1], c[2], c[4]))
-def test_split_contraction_parity(dev, monkeypatch, case):
+def test_split_contraction_parity(dev, case):
     """Contraction split over several workgroups per output tile: fp32
     partials in the workspace, summed in split order with the bias by the
     reduction kernel.  Parity against the oracle with and without a bias, and
     the same bits on a second run (the sum order is fixed)."""
     dt, lay, algo, (N, C, H, W, K, R, S, st, pd, dl), forced = case
-    monkeypatch.setenv("CONVLOWER_KERNEL", forced)
-    d = cl.Conv2d(N, C, H, W, K, R, S, stride=st, padding=pd, dilation=dl, layout=lay, dtype=dt, algo=algo)
+    d = cl.Conv2d(N, C, H, W, K, R, S, stride=st, padding=pd, dilation=dl, layout=lay, dtype=dt, algo=algo,
+                  plan=forced)
     ks = int(forced.split(":")[2])
     assert d.info["kernel"] == KERNELS[forced.split(":")[0]][0] and d.info["ksplit"] == ks, d.info
     assert d.info["ws_partial_bytes"] == ks * d.info["M"] * K * 4
@@ -243,10 +246,10 @@ def test_split_contraction_parity(dev, monkeypatch, case):
     ("bf16", "nhwc", (8, 3, 64, 64, 64, 7, 7, (2, 2), (3, 3), (1, 1))),
     ("bf16", "nhwc", (8, 192, 20, 20, 96, 3, 3, (1, 1), (1, 1), (1, 1))),
 ], ids=lambda c: "%s-%s" % c[:2])
-def test_tune_keeps_a_correct_plan(dev, monkeypatch, case):
-    """conv_tune times the candidates and keeps the fastest; the kept plan
-    still matches the oracle, and is never slower than the default it timed."""
-    monkeypatch.delenv("CONVLOWER_KERNEL", raising=False)
+def test_tune_keeps_a_correct_plan(dev, case):
+    """conv_tune times the candidates and returns the fastest as a new
+    descriptor, leaving the one it tuned as it was; the kept plan still
+    matches the oracle, and is never slower than the default it timed."""
     dt, lay, (N, C, H, W, K, R, S, st, pd, dl) = case
     d = cl.Conv2d(N, C, H, W, K, R, S, stride=st, padding=pd, dilation=dl, layout=lay, dtype=dt, algo="implicit")
     g = torch.Generator().manual_seed(61)
@@ -257,12 +260,14 @@ def test_tune_keeps_a_correct_plan(dev, monkeypatch, case):
     xd, wd, bd = xl.to(dev), wl.to(dev), b.to(dev)
     ws = torch.empty(max(d.workspace_bytes, 8 << 20), dtype=torch.uint8, device=dev)
     print("tune %s %s %s" % (dt, lay, case[2]), flush=True)
-    r = d.tune(xd, wd, bd, ws=ws, reps=3)
+    before = (d.info["kernel"], d.info["kernel_variant"], d.info["ksplit"])
+    r, t = d.tune(xd, wd, bd, ws=ws, reps=3)
     assert r["candidates"] >= 2 and r["best_ms"] <= r["default_ms"]
-    assert (r["kernel"], r["kernel_variant"], r["ksplit"]) == (d.info["kernel"], d.info["kernel_variant"],
-                                                             d.info["ksplit"])
-    assert d.workspace_bytes <= ws.numel()
-    y = d.forward(xd, wd, bd, ws=ws)
+    assert (r["kernel"], r["kernel_variant"], r["ksplit"]) == (t.info["kernel"], t.info["kernel_variant"],
+                                                             t.info["ksplit"])
+    assert (d.info["kernel"], d.info["kernel_variant"], d.info["ksplit"]) == before
+    assert t.workspace_bytes <= ws.numel()
+    y = t.forward(xd, wd, bd, ws=ws)
     torch.cuda.synchronize()
     ref, yabs = oracle.conv2d(xl, wl, b, layout=lay, stride=st, padding=pd, dilation=dl, with_abs=True)
     assert_parity(to_f64(y.cpu()), ref, yabs, dt, "tuned %s" % (r,))
