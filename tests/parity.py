@@ -42,36 +42,6 @@ def assert_parity(got, ref, yabs, dtype: str, what: str = ""):
     return err
 
 
-def to_nkpq(y: np.ndarray, layout: str) -> np.ndarray:
-    return y if layout == "nchw" else np.ascontiguousarray(np.transpose(y, (0, 3, 1, 2)))
-
-
-def sample_points(N, K, P, Q, count, rng) -> np.ndarray:
-    """(n, k, p, q) rows: the whole border of the output map for the first and
-    last (n, k), the last channel tile's tail, and uniform random points."""
-    pts = []
-    for n, k in {(0, 0), (N - 1, K - 1), (N - 1, 0), (0, K - 1)}:
-        for p in range(P):
-            pts.append((n, k, p, 0))
-            pts.append((n, k, p, Q - 1))
-        for q in range(Q):
-            pts.append((n, k, 0, q))
-            pts.append((n, k, P - 1, q))
-    for k in range(max(0, K - 20), K):
-        pts.append((N - 1, k, P - 1, Q - 1))
-    r = np.stack([rng.integers(0, N, count), rng.integers(0, K, count), rng.integers(0, P, count),
-                  rng.integers(0, Q, count)], axis=1)
-    return np.unique(np.concatenate([np.array(pts, dtype=np.int64).reshape(-1, 4), r]), axis=0)
-
-
-def gather(y_nkpq_tensor_or_array, pts: np.ndarray) -> np.ndarray:
-    y = y_nkpq_tensor_or_array
-    if isinstance(y, torch.Tensor):
-        idx = torch.from_numpy(pts)
-        return to_f64(y[idx[:, 0], idx[:, 1], idx[:, 2], idx[:, 3]])
-    return y[tuple(pts.T)]
-
-
 # ---------------------------------------------------------------- expected lowered layouts (numpy)
 
 def padded_nchw(x_nchw: np.ndarray, ph: int, pw: int, extra_h: int, extra_w: int) -> np.ndarray:
