@@ -1,21 +1,32 @@
 """Benchmark: forward convolution through the HIP library on one MI355X.
 
-A step is one pass of the whole path over the workload's batch: for every
-layer, the filter pack, the input lowering (im2win strips by default) and the
-MFMA contraction with its fused bias epilogue; chained layers feed each
+A step is one pass of the whole path over one workload's batch: for every
+layer, the filter pack, the input lowering and the MFMA contraction with its
+fused bias epilogue (by default the fused path, whose windows are staged
+straight into LDS, so there is no lowering launch); chained layers feed each
 other's outputs.  Inputs are resident in device memory before timing starts.
 
-Default workload (N=1): the MSCRED-style encoder stack -- 1280 images of three
-30x30 symmetric signature matrices, fp32 NCHW, four convolutions 3x3 3->32 s1
-p1, 3x3 32->64 s2, 2x2 64->128 s2, 2x2 128->256 s2 ("GPU-Accelerating MSCRED
-with CUDA, im2col, GEMM, and a Custom PyTorch Extension", sections
-"Experimental Setup" and "Where the Performance Bottleneck Appeared").  The
-other workloads (c1, c3, c4, c5) can be timed with --workload.
+Headline (the default, N=1): the kernel-size sweep -- fp16 NHWC, 32 images of
+128 channels at 64x64, R = S in {1, 3, 5, 7, 11}, same padding -- the largest
+of the five workloads (880 GFLOP per step).  The other four workloads get a
+record each in the same JSON line (--configs).
 
-Prints one JSON line: TFLOP/s of the whole step (2*N*K*P*Q*C*R*S summed over
-layers / step time), the roofline position of the dominant kernel measured
-with HIP events on its own stream over the timed region, and the fp64
-reference convolution timed on the host cores on a bounded sample.
+Timing ("GPU-Accelerating MSCRED with CUDA, im2col, GEMM, and a Custom PyTorch
+Extension", section "Timing Methodology": the same input dimensions and batch
+for every measurement; "Thousands of (not-so) tiny SVDs: from 15 s to 66 ms on
+a GPU": best of several runs after a warm-up):
+  cold  every step follows a streaming pass over a 512 MiB buffer, twice the
+        256 MB last-level cache, so the step's inputs come from HBM; HIP events
+        around each step; the headline value is the median of these steps;
+  warm  the same steps back to back;
+both give the median over all timed steps and the best step.  The dominant
+kernel's launches are timed with HIP events on their own stream inside the
+cold timed region.  Measured peaks of this GPU (a register-only MFMA loop per
+instruction, the shader clock under it, a streaming copy) are taken in the
+same run and every fraction is given against them as well as against the
+published MI355X figures.
+
+Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -23,6 +34,7 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -34,9 +46,10 @@ METRIC = "conv2d fwd TFLOPS and % of MFMA peak; workspace bytes vs im2col"
 # MI355X published peaks: dense MFMA per storage type, HBM3E bandwidth
 PEAK_TFLOPS = {"f32": 157.3, "f16": 2516.6, "bf16": 2516.6}
 PEAK_HBM_GBS = 8000.0
-# ConvLSTM step measured beside the stack (--workload lstm): one cell per
-# encoder level of c2 (hidden channels = the level's channels, 3x3 gate
-# filter, same padding), 256 windows, 5 time steps per pass.
+FLUSH_BYTES = 512 << 20          # twice the 256 MB last-level cache
+# ConvLSTM step measured on its own (--workload lstm): one cell per encoder
+# level of c2 (hidden channels = the level's channels, 3x3 gate filter, same
+# padding), 256 windows, 5 time steps per pass.
 LSTM_LEVELS = [(32, 30), (64, 14), (128, 7), (256, 3)]   # (channels, H = W)
 LSTM_WINDOWS, LSTM_STEPS = 256, 5
 WORKLOAD_TEXT = {
@@ -63,6 +76,14 @@ def source_digest() -> str:
     return h.hexdigest()[:16]
 
 
+def _x_dims(shape, layout):
+    if layout == "nchw":
+        N, C, H, W = shape
+    else:
+        N, H, W, C = shape
+    return N, C, H, W
+
+
 def build_layers(wl, dev, algo):
     import cnn_convolution_lowering_amd as cl
     import torch
@@ -80,14 +101,6 @@ def build_layers(wl, dev, algo):
     ws_bytes = max(l["desc"].workspace_bytes for l in layers)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     return layers, ws
-
-
-def _x_dims(shape, layout):
-    if layout == "nchw":
-        N, C, H, W = shape
-    else:
-        N, H, W, C = shape
-    return N, C, H, W
 
 
 STAGES = ("pack", "lower", "contract")
@@ -113,7 +126,7 @@ def stage_launches(l, stage) -> bool:
 
 
 def kernel_breakdown(layers, ws, stream, reps=10):
-    """Average duration (ms) of every launched kernel, from HIP events on `stream`."""
+    """Average duration (ms) of every launched stage, from HIP events on `stream`."""
     import torch
     out = {}
     for i, l in enumerate(layers):
@@ -135,7 +148,12 @@ def kernel_breakdown(layers, ws, stream, reps=10):
 
 
 def kernel_work(l, stage):
-    """(algorithmic flops, algorithmic bytes) of one launch of a stage kernel."""
+    """(algorithmic flops, algorithmic bytes) of one launch of a stage.
+
+    contract: 2*C*R*S flops per output element; bytes = the A operand read
+    once (x for the fused and in-place paths, else the lowered buffer) + the
+    filter (or its packed copy) + y + bias.  lower: x + the lowered buffer.
+    pack: the filter + its packed copy."""
     info = l["desc"].info
     eb = info["elem_bytes"]
     d = l["desc"]
@@ -154,7 +172,7 @@ def kernel_work(l, stage):
 
 CONTRACT_KERNELS = ["conv_gemm_kernel", "conv_gemm_dma_kernel", "conv_gemm_wide_kernel", "conv_nchw_f32_dma_kernel",
                     "conv_strip_kernel", "conv_strip_rb_kernel", "conv_nchw_f32_strip_kernel",
-                    "conv_nchw_f32_tile_kernel", "conv_nhwc_tile16_kernel"]
+                    "conv_nchw_f32_tile_kernel", "conv_nhwc_tile16_kernel", "conv_gemm_streamk_kernel"]
 
 
 def kernel_symbol(l, stage):
@@ -176,23 +194,221 @@ def kernel_symbol(l, stage):
     return "lower_%s_band_kernel" % d.layout
 
 
+def load_traffic(kernel_key: str):
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(kernel_key)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha256_16") != source_digest():
+        return None      # counters were taken on a different kernel source
+    return rec.get("bytes_per_launch")
+
+
+class Flusher:
+    """A streaming read-modify-write of FLUSH_BYTES (twice the 256 MB
+    last-level cache) between cold steps."""
+
+    def __init__(self, dev):
+        import torch
+        self.buf = torch.zeros(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+
+    def __call__(self):
+        self.buf.add_(1.0)
+
+
+def time_steps(step, stream, steps, warmup, flush=None, rec_dom=False):
+    """Per-step ms from HIP events on `stream` (warm: back to back; cold:
+    `flush` before each step, outside its events), the dominant kernel's
+    launch times when `rec_dom`, and host wall seconds of the whole region."""
+    import torch
+    for _ in range(warmup):
+        if flush:
+            flush()
+        step(None)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    dom = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    h0 = time.perf_counter()
+    for k in range(steps):
+        if flush:
+            flush()
+        evs[k][0].record(stream)
+        step(dom[k] if rec_dom else None)
+        evs[k][1].record(stream)
+    torch.cuda.synchronize()
+    h1 = time.perf_counter()
+    ms = [a.elapsed_time(b) for a, b in evs]
+    dms = [a.elapsed_time(b) for a, b in dom] if rec_dom else []
+    return ms, dms, h1 - h0
+
+
+def summary(ms):
+    s = sorted(ms)
+    return {"median_ms": statistics.median(s), "best_ms": s[0], "best5_mean_ms": sum(s[:5]) / len(s[:5]),
+            "steps": len(s)}
+
+
+def bench_config(name, dev, args, peaks, headline=False):
+    """Time one workload: the fused path cold and warm (headline measures),
+    per-kernel durations, the roofline of its dominant kernel, and the two
+    lowered algorithms."""
+    import torch
+    from cnn_convolution_lowering_amd.workloads import make_workload
+    wl = make_workload(name)
+    spec = wl.spec
+    say("bench: %s: building inputs" % name)
+    layers, ws = build_layers(wl, dev, args.algo)
+    stream = torch.cuda.current_stream(dev)
+    step_flops = sum(l["flops"] for l in layers)
+    peak_f = PEAK_TFLOPS[spec.dtype]
+    mpeak_f = peaks.get(spec.dtype) if peaks else None
+
+    for _ in range(2):
+        for l in layers:
+            for st in STAGES:
+                run_stage(l, st, ws, stream)
+    torch.cuda.synchronize()
+    brk = kernel_breakdown(layers, ws, stream)
+    dom = max(brk, key=brk.get)
+    dom_layer, dom_stage = dom
+
+    def step(rec=None):
+        for i, l in enumerate(layers):
+            for st in STAGES:
+                if rec is not None and (i, st) == dom:
+                    rec[0].record(stream)
+                    run_stage(l, st, ws, stream)
+                    rec[1].record(stream)
+                else:
+                    run_stage(l, st, ws, stream)
+
+    steps = args.steps if headline else max(30, args.steps // 2)
+    warmup = args.warmup if headline else max(3, args.warmup // 2)
+    flush = Flusher(dev)
+    say("bench: %s: %d cold steps" % (name, steps))
+    cold_ms, dom_ms_list, host_s = time_steps(step, stream, steps, warmup, flush=flush, rec_dom=True)
+    del flush
+    torch.cuda.empty_cache()
+    say("bench: %s: %d warm steps" % (name, steps))
+    warm_ms, _, _ = time_steps(step, stream, steps, warmup)
+    cold, warm = summary(cold_ms), summary(warm_ms)
+    dom_ms = sum(dom_ms_list) / len(dom_ms_list)
+
+    dl = layers[dom_layer]
+    flops, nbytes = kernel_work(dl, dom_stage)
+    compute_bound = flops > 0 and flops / (peak_f * 1e12) >= nbytes / (PEAK_HBM_GBS * 1e9)
+    kernel_key = "%s/%s/layer%d/%s" % (spec.name, args.algo, dom_layer, dom_stage)
+    if compute_bound:
+        achieved = flops / (dom_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": peak_f, "unit": "TFLOP/s", "frac": achieved / peak_f}
+        if mpeak_f:
+            roof.update({"measured_peak": mpeak_f, "frac_of_measured": achieved / mpeak_f})
+    else:
+        achieved = nbytes / (dom_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS}
+        if peaks and peaks.get("hbm_gbs"):
+            roof.update({"measured_peak": peaks["hbm_gbs"], "frac_of_measured": achieved / peaks["hbm_gbs"]})
+    roof.update({"traffic": load_traffic(kernel_key), "kernel": kernel_symbol(dl, dom_stage),
+                 "kernel_key": kernel_key, "layer": dl["spec"].label, "avg_launch_ms": dom_ms,
+                 "launches_timed": len(dom_ms_list), "algorithmic_flops": flops, "algorithmic_bytes": nbytes})
+
+    per_layer = []
+    for i, l in enumerate(layers):
+        info = l["desc"].info
+        lay_ms = sum(v for (j, _), v in brk.items() if j == i)
+        p, eb = l["desc"].params, info["elem_bytes"]
+        b_min = (p.N * p.C * p.H * p.W + p.K * p.C * p.R * p.S + p.K + p.N * p.K * l["desc"].P * l["desc"].Q) * eb
+        mfma_bound = l["flops"] / (peak_f * 1e12) >= b_min / (PEAK_HBM_GBS * 1e9)
+        gbs = b_min / (lay_ms * 1e-3) / 1e9 if lay_ms else None
+        tfs = l["flops"] / (lay_ms * 1e-3) / 1e12 if lay_ms else None
+        rec = {"layer": l["spec"].label, "gflop": l["flops"] / 1e9,
+               "kernels_ms": {st: round(brk[(i, st)], 5) for st in STAGES if (i, st) in brk},
+               "contract_kernel": kernel_symbol(l, "contract"),
+               "plan": [info["kernel"], info["kernel_variant"], info["ksplit"]],
+               "tflops_isolated": tfs, "bound": "mfma" if mfma_bound else "hbm",
+               "frac_of_peak": (tfs / peak_f if mfma_bound else gbs / PEAK_HBM_GBS) if lay_ms else None,
+               "b_min_bytes": b_min, "b_min_gbs_isolated": gbs,
+               "im2win_bytes": info["im2win_bytes"], "im2col_bytes": info["im2col_bytes"],
+               "tile": [info["tile_m"], info["tile_n"], info["tile_k"]]}
+        if mfma_bound and mpeak_f and tfs:
+            rec["frac_of_measured_peak"] = tfs / mpeak_f
+        per_layer.append(rec)
+    del layers, ws
+    torch.cuda.empty_cache()
+
+    rec = {"workload": "%s: %s" % (spec.name, WORKLOAD_TEXT[spec.name]), "dtype": spec.dtype,
+           "gflop_per_step": step_flops / 1e9,
+           "tflops": step_flops / (cold["median_ms"] * 1e-3) / 1e12,
+           "tflops_warm": step_flops / (warm["median_ms"] * 1e-3) / 1e12,
+           "tflops_best": step_flops / (min(cold["best_ms"], warm["best_ms"]) * 1e-3) / 1e12,
+           "cold": cold, "warm": warm, "host_s_cold_region": host_s,
+           "frac_of_peak": step_flops / (cold["median_ms"] * 1e-3) / 1e12 / peak_f, "roofline": roof,
+           "layers": per_layer, "algo": args.algo}
+    if mpeak_f:
+        rec["frac_of_measured_peak"] = rec["tflops"] / mpeak_f
+
+    # The lowered algorithms: their time and workspace (the im2win / im2col comparison).
+    algos = {}
+    for algo in (("implicit", "im2win", "im2col") if not args.only_algo else (args.algo,)):
+        say("bench: %s: the %s path" % (name, algo))
+        lay, w2 = build_layers(wl, dev, algo)
+
+        def step2(rec=None, lay=lay, w2=w2):
+            for l in lay:
+                for st in STAGES:
+                    run_stage(l, st, w2, stream)
+
+        ms2, _, _ = time_steps(step2, stream, max(10, steps // 3), 2)
+        s2 = summary(ms2)
+        low = max(l["desc"].info["ws_lowered_bytes"] for l in lay)
+        col = max(l["desc"].info["im2col_bytes"] for l in lay)
+        algos[algo] = {"median_ms": s2["median_ms"], "best_ms": s2["best_ms"],
+                       "tflops": step_flops / (s2["median_ms"] * 1e-3) / 1e12,
+                       "workspace_bytes": max(l["desc"].workspace_bytes for l in lay),
+                       "lowered_max_bytes": low, "im2col_max_bytes": col, "lowered_vs_im2col": low / col}
+        del lay, w2
+        torch.cuda.empty_cache()
+    rec["algorithms"] = algos
+    # im2win strips against explicit im2col, max over layers each (the im2win
+    # path's own workspace; in-place 1x1 layers lower nothing)
+    if "im2win" in algos:
+        rec["im2win_vs_im2col"] = algos["im2win"]["lowered_vs_im2col"]
+    return rec, wl
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, budget_s=10.0):
-    """The fp64 reference convolution, as it stands, on a bounded sample of the
-    workload's images (every layer, chained as the workload chains them)."""
+    """The fp64 reference convolution, as it stands, on a bounded sample of
+    the workload's images (every layer, chained as the workload chains them)
+    on every host core the process may use; then one layer of one image on
+    one thread (the single-thread baseline)."""
     import numpy as np
     import torch
     import oracle
     spec = wl.spec
     threads = oracle.default_threads()
 
-    def run(n_img):
+    def run(n_img, layers, nthreads):
         flops = 0
         t0 = time.perf_counter()
         prev = None
-        for L in wl.layers:
+        for L in layers:
             x = (L.x[:n_img] if L.x is not None else prev)
             y = oracle.conv2d(x, L.w, L.b, layout=spec.layout, stride=L.stride, padding=L.padding,
-                              dilation=L.dilation, nthreads=threads)
+                              dilation=L.dilation, nthreads=nthreads)
             if spec.layout == "nchw":
                 _, K, P, Q = y.shape
             else:
@@ -201,16 +417,18 @@ def cpu_baseline(wl, budget_s=10.0):
             prev = torch.from_numpy(np.ascontiguousarray(y)).to(wl.dtype) if spec.chained else None
         return flops, time.perf_counter() - t0
 
-    probe = max(1, min(spec.N, 4))
-    f, t = run(probe)
-    n = int(min(spec.N, max(probe, probe * budget_s / max(t, 1e-6))))
-    if n > probe:
-        f, t = run(n)
-    else:
-        n = probe
-    return {"value": f / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+    f, t = run(1, wl.layers, threads)
+    n = int(min(spec.N, max(1, budget_s / max(t, 1e-6))))
+    if n > 1:
+        f, t = run(n, wl.layers, threads)
+    # single thread: the cheapest compute layer (a chained stack keeps its first layer)
+    one = [wl.layers[0]] if spec.chained else [min(wl.layers, key=lambda L: L.C * L.R * L.S * L.K if L.R > 1 else 1e30)]
+    f1, t1 = run(1, one, 1)
+    return {"value": f / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle", "cpu_model": cpu_model(),
             "sample": "%d of %d images of workload %s, all %d layers, fp64 seven-loop reference, %.1f s"
-                      % (n, spec.N, spec.name, len(wl.layers), t)}
+                      % (n, spec.N, spec.name, len(wl.layers), t),
+            "single_thread": {"value": f1 / t1 / 1e12, "unit": "TFLOP/s", "cores": 1,
+                              "sample": "1 image, layer %s, %.1f s" % (one[0].label, t1)}}
 
 
 def bench_lstm(args, dev):
@@ -233,44 +451,37 @@ def bench_lstm(args, dev):
                        "flops": flops, "ch": ch, "hw": hw})
     step_flops = sum(l["flops"] for l in levels) * LSTM_STEPS
     dom = max(range(len(levels)), key=lambda i: levels[i]["flops"])
+    stream = torch.cuda.current_stream(dev)
 
     def one_pass(rec=None):
         for i, l in enumerate(levels):
             h, c, h2, c2 = l["st"]
             for t in range(LSTM_STEPS):
                 if rec is not None and i == dom and t == 0:
-                    rec[0].record()
+                    rec[0].record(stream)
                 l["cell"].step(l["xs"][t], h, c, l["w"], l["b"], h_out=h2, c_out=c2, ws=l["ws"])
                 if rec is not None and i == dom and t == 0:
-                    rec[1].record()
+                    rec[1].record(stream)
                 h, c, h2, c2 = h2, c2, h, c
 
-    for _ in range(args.warmup):
-        one_pass()
-    torch.cuda.synchronize()
-    recs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record()
-    for i in range(args.steps):
-        one_pass(recs[i])
-    t1.record()
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / args.steps
-    dom_ms = sum(a.elapsed_time(b) for a, b in recs) / args.steps
+    ms, dms, host_s = time_steps(one_pass, stream, args.steps, args.warmup, rec_dom=True)
+    s = summary(ms)
+    dom_ms = sum(dms) / len(dms)
     achieved = levels[dom]["flops"] / (dom_ms * 1e-3) / 1e12
-    out = {"metric": "ConvLSTM step gate-convolution TFLOP/s", "value": step_flops / (ms * 1e-3) / 1e12,
-           "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
-           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-           "config": {"workload": "lstm: " + WORKLOAD_TEXT["lstm"], "algo": args.algo},
+    out = {"metric": "ConvLSTM step gate-convolution TFLOP/s", "value": step_flops / (s["median_ms"] * 1e-3) / 1e12,
+           "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": s["median_ms"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "f32", "data": "synthetic", "config": {"workload": "lstm: " + WORKLOAD_TEXT["lstm"],
+                                                           "algo": args.algo},
+           "warm": s, "host_s": host_s,
            "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_TFLOPS["f32"], "unit": "TFLOP/s",
                         "frac": achieved / PEAK_TFLOPS["f32"], "traffic": None,
                         "kernel": "conv_lstm_step (pack, lowering, conv_gemm_dma_kernel with the cell epilogue)",
                         "level": "%dx%dx%d" % (levels[dom]["ch"], levels[dom]["hw"], levels[dom]["hw"]),
                         "avg_launch_ms": dom_ms}}
     if not args.no_cpu_baseline:
-        import numpy as np
         from oracle.convlstm import convlstm_step
+        import oracle
         l = levels[0]
 
         def run(n):
@@ -285,138 +496,46 @@ def bench_lstm(args, dev):
         m = int(min(LSTM_WINDOWS, max(n, n * args.cpu_budget / max(dt, 1e-6))))
         if m > n:
             n, dt = m, run(m)
-        import oracle
         out["cpu_baseline"] = {"value": l["flops"] * n / LSTM_WINDOWS / dt / 1e12, "unit": "TFLOP/s",
-                               "cores": oracle.default_threads(), "kind": "oracle",
+                               "cores": oracle.default_threads(), "kind": "oracle", "cpu_model": cpu_model(),
                                "sample": "%d of %d windows, one step of the 32x30x30 level, fp64 reference, %.2f s"
                                          % (n, LSTM_WINDOWS, dt)}
     print(json.dumps(out), flush=True)
     return 0
 
 
-def time_steps(wl, dev, algo, steps, warmup, layer=None):
-    """ms per step of the whole path with one lowering, HIP events on the
-    current stream; also the largest workspace of its layers."""
-    import torch
-    layers, ws = build_layers(wl, dev, algo)
-    stream = torch.cuda.current_stream(dev)
-    if layer is not None:
-        for l in layers[:layer]:
-            for st in STAGES:
-                run_stage(l, st, ws, stream)
-        layers = [layers[layer]]
-    for _ in range(warmup):
-        for l in layers:
-            for st in STAGES:
-                run_stage(l, st, ws, stream)
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    a.record(stream)
-    for _ in range(steps):
-        for l in layers:
-            for st in STAGES:
-                run_stage(l, st, ws, stream)
-    b.record(stream)
-    torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / steps
-    info = {"ms_per_step": ms,
-            "workspace_bytes": max(l["desc"].workspace_bytes for l in layers),
-            "lowered_bytes_max": max(l["desc"].info["ws_lowered_bytes"] for l in layers),
-            "im2col_bytes_max": max(l["desc"].info["im2col_bytes"] for l in layers)}
-    del layers, ws
-    return info
-
-
-def load_traffic(kernel_key: str):
-    try:
-        with open(TRAFFIC_FILE) as f:
-            rec = json.load(f).get(kernel_key)
-    except (OSError, ValueError):
-        return None
-    if not rec or rec.get("source_sha256_16") != source_digest():
-        return None      # counters were taken on a different kernel source
-    return rec.get("bytes_per_launch")
-
-
-def gemm_calibration(dev):
-    """torch.matmul (hipBLASLt) on A[M x C*R*S] @ B[C*R*S x K] for every layer
-    of the 16-bit workloads -- the contraction of each convolution without its
-    window gather -- and on 8192^3 in fp16, bf16 and fp32, 20 timed calls each
-    after 3 warm-up calls;
-    one JSON line per product."""
-    import torch
-    import cnn_convolution_lowering_amd as cl
-    from cnn_convolution_lowering_amd.workloads import workload_spec
-    tdt = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}
-    torch.backends.cuda.matmul.allow_tf32 = False   # full fp32 products
-    shapes = []
-    for name in ("c3", "c4", "c5"):
-        spec = workload_spec(name)
-        H = W = None
-        for L in spec.layers:
-            if L.H is not None:
-                H, W = L.H, L.W
-            c = cl.Conv2d(spec.N, L.C, H, W, L.K, L.R, L.S, stride=L.stride, padding=L.padding,
-                          layout=spec.layout, dtype=spec.dtype, algo="implicit")
-            shapes.append(("%s %s" % (name, L.label), spec.dtype, c.info["M"], L.K, L.C * L.R * L.S))
-            if spec.chained:
-                H, W = c.P, c.Q
-    shapes += [("square 8192", dt, 8192, 8192, 8192) for dt in ("f16", "bf16", "f32")]
-    for label, dt, M, N, K in shapes:
-        g = torch.Generator(device=dev).manual_seed(7)
-        a = torch.randn(M, K, device=dev, generator=g).to(tdt[dt])
-        b = torch.randn(K, N, device=dev, generator=g).to(tdt[dt])
-        for _ in range(3):
-            c = a @ b
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(20):
-            c = a @ b
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / 20
-        tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
-        print(json.dumps({"gemm": label, "dtype": dt, "M": M, "N": N, "K": K, "ms": round(ms, 4),
-                          "tflops": round(tf, 1), "frac_of_peak": round(tf / PEAK_TFLOPS[dt], 3)}), flush=True)
-        del a, b, c
-    return 0
+def say(msg):
+    print(msg, file=sys.stderr, flush=True)
 
 
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=50, help="timed steps of the headline workload (>= 30)")
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="c2", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--workload", default="c5", choices=sorted(WORKLOAD_TEXT), help="headline workload")
+    ap.add_argument("--configs", default="c1,c2,c3,c4",
+                    help="other workloads given a record in the same line (comma list; '' for none)")
     ap.add_argument("--algo", default="implicit", choices=["im2win", "im2col", "implicit"],
-                    help="lowering timed for the headline value (the other two are timed as well, "
-                         "unless --only-algo)")
+                    help="path timed for the headline (the other two are timed as well, unless --only-algo)")
     ap.add_argument("--only-algo", action="store_true", help="time only --algo")
-    ap.add_argument("--layer", type=int, default=None,
-                    help="time only this layer of the workload (chained inputs are still computed once)")
-    ap.add_argument("--tune", action="store_true",
-                    help="conv_tune every layer (kernel and tile variant) before timing")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured-peak microbenchmarks")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of reference work to time")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
-                    help="only run a plain device-to-device copy of this many MiB (5 times), to scale "
-                         "the HBM byte counters of a profiler against a transfer of known size")
-    ap.add_argument("--gemm-calibration", action="store_true",
-                    help="only time the vendor GEMM (torch.matmul, hipBLASLt) on the plain M x K x C*R*S "
-                         "products of the 16-bit workloads' layers and on 8192^3 products (fp16, bf16, "
-                         "fp32): what the library reaches on this GPU, a measured peak next to the "
-                         "published one")
+                    help="only run the library's streaming copy over this many MiB, 5 times: a transfer of known "
+                         "size against which a profiler's HBM byte counters are scaled")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
         print("bench.py: measures one GPU; --gpus %d is not supported (the convolution would shard over "
               "images, each GPU running the same path on its share with no exchange)" % args.gpus, file=sys.stderr)
         return 2
+    args.steps = max(30, args.steps)
 
     import torch
     import cnn_convolution_lowering_amd as cl
-    from cnn_convolution_lowering_amd.workloads import make_workload
+    from cnn_convolution_lowering_amd import peak
 
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
@@ -424,148 +543,59 @@ def main(argv=None):
     cl.load_library()
     dev = torch.device("cuda:0")
     if args.copy_calibration_mib:
+        import ctypes
+        lib = peak.load_peak_library()
         n = args.copy_calibration_mib << 20
         src = torch.ones(n, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
+        sp = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
         for _ in range(5):
-            dst.copy_(src)
+            if lib.convpeak_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()), n, sp) != 0:
+                raise RuntimeError("convpeak_copy failed")
         torch.cuda.synchronize()
-        print(json.dumps({"copy_bytes_per_launch": n, "launches": 5}))
+        print(json.dumps({"copy_bytes_read_per_launch": n, "copy_bytes_written_per_launch": n, "launches": 5,
+                          "kernel": "peak_copy_kernel"}))
         return 0
-    if args.gemm_calibration:
-        return gemm_calibration(dev)
     if args.workload == "lstm":
         if args.algo == "implicit":
             args.algo = "im2win"   # the ConvLSTM step reads x and h through the lowering
         return bench_lstm(args, dev)
-    wl = make_workload(args.workload)
+
+    peaks = None
+    if not args.no_peaks:
+        say("bench: measured peaks (MFMA loop per instruction, sustained and burst; streaming copy)")
+        peaks = peak.measure_peaks(dev)
+
+    head, wl = bench_config(args.workload, dev, args, peaks, headline=True)
     spec = wl.spec
-    print("bench: workload %s, algo %s, building inputs" % (spec.name, args.algo), file=sys.stderr, flush=True)
-    layers, ws = build_layers(wl, dev, args.algo)
-    stream = torch.cuda.current_stream(dev)
-    tuned = None
-    if args.tune:
-        print("bench: tuning the layers' kernels", file=sys.stderr, flush=True)
-        tuned = []
-        for l in layers:   # in order: a chained layer's input is its producer's output
-            r = l["desc"].tune(l["x"], l["w"], l["b"], l["y"], ws, reps=5)
-            tuned.append({"layer": l["spec"].label, "kernel": r["kernel"], "variant": r["kernel_variant"],
-                          "candidates": r["candidates"], "default_ms": r["default_ms"], "best_ms": r["best_ms"]})
-    if args.layer is not None:
-        # inputs of a chained layer come from one pass of the layers before it
-        for l in layers[:args.layer]:
-            for st in STAGES:
-                run_stage(l, st, ws, stream)
-        layers = [layers[args.layer]]
-    step_flops = sum(l["flops"] for l in layers)
-
-    # Per-kernel durations (outside the timed region) pick the dominant kernel.
-    for _ in range(2):
-        for l in layers:
-            for st in STAGES:
-                run_stage(l, st, ws, stream)
-    torch.cuda.synchronize()
-    brk = kernel_breakdown(layers, ws, stream)
-    dom = max(brk, key=brk.get)
-    dom_layer, dom_stage = dom
-
-    def step(rec=None):
-        for i, l in enumerate(layers):
-            for st in STAGES:
-                if rec is not None and (i, st) == dom:
-                    rec[0].record(stream)
-                    run_stage(l, st, ws, stream)
-                    rec[1].record(stream)
-                else:
-                    run_stage(l, st, ws, stream)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    print("bench: timing %d steps" % args.steps, file=sys.stderr, flush=True)
-    recs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    h0 = time.perf_counter()
-    t_start.record(stream)
-    for k in range(args.steps):
-        step(recs[k])
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    h1 = time.perf_counter()
-    ms_step = t_start.elapsed_time(t_end) / args.steps
-    dom_ms = sum(a.elapsed_time(b) for a, b in recs) / args.steps
-    tflops = step_flops / (ms_step * 1e-3) / 1e12
-
-    # roofline of the dominant kernel
-    dl = layers[dom_layer]
-    flops, nbytes = kernel_work(dl, dom_stage)
-    peak_f = PEAK_TFLOPS[spec.dtype]
-    compute_bound = flops > 0 and flops / (peak_f * 1e12) >= nbytes / (PEAK_HBM_GBS * 1e9)
-    kernel_key = "%s/%s/layer%d/%s" % (spec.name, args.algo, dom_layer, dom_stage)
-    traffic = load_traffic(kernel_key)
-    if compute_bound:
-        achieved = flops / (dom_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": achieved, "peak": peak_f, "unit": "TFLOP/s", "frac": achieved / peak_f}
-    else:
-        achieved = nbytes / (dom_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": achieved / PEAK_HBM_GBS}
-    roof.update({"traffic": traffic, "kernel": kernel_symbol(dl, dom_stage), "kernel_key": kernel_key,
-                 "layer": dl["spec"].label, "avg_launch_ms": dom_ms, "algorithmic_flops": flops,
-                 "algorithmic_bytes": nbytes})
-
-    per_layer = []
-    for i, l in enumerate(layers):
-        info = l["desc"].info
-        lay_ms = sum(v for (j, _), v in brk.items() if j == i)
-        # compulsory traffic B_min = x + w + b + y once, and the layer's bound
-        p, eb = l["desc"].params, info["elem_bytes"]
-        b_min = (p.N * p.C * p.H * p.W + p.K * p.C * p.R * p.S + p.K + p.N * p.K * l["desc"].P * l["desc"].Q) * eb
-        mfma_bound = l["flops"] / (peak_f * 1e12) >= b_min / (PEAK_HBM_GBS * 1e9)
-        gbs = b_min / (lay_ms * 1e-3) / 1e9 if lay_ms else None
-        tfs = l["flops"] / (lay_ms * 1e-3) / 1e12 if lay_ms else None
-        per_layer.append({
-            "layer": l["spec"].label, "gflop": l["flops"] / 1e9,
-            "kernels_ms": {st: round(brk[(i, st)], 5) for st in STAGES if (i, st) in brk},
-            "tflops_isolated": tfs,
-            "bound": "mfma" if mfma_bound else "hbm",
-            "frac_of_peak": (tfs / peak_f if mfma_bound else gbs / PEAK_HBM_GBS) if lay_ms else None,
-            "b_min_bytes": b_min, "b_min_gbs_isolated": gbs,
-            "ws_lowered_bytes": info["ws_lowered_bytes"], "im2col_bytes": info["im2col_bytes"],
-            "ws_vs_im2col": info["ws_lowered_bytes"] / info["im2col_bytes"],
-            "tile": [info["tile_m"], info["tile_n"], info["tile_k"]]})
-
+    ms = head["cold"]["median_ms"]
     out = {
-        "metric": METRIC, "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "metric": METRIC, "value": head["tflops"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": spec.dtype, "data": "synthetic",
-        "config": {"workload": "%s: %s" % (spec.name, WORKLOAD_TEXT[spec.name]), "algo": args.algo,
-                   "batch": spec.N, "layers": len(layers), "layout": spec.layout},
-        "pct_of_mfma_peak": 100.0 * tflops / peak_f,
-        "host_ms_per_step": (h1 - h0) * 1e3 / args.steps,
-        "roofline": roof,
-        "workspace": {"bytes": max(l["desc"].workspace_bytes for l in layers),
-                      "lowered_max_bytes": max(p["ws_lowered_bytes"] for p in per_layer),
-                      "im2col_max_bytes": max(p["im2col_bytes"] for p in per_layer),
-                      "ratio_max_over_layers": max(p["ws_vs_im2col"] for p in per_layer)},
-        "layers": per_layer,
+        "config": {"workload": head["workload"], "algo": args.algo, "batch": spec.N, "layers": len(spec.layers),
+                   "layout": spec.layout, "timing": "cold (512 MiB streamed between steps), median of %d steps"
+                                                    % args.steps},
+        "pct_of_mfma_peak": 100.0 * head["frac_of_peak"],
+        "roofline": head["roofline"],
+        "cold": head["cold"], "warm": head["warm"], "tflops_warm": head["tflops_warm"],
+        "tflops_best": head["tflops_best"],
+        "measured_peak": peaks,
+        "workspace": {"im2win_vs_im2col": head.get("im2win_vs_im2col"),
+                      "definition": "largest im2win lowered buffer over the layers / largest explicit im2col "
+                                    "matrix over the layers",
+                      "fused_path_lowered_bytes": head["algorithms"].get("implicit", {}).get("lowered_max_bytes")},
+        "layers": head["layers"], "algorithms": head["algorithms"],
     }
-    if tuned is not None:
-        out["config"]["tuned"] = True
-        out["tuning"] = tuned
-    if not args.only_algo:
-        flops_total = step_flops
-        algos = {}
-        for algo in ("implicit", "im2win", "im2col"):
-            print("bench: timing the %s lowering" % algo, file=sys.stderr, flush=True)
-            r = time_steps(wl, dev, algo, max(5, args.steps // 2), max(2, args.warmup // 2), args.layer)
-            r["tflops"] = flops_total / (r["ms_per_step"] * 1e-3) / 1e12
-            algos[algo] = r
-        out["algorithms"] = algos
+    if peaks:
+        out["pct_of_measured_mfma_peak"] = 100.0 * head["frac_of_measured_peak"]
+    configs = {}
+    for name in [c for c in args.configs.split(",") if c and c != args.workload]:
+        rec, _ = bench_config(name, dev, args, peaks)
+        configs[name] = rec
+    out["configs"] = configs
     if not args.no_cpu_baseline:
-        print("bench: timing the fp64 reference on the host", file=sys.stderr, flush=True)
+        say("bench: timing the fp64 reference on the host")
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
     print(json.dumps(out), flush=True)
     return 0
