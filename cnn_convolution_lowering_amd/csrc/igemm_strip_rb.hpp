@@ -221,9 +221,20 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) conv_strip_rb_kernel(GemmAr
         if (new_strip) {
             // Strip strip_k+1 (in the other buffer) must have landed for every
             // wave, and every wave must be done reading this strip's buffer
-            // before it is refilled.  The wave's loads issued after that strip
-            // are filter loads only, at least one step's worth (S >= 2).
-            wait_vmcnt<2 * TN>();
+            // before it is refilled.  Its loads went out at the end of the
+            // previous strip boundary; the wave's loads since then are filter
+            // fragments only: 2*TN per step of this strip, less the TN of this
+            // half not yet issued, (2S-1)*TN in all.  Loads complete in order,
+            // so waiting until at most that many are in flight waits for the
+            // strip and nothing later; the wait keeps as many of the filter
+            // loads in flight as its 6-bit count allows, so the filter
+            // prefetch does not drain at every strip.
+            if (S >= 8)
+                wait_vmcnt<(15 * TN < 63 ? 15 * TN : 63)>();
+            else if (S >= 4)
+                wait_vmcnt<7 * TN>();
+            else
+                wait_vmcnt<2 * TN>();
             asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
             lds_barrier();
         }
