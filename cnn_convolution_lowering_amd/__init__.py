@@ -83,6 +83,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "conv_output_dims": [vp, i64p, i64p],
         "conv_plan_info": [vp, ctypes.POINTER(PlanInfo)],
         "conv2d_fwd": [vp, vp, vp, vp, vp, vp, vp],
+        "conv2d_fwd_noalloc": [vp, vp, vp, vp, vp, vp],
         "conv_pack_filter": [vp, vp, vp, vp],
         "conv_lower_input": [vp, vp, vp, vp],
         "conv_contract": [vp, vp, vp, vp, vp, vp, vp],
@@ -246,6 +247,18 @@ class Conv2d:
         ws = self._ws(ws, x.device)
         _check(self.lib.conv2d_fwd(self._desc, self._ptr(x), self._ptr(w), self._ptr(bias), self._ptr(y),
                                    self._ptr(ws), self._stream(stream, x.device)), "conv2d_fwd")
+        return y
+
+    def forward_noalloc(self, x, w, bias=None, y=None, stream=None):
+        """conv2d_fwd_noalloc: as forward, with the library's fixed device
+        scratch as the workspace (no allocation in the library; ``y`` is
+        allocated here with torch only when not given)."""
+        self._tensor(x, self.x_shape(), "x")
+        self._tensor(w, self.w_shape(), "w")
+        self._tensor(bias, (self.params.K,), "bias")
+        y = self.new_output(x.device) if y is None else self._tensor(y, self.y_shape(), "y")
+        _check(self.lib.conv2d_fwd_noalloc(self._desc, self._ptr(x), self._ptr(w), self._ptr(bias), self._ptr(y),
+                                           self._stream(stream, x.device)), "conv2d_fwd_noalloc")
         return y
 
     def tune(self, x, w, bias=None, y=None, ws=None, reps=5, stream=None):

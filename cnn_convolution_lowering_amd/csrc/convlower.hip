@@ -9,6 +9,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
@@ -706,6 +707,35 @@ conv_status_t run_lstm(const conv_desc& d, const void* x, const void* h_prev, co
     return launch_status();
 }
 
+// ---------------------------------------------------------------- scratch of conv2d_fwd_noalloc
+
+// The workspace of conv2d_fwd_noalloc: a fixed array in device memory (each
+// GPU the library runs on holds its own copy until the process ends).  Its
+// name is a host-side stand-in, never a device address: host code only ever
+// uses the address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[CONV_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kScratchDevices = 64;
+std::atomic<void*> g_scratch[kScratchDevices];
+
+// This device's copy of `scratch`, looked up once per device with that
+// device current (the first call on it) and kept.
+conv_status_t scratch_ptr(void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return CONV_ERR_HIP;
+    if (dev < 0 || dev >= kScratchDevices) return CONV_ERR_UNSUPPORTED;
+    void* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return CONV_ERR_HIP;
+        }
+        g_scratch[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return CONV_OK;
+}
+
 }  // namespace
 
 // ====================================================================== C ABI
@@ -856,6 +886,27 @@ conv_status_t conv2d_fwd(conv_desc_t d, const void* x, const void* w, const void
     if ((s = check_dev(y, 16)) != CONV_OK) return s;
     if (bias && (s = check_dev(bias, size_t(d->elem))) != CONV_OK) return s;
     if ((s = check_ws(*d, ws)) != CONV_OK) return s;
+    if ((s = run_pack(*d, w, ws, st)) != CONV_OK) return s;
+    if ((s = run_lower(*d, x, ws, st)) != CONV_OK) return s;
+    return run_contract(*d, x, w, bias, y, ws, st);
+}
+
+conv_status_t conv2d_fwd_noalloc(conv_desc_t d, const void* x, const void* w, const void* bias, void* y,
+                                 void* stream) {
+    if (!desc_ok(d) || d->lstm_cx) return CONV_ERR_INVALID_ARG;
+    if (d->ws_bytes > CONV_NOALLOC_SCRATCH_BYTES) return CONV_ERR_UNSUPPORTED;
+    if (d->p.N == 0) return CONV_OK;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    conv_status_t s;
+    if ((s = check_dev(x, 16)) != CONV_OK) return s;
+    if ((s = check_dev(w, 16)) != CONV_OK) return s;
+    if ((s = check_dev(y, 16)) != CONV_OK) return s;
+    if (bias && (s = check_dev(bias, size_t(d->elem))) != CONV_OK) return s;
+    // Every kernel writes each workspace byte it reads before reading it
+    // (packed filters, lowered rows, split partial sums), so the scratch left
+    // by an earlier call needs no clearing.
+    void* ws = nullptr;
+    if (d->ws_bytes && (s = scratch_ptr(&ws)) != CONV_OK) return s;
     if ((s = run_pack(*d, w, ws, st)) != CONV_OK) return s;
     if ((s = run_lower(*d, x, ws, st)) != CONV_OK) return s;
     return run_contract(*d, x, w, bias, y, ws, st);

@@ -216,6 +216,27 @@ conv_status_t conv_plan_info(conv_desc_t d, conv_plan_info_t* info);
 conv_status_t conv2d_fwd(conv_desc_t d, const void* x, const void* w, const void* bias, void* y,
                          void* ws, void* stream);
 
+/* Workspace limit of conv2d_fwd_noalloc, in bytes (64 MiB). */
+#define CONV_NOALLOC_SCRATCH_BYTES (64ull << 20)
+
+/* conv2d_fwd for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * caller still passes x, w, bias and y (as for conv2d_fwd); the workspace is
+ * instead a fixed array of CONV_NOALLOC_SCRATCH_BYTES in device memory that
+ * the library holds on each GPU it runs on until the process ends (its address
+ * is looked up on the first call on a device).  No hipMalloc, hipFree or
+ * other allocating call is made.  Every call on one GPU shares that GPU's
+ * array: calls that overlap in time on one GPU (other streams, other
+ * threads) race on it and must not be issued; calls in sequence on one stream
+ * are safe (each kernel writes every scratch byte it reads before reading
+ * it, so nothing is cleared between calls).  Errors as conv2d_fwd, and
+ * CONV_ERR_UNSUPPORTED (nothing enqueued) when conv_workspace_size(d) exceeds
+ * CONV_NOALLOC_SCRATCH_BYTES (for scale: the fused path of a 3x3, 512- to
+ * 512-channel layer over 128 images of 7x7 keeps 26 MB of split-contraction
+ * partial sums; lowered im2win / im2col buffers of large layers exceed it). */
+conv_status_t conv2d_fwd_noalloc(conv_desc_t d, const void* x, const void* w, const void* bias, void* y,
+                                 void* stream);
+
 /* Stage 1 of conv2d_fwd: reorder w into the packed contraction operand
  * Bp[k][s*RCp + r*C + c] in ws (zeros in the RCp padding) -- the "reshaped
  * filter matrix" of "GPU-Accelerating MSCRED ...", section "Transforming
