@@ -105,19 +105,19 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) conv_strip_rb_kernel(GemmAr
               lds0 + uint32_t(buf * STRIP_ELEMS * sizeof(T)) + uint32_t((j * NT + wave * 64) * 16));
     };
     const int frag_chunk = lane >> 5;
-    auto read_a1 = [&](u32x4& fa, int i, int buf, int s, int kb) __attribute__((always_inline)) {
+    // Element offset of the lane's A fragment of the first 16-deep half of a
+    // step (strip buffer buf, tap s).  The second half's fragment is the
+    // next chunk pair of the same row: its swizzled chunk index differs in
+    // bit 1 only (the XOR mask touches bits 0-1 of the chunk, and the first
+    // half's chunk is 0 or 1), i.e. its offset is this one XOR 2*VEC (buffer
+    // starts are multiples of 2048 elements, rows of 4*VEC).  So each step
+    // computes one offset per fragment and the second half reuses it.
+    static_assert(STRIP_ELEMS % 2048 == 0, "offset bit 4 belongs to the chunk");
+    auto a_off = [&](int i, int buf, int s) __attribute__((always_inline)) {
         const int row = srow[i] + s * g.dw;
-        fa = load16(smem + buf * STRIP_ELEMS + (row * 4 + swz_chunk<4, 1>(row, kb * 2 + frag_chunk)) * VEC);
+        return buf * STRIP_ELEMS + (row * 4 + swz_chunk<4, 1>(row, frag_chunk)) * VEC;
     };
-    auto read_a = [&](u32x4 (&fa)[TM], int buf, int s, int kb) __attribute__((always_inline)) {
-        const T* sa = smem + buf * STRIP_ELEMS;
-        const int soff = s * g.dw;
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            const int row = srow[i] + soff;
-            fa[i] = load16(sa + (row * 4 + swz_chunk<4, 1>(row, kb * 2 + frag_chunk)) * VEC);
-        }
-    };
+    int aoff[TM];   // first-half offsets of the current step
     // Filter fragments of step position `kpos16` (contraction index / 16) for both halves.
     auto load_b = [&](u32x4 (&fb)[2][TN], int kpos16) __attribute__((always_inline)) {
 #pragma unroll
@@ -163,7 +163,11 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) conv_strip_rb_kernel(GemmAr
     lds_barrier();
 
     u32x4 fa0[TM], fa1[TM];
-    read_a(fa0, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        aoff[i] = a_off(i, 0, 0);
+        fa0[i] = load16(smem + aoff[i]);
+    }
 
     StepPos pc{0, 0, 0};      // step k
     int strip_k = 0;
@@ -192,14 +196,13 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) conv_strip_rb_kernel(GemmAr
         // Past the end the loads repeat position 0 into a set nobody reads:
         // unconditional loads keep the compiler's count of them exact.
         const int kpos_b = more ? ((pb.r * S + pb.s) * g.C + pb.cb * 32) / 16 : 0;
-        const int buf_k = strip_k & 1, s_k = pc.s;
         // ---- half 0
         static_for<NM>([&](auto idxc) __attribute__((always_inline)) {
             constexpr int idx = decltype(idxc)::value;
             constexpr int i = idx / TN, j = idx % TN;
             acc[i][j] = Mfma32<T>::run(fb[RC][0][j], fa0[i], acc[i][j]);
             if constexpr (idx < TM) {
-                read_a1(fa1[idx], idx, buf_k, s_k, 1);
+                fa1[idx] = load16(smem + (aoff[idx] ^ (2 * VEC)));
             } else if constexpr (idx < TM + TN) {
                 fb[RL][0][idx - TM] = buffer_load16(brsrc, bfrag[idx - TM], kpos_b * 1024);
             }
@@ -208,7 +211,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) conv_strip_rb_kernel(GemmAr
         static_for<(TM + TN > NM ? TM + TN - NM : 0)>([&](auto rc) __attribute__((always_inline)) {
             constexpr int idx = NM + decltype(rc)::value;
             if constexpr (idx < TM)
-                read_a1(fa1[idx], idx, buf_k, s_k, 1);
+                fa1[idx] = load16(smem + (aoff[idx] ^ (2 * VEC)));
             else
                 fb[RL][0][idx - TM] = buffer_load16(brsrc, bfrag[idx - TM], kpos_b * 1024);
         });
@@ -247,7 +250,8 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) conv_strip_rb_kernel(GemmAr
             constexpr int i = idx / TN, j = idx % TN;
             acc[i][j] = Mfma32<T>::run(fb[RC][1][j], fa1[i], acc[i][j]);
             if constexpr (idx < TM) {
-                read_a1(fa0[idx], idx, buf_n, s_n, 0);
+                aoff[idx] = a_off(idx, buf_n, s_n);
+                fa0[idx] = load16(smem + aoff[idx]);
             } else if constexpr (idx < TM + TN) {
                 fb[RL][1][idx - TM] = buffer_load16(brsrc, bfrag[idx - TM], (kpos_b + 1) * 1024);
             } else if constexpr (idx - TM - TN < NLA) {
@@ -257,9 +261,10 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 1) conv_strip_rb_kernel(GemmAr
         });
         static_for<(TM + TN + NLA > NM ? TM + TN + NLA - NM : 0)>([&](auto rc) __attribute__((always_inline)) {
             constexpr int idx = NM + decltype(rc)::value;
-            if constexpr (idx < TM)
-                read_a1(fa0[idx], idx, buf_n, s_n, 0);
-            else if constexpr (idx < TM + TN)
+            if constexpr (idx < TM) {
+                aoff[idx] = a_off(idx, buf_n, s_n);
+                fa0[idx] = load16(smem + aoff[idx]);
+            } else if constexpr (idx < TM + TN)
                 fb[RL][1][idx - TM] = buffer_load16(brsrc, bfrag[idx - TM], (kpos_b + 1) * 1024);
             else if (do_strip)
                 strip_load(next_strip & 1, idx - TM - TN, nsr, ncb);
