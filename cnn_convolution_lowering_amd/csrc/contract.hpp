@@ -13,6 +13,7 @@
 #include "igemm_nchw_tile.hpp"
 #include "igemm_strip.hpp"
 #include "igemm_strip_rb.hpp"
+#include "igemm_streamk.hpp"
 #include "igemm_tile16.hpp"
 #include "igemm_wide.hpp"
 
@@ -112,6 +113,38 @@ void launch_dma_tile(const conv_desc& d, const GemmArgs& g, hipStream_t st) {
     }
 }
 
+// The stream-K form of one pipelined tile shape (its operand sources as in
+// launch_dma_tile): sk_grid persistent workgroups; sum slots and flags in the
+// workspace's partial area.
+template <typename T, int BM, int BN, int BK, int WGM, int WGN, int STAGES>
+void launch_streamk_tile(const conv_desc& d, GemmArgs g, uint32_t epoch, hipStream_t st) {
+    constexpr int NT = 64 * WGM * WGN;
+    using B = DmaRows<T, BN, BK, false, false, NT>;
+    g.tiles_n = int32_t((d.p.K + BN - 1) / BN);
+    StreamKArgs sk;
+    sk.part = static_cast<float*>(g.part);
+    sk.flags = reinterpret_cast<uint32_t*>(sk.part + int64_t(d.sk_grid) * BM * BN);
+    sk.epoch = epoch;
+    sk.tiles = int32_t(((d.M + BM - 1) / BM) * g.tiles_n);
+    sk.nkt = int32_t((g.Kc + BK - 1) / BK);
+    sk.grid = d.sk_grid;
+    const bool nhwc = d.p.layout == CONV_NHWC;
+    const dim3 grid(uint32_t(d.sk_grid));
+    if (d.p.algo == CONV_ALGO_IMPLICIT) {
+        // NHWC windows of whole BK-channel blocks (checked when planning)
+        conv_gemm_streamk_kernel<T, BM, BN, BK, WGM, WGN, STAGES, true, DmaWindowNHWCBlocked<T, BM, BK, NT>, B>
+            <<<grid, NT, 0, st>>>(g, sk);
+    } else if (!d.elided && d.p.algo == CONV_ALGO_IM2WIN) {
+        using A = DmaRows<T, BM, BK, true, true, NT>;
+        if (nhwc) conv_gemm_streamk_kernel<T, BM, BN, BK, WGM, WGN, STAGES, true, A, B><<<grid, NT, 0, st>>>(g, sk);
+        else conv_gemm_streamk_kernel<T, BM, BN, BK, WGM, WGN, STAGES, false, A, B><<<grid, NT, 0, st>>>(g, sk);
+    } else {
+        using A = DmaRows<T, BM, BK, true, false, NT>;
+        if (nhwc) conv_gemm_streamk_kernel<T, BM, BN, BK, WGM, WGN, STAGES, true, A, B><<<grid, NT, 0, st>>>(g, sk);
+        else conv_gemm_streamk_kernel<T, BM, BN, BK, WGM, WGN, STAGES, false, A, B><<<grid, NT, 0, st>>>(g, sk);
+    }
+}
+
 // The split contraction's reduction (after the contraction on the same
 // stream); nothing without a split.
 template <typename T>
@@ -126,11 +159,11 @@ void launch_split_reduce(const conv_desc& d, const GemmArgs& g, const void* bias
 
 template <typename T>
 void launch_gemm(const conv_desc& d, const void* x, const void* w, const void* bias, void* y, const void* ws,
-                 hipStream_t st) {
+                 uint32_t epoch, hipStream_t st) {
     const char* wsb = static_cast<const char*>(ws);
     GemmArgs g{};
     g.ksplit = d.ksplit;
-    g.part = d.ksplit > 1 ? static_cast<void*>(const_cast<char*>(wsb) + d.off_part) : nullptr;
+    g.part = d.bytes_part ? static_cast<void*>(const_cast<char*>(wsb) + d.off_part) : nullptr;
     g.b = (d.pack || d.frag_pack) ? static_cast<const void*>(wsb + d.off_filter) : w;
     g.bias = bias;
     g.y = y;
@@ -220,6 +253,20 @@ void launch_gemm(const conv_desc& d, const void* x, const void* w, const void* b
     }
     // BK of a variant is given for 16-bit storage; fp32 rows of the same bytes hold half as many elements.
     constexpr int DIV = sizeof(T) == 4 ? 2 : 1;
+    if (d.kernel == KERN_STREAMK) {
+#define CONVLOWER_SK_CASE(I)                                                                        \
+    case I: {                                                                                       \
+        constexpr TileVariant v = kDmaVariants[I];                                                  \
+        launch_streamk_tile<T, v.bm, v.bn, v.bk / DIV, v.wgm, v.wgn, v.stages>(d, g, epoch, st);   \
+        break;                                                                                      \
+    }
+        switch (d.variant) {
+            CONVLOWER_SK_CASE(8)
+            default: break;
+        }
+#undef CONVLOWER_SK_CASE
+        return;
+    }
     if (d.kernel == KERN_DMA) {
 #define CONVLOWER_DMA_CASE(I)                                                                     \
     case I: {                                                                                     \

@@ -2,6 +2,6 @@
 #include "contract.hpp"
 
 namespace convlower {
-template void launch_gemm<__bf16>(const conv_desc&, const void*, const void*, const void*, void*, const void*,
+template void launch_gemm<__bf16>(const conv_desc&, const void*, const void*, const void*, void*, const void*, uint32_t,
                               hipStream_t);
 }  // namespace convlower

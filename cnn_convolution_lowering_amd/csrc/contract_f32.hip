@@ -2,7 +2,7 @@
 #include "contract.hpp"
 
 namespace convlower {
-template void launch_gemm<float>(const conv_desc&, const void*, const void*, const void*, void*, const void*,
+template void launch_gemm<float>(const conv_desc&, const void*, const void*, const void*, void*, const void*, uint32_t,
                               hipStream_t);
 
 // The contraction of a ConvLSTM step (fp32 NCHW, lowered input in ws, gate

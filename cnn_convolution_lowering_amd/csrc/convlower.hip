@@ -42,6 +42,14 @@ conv_status_t from_hip(hipError_t e) { return e == hipSuccess ? CONV_OK : CONV_E
 
 // ---------------------------------------------------------------- planning
 
+// The pipelined tile shape compiled in stream-K form: 128 x 128 over eight
+// waves, early issue (variant 8), whose registers (at most 128 per lane with
+// the blocked window loader or lowered rows) leave two workgroups per CU.
+bool streamk_variant(int v) {
+    return v >= 0 && v < count_of(kDmaVariants) && kDmaVariants[v].bm == 128 && kDmaVariants[v].bn == 128 &&
+           kDmaVariants[v].early == 1 && kDmaVariants[v].wgm * kDmaVariants[v].wgn == 8;
+}
+
 // force: "<kernel>:<variant>[:<ksplit>]" (conv_create_desc_forced, conv_tune),
 // or nullptr for the default choice.
 conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force) {
@@ -234,6 +242,13 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force) {
     // Forced choice "<kernel>:<variant>[:<ksplit>]" with kernel one of the
     // names in kKernelFamilies, applied where that kernel takes this
     // convolution (ksplit: the pipelined DMA kernel's contraction split).
+    // Stream-K operands: lowered rows, or windows of whole stage-deep channel
+    // blocks (the blocked loader; the other one needs more registers than two
+    // workgroups per CU allow).
+    auto sk_operands = [&](int v) {
+        const int64_t bk = p.dtype == CONV_F32 ? kDmaVariants[v].bk / 2 : kDmaVariants[v].bk;
+        return !implicit || p.C % bk == 0;
+    };
     int force_ks = 0;
     if (const char* v = force) {
         const char* colon = std::strchr(v, ':');
@@ -273,6 +288,9 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force) {
             } else if (name == "nchw" && nchw_ok && i >= 0 && i < count_of(kNchwVariants)) {
                 d.kernel = KERN_NCHW;
                 d.variant = i;
+            } else if (name == "streamk" && dma_ok && !nchw_ok && streamk_variant(i) && sk_operands(i)) {
+                d.kernel = KERN_STREAMK;
+                d.variant = i;
             }
         }
     }
@@ -285,6 +303,28 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force) {
     // cost a write and a read of ksplit*M*K*4 bytes.  Every split non-empty.
     // (The wide-tile kernel splits only when forced, or when conv_tune keeps
     // such a plan.)
+    // Stream-K (the 128 x 128 pipelined tiles over a persistent grid of two
+    // workgroups per CU, every workgroup the same share of (tile, step)
+    // pairs) is taken only when forced or kept by conv_tune: on the layers
+    // whose tiles fill the GPU unevenly (3x3 at 14x14 with 256 channels, 1x1
+    // with 1024 input channels) it measured 1.3 to 1.45 times slower than one
+    // workgroup per tile.  Its rate on evenly divided layers matches the
+    // plain kernel, so the loss is in the split tiles: the pieces of a tile
+    // run at different contraction offsets at once and no longer share the
+    // window rows they read through L2.
+    const auto sk_shape = [&](int v, int64_t& tiles, int64_t& nkt) {
+        const TileVariant& tv = kDmaVariants[v];
+        const int64_t bk = p.dtype == CONV_F32 ? tv.bk / 2 : tv.bk;
+        tiles = ((d.M + tv.bm - 1) / tv.bm) * ((p.K + tv.bn - 1) / tv.bn);
+        nkt = ((implicit ? d.Kg : d.Kl) + bk - 1) / bk;
+    };
+    const int64_t sk_cap = kStreamKCus * kStreamKPerCu;
+    d.sk_grid = 0;
+    if (d.kernel == KERN_STREAMK) {
+        int64_t tiles = 0, nkt = 0;
+        sk_shape(d.variant, tiles, nkt);
+        d.sk_grid = int32_t(std::max<int64_t>(1, std::min<int64_t>(tiles * nkt, sk_cap)));
+    }
     d.ksplit = 1;
     if (d.kernel == KERN_DMA || d.kernel == KERN_WIDE) {
         const TileVariant& tv = d.kernel == KERN_DMA ? kDmaVariants[d.variant] : kWideVariants[d.variant];
@@ -324,10 +364,10 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force) {
         d.tile_n = sv.bn;
         d.tile_k = 32;
     } else {
-        const TileVariant& tv = d.kernel == KERN_NCHW ? kNchwVariants[d.variant]
-                                : d.kernel == KERN_WIDE ? kWideVariants[d.variant]
-                                : d.kernel == KERN_DMA  ? kDmaVariants[d.variant]
-                                                        : kRegVariants[d.variant];
+        const TileVariant& tv = d.kernel == KERN_NCHW                            ? kNchwVariants[d.variant]
+                                : d.kernel == KERN_WIDE                          ? kWideVariants[d.variant]
+                                : d.kernel == KERN_DMA || d.kernel == KERN_STREAMK ? kDmaVariants[d.variant]
+                                                                                   : kRegVariants[d.variant];
         d.tile_m = tv.bm;
         d.tile_n = tv.bn;
         d.tile_k = d.kernel == KERN_NCHW ? tv.bk : (p.dtype == CONV_F32 ? tv.bk / 2 : tv.bk);
@@ -348,9 +388,12 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force) {
         d.ws_bytes = p.N == 0 ? 0 : d.bytes_filter;
     }
 
-    // The split contraction's fp32 partials go last in the workspace.
+    // The split contraction's fp32 partials, or the stream-K sum slots and
+    // their flags, go last in the workspace.
     d.off_part = 0;
     d.bytes_part = d.ksplit > 1 ? uint64_t(d.ksplit) * uint64_t(d.M) * uint64_t(p.K) * 4 : 0;
+    if (d.kernel == KERN_STREAMK)
+        d.bytes_part = uint64_t(d.sk_grid) * uint64_t(d.tile_m) * uint64_t(d.tile_n) * 4 + uint64_t(d.sk_grid) * 4;
     if (d.bytes_part && p.N > 0) {
         d.off_part = round_up(d.ws_bytes, kWsAlign);
         d.ws_bytes = d.off_part + d.bytes_part;
@@ -417,6 +460,7 @@ constexpr KernelFamily kKernelFamilies[] = {
     {"nchwstrip", KERN_NCHW_STRIP, count_of(kNchwStripVariants)},
     {"nchwtile", KERN_NCHW_TILE, count_of(kNchwTileVariants)},
     {"tile16", KERN_TILE16, count_of(kTile16Variants)},
+    {"streamk", KERN_STREAMK, count_of(kDmaVariants)},
 };
 
 // A ConvLSTM step: the gate convolution over concat(x, h) of p (C = c_x +
@@ -660,10 +704,19 @@ struct LowerOp {
 template <typename T>
 struct GemmOp {
     static void run(const conv_desc& d, const void* x, const void* w, const void* bias, void* y, const void* ws,
-                    hipStream_t st) {
-        launch_gemm<T>(d, x, w, bias, y, ws, st);
+                    uint32_t epoch, hipStream_t st) {
+        launch_gemm<T>(d, x, w, bias, y, ws, epoch, st);
     }
 };
+
+// Launch epochs (stream-K flags): one counter for the process, so that no
+// two launches sharing a workspace use the same value; 0 is never used.
+std::atomic<uint32_t> g_epoch{0};
+uint32_t next_epoch() {
+    uint32_t e = g_epoch.fetch_add(1, std::memory_order_relaxed) + 1;
+    while (e == 0) e = g_epoch.fetch_add(1, std::memory_order_relaxed) + 1;
+    return e;
+}
 
 conv_status_t launch_status() { return from_hip(hipGetLastError()); }
 
@@ -688,7 +741,7 @@ conv_status_t run_lower(const conv_desc& d, const void* x, void* ws, hipStream_t
 conv_status_t run_contract(const conv_desc& d, const void* x, const void* w, const void* bias, void* y,
                            const void* ws, hipStream_t st) {
     if (d.p.N == 0) return CONV_OK;
-    by_dtype<GemmOp>(d.p.dtype, d, x, w, bias, y, ws, st);
+    by_dtype<GemmOp>(d.p.dtype, d, x, w, bias, y, ws, next_epoch(), st);
     return launch_status();
 }
 

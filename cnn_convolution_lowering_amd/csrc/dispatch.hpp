@@ -19,6 +19,8 @@ enum KernelId : int32_t {
     KERN_NCHW_STRIP = 6,  // fp32 NCHW strips (16-byte row loads), register-streamed filter (pad_w == 0, C % 16 == 0)
     KERN_NCHW_TILE = 7,   // fp32 NCHW small windows: input rows staged once per block of output rows, filter in registers
     KERN_TILE16 = 8,      // 16-bit NHWC small windows: the same staging, window rows read as contiguous runs
+    KERN_STREAMK = 9,     // the LDS-DMA pipeline (a kDmaVariants shape) in stream-K form: equal contraction
+                          // ranges per workgroup of a persistent grid, split tiles summed from workspace slots
 };
 
 // One compiled tile shape: BM x BN output tile, BK-deep LDS stages (in 16-bit
@@ -133,8 +135,11 @@ struct conv_desc {
     int64_t lstm_cx;    // ConvLSTM step descriptor: input channels taken from x (0: a plain convolution)
     // Split contraction (pipelined DMA kernel): ksplit ranges of the
     // contraction per output tile, fp32 partials [ksplit][M*K] in ws at off_part.
+    // Stream-K (KERN_STREAMK): sk_grid workgroups, their sum slots
+    // [sk_grid][BM*BN] fp32 then sk_grid flags at off_part (bytes_part in all).
     int32_t ksplit;
     uint64_t off_part, bytes_part;
+    int32_t sk_grid;
     // Band lowering (NCHW input, or NHWC with C not a whole number of
     // vectors): output rows (band_g) and output columns (band_cw) per item,
     // staged input rows and columns, LDS row and channel pitch (elements) and
@@ -145,20 +150,25 @@ struct conv_desc {
 
 namespace convlower {
 
+// Workgroups resident per CU for the stream-K grid, and the CUs it covers.
+constexpr int64_t kStreamKCus = 256;
+constexpr int64_t kStreamKPerCu = 2;
+
 // Enqueue the contraction (with its fused epilogue) for storage type T.
+// epoch: a value no earlier launch used (the stream-K flags).
 template <typename T>
 void launch_gemm(const conv_desc& d, const void* x, const void* w, const void* bias, void* y, const void* ws,
-                 hipStream_t st);
+                 uint32_t epoch, hipStream_t st);
 
 // The contraction of a ConvLSTM step with its cell-update epilogue (fp32).
 void launch_lstm_gemm(const conv_desc& d, const void* bias, const void* c_prev, void* h_out, void* c_out,
                       const void* ws, hipStream_t st);
 
 extern template void launch_gemm<float>(const conv_desc&, const void*, const void*, const void*, void*,
-                                        const void*, hipStream_t);
+                                        const void*, uint32_t, hipStream_t);
 extern template void launch_gemm<_Float16>(const conv_desc&, const void*, const void*, const void*, void*,
-                                           const void*, hipStream_t);
+                                           const void*, uint32_t, hipStream_t);
 extern template void launch_gemm<__bf16>(const conv_desc&, const void*, const void*, const void*, void*,
-                                         const void*, hipStream_t);
+                                         const void*, uint32_t, hipStream_t);
 
 }  // namespace convlower

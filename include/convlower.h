@@ -127,8 +127,14 @@ typedef struct {
      * 8 16-bit NHWC small windows (the stem layers: C*sw and W*C even, unit
      * horizontal dilation, K <= 64): the same staging, each filter row's
      * window part read as one contiguous run, filter in registers from a
-     * copy in MFMA fragment order;
-     * kernel_variant indexes that kernel's compiled tile shapes */
+     * copy in MFMA fragment order, 9 the LDS-DMA pipeline of 1 in stream-K
+     * form: a persistent grid whose workgroups take equal ranges of the
+     * (tile, contraction step) pairs, a tile split between workgroups summed
+     * in contraction order from fp32 slots in the workspace's partial area
+     * (one tile_m*tile_n slot and one flag per workgroup), taken only when
+     * named (conv_create_desc_forced) or kept by conv_tune;
+     * kernel_variant indexes that kernel's compiled tile shapes (for 9 the
+     * shapes of 1) */
     int32_t kernel, kernel_variant;
     /* split contraction (kernels 1 and 2): ksplit workgroups share each output
      * tile, each over a contiguous range of the contraction, their fp32
@@ -155,8 +161,8 @@ conv_status_t conv_create_desc(const conv_params_t* p, conv_desc_t* out);
 
 /* As conv_create_desc, with the contraction kernel named explicitly: plan is
  * "<kernel>:<variant>" or "<kernel>:<variant>:<ksplit>" with kernel one of
- * reg, dma, wide, nchw, strip, striprb, nchwstrip, nchwtile, tile16 (the
- * numbering of conv_plan_info_t.kernel, in that order) and variant an index
+ * reg, dma, wide, nchw, strip, striprb, nchwstrip, nchwtile, tile16, streamk
+ * (the numbering of conv_plan_info_t.kernel, in that order) and variant an index
  * into that kernel's compiled tile shapes; ksplit (1-8) splits the
  * contraction of the dma and wide kernels.  "GPU-Accelerating MSCRED ...",
  * section "Engineering Challenges" (kernel configuration: thread-block

@@ -226,6 +226,7 @@ def test_implicit_needs_no_workspace(layout, dtype):
         assert c.info["ws_lowered_bytes"] == 0 and c.info["lowering_elided"] == 1
         # besides the filter copy, a split contraction's fp32 partials (not lowered input)
         part = c.info["ws_partial_bytes"]
+        assert c.info["kernel"] != 9   # stream-K only when named
         assert part == (c.info["ksplit"] * c.info["M"] * 16 * 4 if c.info["ksplit"] > 1 else 0)
         assert c.workspace_bytes == (c.info["ws_partial_offset"] + part if part else c.info["ws_filter_bytes"])
         elem = {"f32": 4, "f16": 2, "bf16": 2}[dtype]
@@ -242,6 +243,10 @@ def test_implicit_needs_no_workspace(layout, dtype):
 def test_elided_layers_use_no_lowering_workspace():
     c = cl.Conv2d(128, 1024, 14, 14, 256, 1, 1, layout="nhwc", dtype="bf16")
     assert c.info["lowering_elided"] == 1 and c.workspace_bytes == 0
+    # named stream-K: its sum slots are the only workspace
+    c = cl.Conv2d(128, 1024, 14, 14, 256, 1, 1, layout="nhwc", dtype="bf16", plan="streamk:8")
+    assert c.info["kernel"] == 9 and c.info["ws_lowered_bytes"] == 0
+    assert c.workspace_bytes == c.info["ws_partial_offset"] + c.info["ws_partial_bytes"]
     c = cl.Conv2d(32, 128, 64, 64, 128, 1, 1, layout="nhwc", dtype="f16", algo="im2col")
     assert c.workspace_bytes == 0
 
@@ -392,3 +397,44 @@ def test_peak_library_exports_and_host_checks():
     assert lib.convpeak_copy(ctypes.c_void_p((1 << 20) + 8), fake, 32, None) == -1      # misaligned
     assert lib.convpeak_copy(fake, ctypes.c_void_p((1 << 20) + 16), 64, None) == -1    # overlapping
     assert lib.convpeak_copy(fake, ctypes.c_void_p(1 << 24), 0, None) == 0             # nothing to copy
+
+
+def test_streamk_plan():
+    """Stream-K is taken only when named ("streamk:8", the 128 x 128
+    pipelined tiles with early issue) and where its operands allow it; its
+    workspace's partial area is one fp32 tile slot and one flag per workgroup
+    of a grid of min(tile steps, 512), after the other parts.  The default
+    plan of the same layers is the plain pipeline."""
+    cases = [((64, 256, 14, 14, 256, 3, 3, 1), "f16", 196 * 36), ((128, 512, 7, 7, 512, 3, 3, 1), "bf16", 196 * 72),
+             ((128, 1024, 14, 14, 256, 1, 1, 0), "bf16", 392 * 16)]
+    for a, dt, units in cases:
+        for algo in ("implicit", "im2win", "im2col"):
+            c = cl.Conv2d(*a[:7], padding=a[7], layout="nhwc", dtype=dt, algo=algo)
+            assert c.info["kernel"] == 1, (a, algo)
+            c = cl.Conv2d(*a[:7], padding=a[7], layout="nhwc", dtype=dt, algo=algo, plan="streamk:8")
+            i = c.info
+            assert (i["kernel"], i["kernel_variant"], i["ksplit"]) == (9, 8, 1), (a, algo)
+            grid = min(units, 512)
+            assert i["ws_partial_bytes"] == grid * 128 * 128 * 4 + grid * 4
+            assert i["ws_partial_offset"] % 256 == 0
+            assert c.workspace_bytes == i["ws_partial_offset"] + i["ws_partial_bytes"]
+            low = i["ws_lowered_bytes"]
+            if low:
+                assert i["ws_partial_offset"] >= i["ws_lowered_offset"] + low
+    c = cl.Conv2d(32, 128, 64, 64, 128, 3, 3, padding=1, layout="nhwc", dtype="f16", algo="implicit")
+    assert c.info["kernel"] == 1 and c.info["ws_partial_bytes"] == 0
+    c = cl.Conv2d(64, 256, 14, 14, 256, 3, 3, padding=1, layout="nhwc", dtype="f16", algo="implicit", plan="dma:8")
+    assert (c.info["kernel"], c.info["ksplit"], c.info["ws_partial_bytes"]) == (1, 1, 0)
+    c = cl.Conv2d(2, 64, 17, 17, 72, 3, 3, padding=1, layout="nhwc", dtype="f16", algo="implicit", plan="streamk:8")
+    assert c.info["kernel"] == 9 and c.info["ws_partial_bytes"] == 5 * 9 * 128 * 128 * 4 + 5 * 9 * 4
+    # windows whose channels are not whole 64-element stage blocks, fp32 NCHW windows, other shapes: not taken
+    for kw in (dict(C=96), dict(layout="nchw", dtype="f32")):
+        args = dict(C=64, layout="nhwc", dtype="f16")
+        args.update(kw)
+        c = cl.Conv2d(2, args["C"], 17, 17, 72, 3, 3, padding=1, layout=args["layout"], dtype=args["dtype"],
+                      algo="implicit", plan="streamk:8")
+        assert c.info["kernel"] != 9, kw
+    for v in (0, 7, 9, 10, 11):
+        c = cl.Conv2d(2, 64, 17, 17, 72, 3, 3, padding=1, layout="nhwc", dtype="f16", algo="implicit",
+                      plan="streamk:%d" % v)
+        assert c.info["kernel"] != 9, v

@@ -22,7 +22,9 @@ from parity import TORCH_DT, assert_parity, to_f64
 pytestmark = pytest.mark.gpu
 
 # kernel name -> (plan_info kernel id, number of compiled variants)
-KERNELS = {"reg": (0, 3), "dma": (1, 12), "wide": (2, 9), "nchw": (3, 12), "strip": (4, 5), "striprb": (5, 7), "nchwstrip": (6, 10), "nchwtile": (7, 6), "tile16": (8, 11)}
+KERNELS = {"reg": (0, 3), "dma": (1, 12), "wide": (2, 9), "nchw": (3, 12), "strip": (4, 5), "striprb": (5, 7), "nchwstrip": (6, 10), "nchwtile": (7, 6), "tile16": (8, 11), "streamk": (9, 12)}
+# kernels compiled for some variants only
+VARIANTS = {"streamk": (8,)}
 
 # (N, C, H, W, K, R, S, stride, pad, dilation)
 SHAPES_C32 = [
@@ -93,13 +95,20 @@ PLANS = [
     ("nchwtile", "f32", "nchw", "implicit", SHAPES_SMALL_KG),
     ("tile16", "bf16", "nhwc", "implicit", SHAPES_TILE16),
     ("tile16", "f16", "nhwc", "implicit", SHAPES_TILE16),
+    # stream-K: few tiles and short contractions, so that nearly every tile is
+    # split between workgroups, some over three or more
+    ("streamk", "f16", "nhwc", "implicit", SHAPES_C32 + SHAPES_SMALL_C[1:]),
+    ("streamk", "bf16", "nhwc", "im2win", SHAPES_C32[:3] + SHAPES_SMALL_C[:1]),
+    ("streamk", "f16", "nhwc", "im2col", SHAPES_C32[:2]),
+    ("streamk", "f32", "nhwc", "implicit", SHAPES_C32[:2]),
+    ("streamk", "bf16", "nchw", "im2win", SHAPES_SMALL_C[:2]),
 ]
 
 
 def _cases():
     out = []
     for kind, dt, lay, algo, shapes in PLANS:
-        for v in range(KERNELS[kind][1]):
+        for v in VARIANTS.get(kind, range(KERNELS[kind][1])):
             out.append((kind, v, dt, lay, algo, shapes))
     return out
 
