@@ -54,12 +54,13 @@ class PlanInfo(ctypes.Structure):
                 ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32), ("tile_k", ctypes.c_int32),
                 ("elem_bytes", ctypes.c_int32), ("kernel", ctypes.c_int32), ("kernel_variant", ctypes.c_int32),
                 ("ws_partial_offset", ctypes.c_uint64), ("ws_partial_bytes", ctypes.c_uint64),
-                ("ksplit", ctypes.c_int32)]
+                ("ksplit", ctypes.c_int32), ("tile_order", ctypes.c_int32)]
 
 
 class TuneResult(ctypes.Structure):
     _fields_ = [("candidates", ctypes.c_int32), ("kernel", ctypes.c_int32), ("kernel_variant", ctypes.c_int32),
-                ("default_ms", ctypes.c_float), ("best_ms", ctypes.c_float), ("ksplit", ctypes.c_int32)]
+                ("default_ms", ctypes.c_float), ("best_ms", ctypes.c_float), ("ksplit", ctypes.c_int32),
+                ("tile_order", ctypes.c_int32)]
 
 
 _lib = None
@@ -140,9 +141,10 @@ def _dtype_name(t) -> str:
 class Conv2d:
     """One convolution descriptor (a plan); immutable once created.
 
-    ``plan`` asks for a contraction kernel explicitly ("<kernel>:<variant>"
-    or "<kernel>:<variant>:<ksplit>", conv_create_desc_forced): for tests and
-    tuning; None is the library's default choice."""
+    ``plan`` asks for a contraction kernel explicitly ("<kernel>:<variant>",
+    "<kernel>:<variant>:<ksplit>" or "<kernel>:<variant>:<ksplit>:<tile order>",
+    conv_create_desc_forced): for tests and tuning; None is the library's
+    default choice."""
 
     def __init__(self, N, C, H, W, K, R, S, *, stride=1, padding=0, dilation=1, layout="nchw",
                  dtype="f32", algo="im2win", plan: Optional[str] = None, _handle=None):

@@ -17,6 +17,11 @@
 #include "igemm_tile16.hpp"
 #include "igemm_wide.hpp"
 
+static_assert(convlower::TILE_ORDER_LINEAR == CONV_TILE_LINEAR && convlower::TILE_ORDER_XCD_ROWS == CONV_TILE_XCD_ROWS &&
+                  convlower::TILE_ORDER_XCD_SERPENT == CONV_TILE_XCD_SERPENT &&
+                  convlower::TILE_ORDER_XCD_COLS == CONV_TILE_XCD_COLS,
+              "tile order numbering");
+
 namespace convlower {
 
 template <typename T, int BM, int BN, int BK, int WGM, int WGN, bool NHWC_OUT, class ALoad, class BLoad>
@@ -163,6 +168,7 @@ void launch_gemm(const conv_desc& d, const void* x, const void* w, const void* b
     const char* wsb = static_cast<const char*>(ws);
     GemmArgs g{};
     g.ksplit = d.ksplit;
+    g.tile_order = d.tile_order;
     g.part = d.bytes_part ? static_cast<void*>(const_cast<char*>(wsb) + d.off_part) : nullptr;
     g.b = (d.pack || d.frag_pack) ? static_cast<const void*>(wsb + d.off_filter) : w;
     g.bias = bias;

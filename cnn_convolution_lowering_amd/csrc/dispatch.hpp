@@ -140,6 +140,7 @@ struct conv_desc {
     int32_t ksplit;
     uint64_t off_part, bytes_part;
     int32_t sk_grid;
+    int32_t tile_order;   // pipelined kernel: conv_tile_order_t
     // Band lowering (NCHW input, or NHWC with C not a whole number of
     // vectors): output rows (band_g) and output columns (band_cw) per item,
     // staged input rows and columns, LDS row and channel pitch (elements) and

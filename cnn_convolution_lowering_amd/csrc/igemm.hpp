@@ -59,10 +59,58 @@ struct GemmArgs {
     // each storing fp32 partial sums in the output layout at part + z*M*K.
     int32_t ksplit;
     void* part;
+    // Order in which the pipelined kernel's workgroups take the (split,
+    // output tile) pairs: TileOrder.
+    int32_t tile_order;
     // window loaders: the convolution itself
     int32_t C, H, W, R, S;
     int32_t sh, sw, ph, pw, dh, dw;
 };
+
+// Workgroup -> (split z, tile row, tile column) of the pipelined kernel.
+// The GPU deals workgroups to its eight XCDs (each with its own L2) round
+// robin by linear index, so in the plain order consecutive tiles, which share
+// an input panel, land on different XCDs.  The other orders give each XCD one
+// contiguous range of the (z, tile row, tile column) sequence, so that the
+// tiles an XCD runs at once share input and filter panels in its L2:
+//   TILE_ORDER_XCD_ROWS     the range in row-major order (tile column fastest);
+//   TILE_ORDER_XCD_SERPENT  the same, odd tile rows taken right to left, so
+//                           that consecutive tiles always share a panel;
+//   TILE_ORDER_XCD_COLS     the range in column-major order (tile row fastest).
+// ("Enabling Memory-efficient Im2win Convolution ...", abstract: the order
+// of memory accesses as a tuning dimension; "GPU-Accelerating MSCRED ...",
+// section "Future Work": further tile and thread-block configurations.)
+enum TileOrder : int32_t { TILE_ORDER_LINEAR = 0, TILE_ORDER_XCD_ROWS = 1, TILE_ORDER_XCD_SERPENT = 2,
+                           TILE_ORDER_XCD_COLS = 3 };
+constexpr int kTileOrders = 4;
+constexpr int kXcds = 8;
+
+struct TileCoord {
+    int m, n, z;
+};
+
+__device__ __forceinline__ TileCoord tile_coord(const GemmArgs& g, int tiles_m) {
+    const int tiles = tiles_m * g.tiles_n;
+    int pos = int(blockIdx.x) + int(blockIdx.y) * int(gridDim.x);
+    if (g.tile_order != TILE_ORDER_LINEAR) {
+        const int total = tiles * int(gridDim.y);
+        const int x = pos % kXcds, i = pos / kXcds;
+        const int q = total / kXcds, r = total - q * kXcds;
+        pos = x * q + (x < r ? x : r) + i;   // XCD x: [x*q + min(x, r), +q + (x < r))
+    }
+    TileCoord c;
+    c.z = pos / tiles;
+    const int t = pos - c.z * tiles;
+    if (g.tile_order == TILE_ORDER_XCD_COLS) {
+        c.n = t / tiles_m;
+        c.m = t - c.n * tiles_m;
+    } else {
+        c.m = t / g.tiles_n;
+        c.n = t - c.m * g.tiles_n;
+        if (g.tile_order == TILE_ORDER_XCD_SERPENT && (c.m & 1)) c.n = g.tiles_n - 1 - c.n;
+    }
+    return c;
+}
 
 template <typename T>
 struct Mfma;

@@ -317,24 +317,23 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 8 / (WGM * WGN)) conv_gemm_dma
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WGN, wn = wave - (wave / WGN) * WGN;
-    const int tile_m = blockIdx.x / g.tiles_n;
-    const int tile_n = blockIdx.x - tile_m * g.tiles_n;
-    const int64_t m0 = int64_t(tile_m) * BM;
-    const int n0 = tile_n * BN;
+    const TileCoord tc = tile_coord(g, int((g.M + BM - 1) / BM));
+    const int64_t m0 = int64_t(tc.m) * BM;
+    const int n0 = tc.n * BN;
 
     ASrc la;
     BSrc lb;
     la.init(g, m0, tid);
     lb.init(g, n0, tid);
 
-    // Split contraction (ksplit > 1): workgroup z = blockIdx.y takes the
+    // Split contraction (ksplit > 1): the workgroup of split z takes the
     // contraction tiles [z*per, min(nkt, (z+1)*per)); the loaders start there.
     // An empty range stores zeros.
     const int nkt_all = (g.Kc + BK - 1) / BK;
     int nkt = nkt_all;
     if (g.ksplit > 1) {
         const int per = (nkt_all + g.ksplit - 1) / g.ksplit;
-        const int kt0 = int(blockIdx.y) * per;
+        const int kt0 = tc.z * per;
         nkt = nkt_all - kt0 < per ? nkt_all - kt0 : per;
         for (int i = 0; i < kt0; ++i) {
             la.next(g);
@@ -426,7 +425,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 8 / (WGM * WGN)) conv_gemm_dma
     } else if (g.ksplit > 1) {
         // this split's fp32 partial sums, no bias, in the output layout
         GemmArgs h = g;
-        h.y = static_cast<float*>(g.part) + int64_t(blockIdx.y) * g.M * g.K;
+        h.y = static_cast<float*>(g.part) + int64_t(tc.z) * g.M * g.K;
         h.bias = nullptr;
         store_tile<float, BM, BN, WM, WN, TM, TN, NHWC_OUT>(h, acc, m0, n0, wm, wn, lane);
     } else {

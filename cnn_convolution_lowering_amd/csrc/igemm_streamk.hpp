@@ -78,7 +78,16 @@ __global__ void __launch_bounds__(64 * WGM * WGN, 16 / (WGM * WGN))
     const int frag_chunk = lane >> 4;
     const uint32_t lds0 = lds_offset(smem);
 
-    const int v = int(blockIdx.x);
+    // The workgroup's rank in the work: workgroups are dealt to the eight
+    // XCDs round robin, so ranks go to XCDs in contiguous blocks -- the pieces
+    // of a split tile, and neighbouring tiles, then mostly run on one XCD and
+    // share its L2.
+    int v;
+    {
+        const int x = int(blockIdx.x) % kXcds, i = int(blockIdx.x) / kXcds;
+        const int q = sk.grid / kXcds, r = sk.grid - q * kXcds;
+        v = x * q + (x < r ? x : r) + i;
+    }
     const int64_t total = int64_t(sk.tiles) * sk.nkt;
     auto start_of = [&](int w) { return int64_t(w) * total / sk.grid; };   // first unit of workgroup w
     const int64_t u_end = start_of(v + 1);

@@ -142,7 +142,27 @@ typedef struct {
      * ws_partial_offset; 1 = no split (ws_partial_bytes 0) */
     uint64_t ws_partial_offset, ws_partial_bytes;
     int32_t ksplit;
+    /* order in which the workgroups of kernel 1 take the (split, output tile)
+     * pairs (conv_tile_order_t); 0 for the other kernels */
+    int32_t tile_order;
 } conv_plan_info_t;
+
+/* Tile orders of the pipelined kernel (conv_plan_info_t.tile_order, the
+ * fourth field of a forced plan).  The GPU deals workgroups to its eight XCDs,
+ * each with its own L2, round robin; LINEAR leaves consecutive tiles on
+ * different XCDs, the other orders give each XCD one contiguous range of the
+ * (split, tile row, tile column) sequence: row-major, row-major with odd tile
+ * rows right to left (serpentine: consecutive tiles always share an operand
+ * panel), or column-major.  "Enabling Memory-efficient Im2win Convolution
+ * ...", abstract (the order of memory accesses as a tuning dimension);
+ * "GPU-Accelerating MSCRED ...", section "Future Work" (further tile and
+ * thread-block configurations). */
+typedef enum {
+    CONV_TILE_LINEAR = 0,
+    CONV_TILE_XCD_ROWS = 1,
+    CONV_TILE_XCD_SERPENT = 2,
+    CONV_TILE_XCD_COLS = 3
+} conv_tile_order_t;
 
 /* Validate *p and build a descriptor.  "GPU-Accelerating MSCRED ...",
  * section "Integrating the CUDA Implementation with PyTorch" (the extension
@@ -160,11 +180,13 @@ typedef struct {
 conv_status_t conv_create_desc(const conv_params_t* p, conv_desc_t* out);
 
 /* As conv_create_desc, with the contraction kernel named explicitly: plan is
- * "<kernel>:<variant>" or "<kernel>:<variant>:<ksplit>" with kernel one of
- * reg, dma, wide, nchw, strip, striprb, nchwstrip, nchwtile, tile16, streamk
- * (the numbering of conv_plan_info_t.kernel, in that order) and variant an index
+ * "<kernel>:<variant>", "<kernel>:<variant>:<ksplit>" or
+ * "<kernel>:<variant>:<ksplit>:<tile order>" with kernel one of reg, dma,
+ * wide, nchw, strip, striprb, nchwstrip, nchwtile, tile16, streamk (the
+ * numbering of conv_plan_info_t.kernel, in that order) and variant an index
  * into that kernel's compiled tile shapes; ksplit (1-8) splits the
- * contraction of the dma and wide kernels.  "GPU-Accelerating MSCRED ...",
+ * contraction of the dma and wide kernels; tile order (conv_tile_order_t)
+ * applies to the dma kernel.  "GPU-Accelerating MSCRED ...",
  * section "Engineering Challenges" (kernel configuration: thread-block
  * dimensions and tile sizes change occupancy, memory access and work
  * distribution, so they are measured, not assumed).  For tests and tuning: a
@@ -318,7 +340,8 @@ conv_status_t conv_lstm_step(conv_desc_t d, const void* x, const void* h_prev, c
  * current plan and every other compiled contraction kernel and tile variant
  * that takes its convolution and whose workspace fits ws_bytes (the pipelined
  * and wide-tile kernels' variants each without a split contraction and with 2
- * and 4 splits), and keeps the fastest in d. */
+ * and 4 splits), then, when the fastest is the pipelined kernel, that plan in
+ * each tile order, and keeps the fastest. */
 typedef struct {
     int32_t candidates;       /* plans timed, the current one included */
     int32_t kernel;           /* the plan kept (conv_plan_info_t numbering) */
@@ -326,6 +349,7 @@ typedef struct {
     float default_ms;         /* ms per conv2d_fwd-equivalent call, the plan d had on entry */
     float best_ms;            /* ms per call of the plan kept */
     int32_t ksplit;           /* its split contraction (conv_plan_info_t.ksplit) */
+    int32_t tile_order;       /* its tile order (conv_plan_info_t.tile_order) */
 } conv_tune_result_t;
 
 /* Tune the plan of d (not a ConvLSTM descriptor) with reps timed calls per

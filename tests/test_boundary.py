@@ -438,3 +438,25 @@ def test_streamk_plan():
         c = cl.Conv2d(2, 64, 17, 17, 72, 3, 3, padding=1, layout="nhwc", dtype="f16", algo="implicit",
                       plan="streamk:%d" % v)
         assert c.info["kernel"] != 9, v
+
+
+def test_tile_order_plan():
+    """The pipelined kernel's tile order is the fourth field of a forced plan
+    and defaults to XCD ranges in serpentine order (2); other kernels ignore
+    it."""
+    a = (64, 256, 14, 14, 256, 3, 3)
+    c = cl.Conv2d(*a, padding=1, layout="nhwc", dtype="f16", algo="implicit")
+    assert c.info["kernel"] == 1 and c.info["tile_order"] == 2
+    c = cl.Conv2d(*a, padding=1, layout="nhwc", dtype="f16", algo="implicit", plan="dma:8:1")
+    assert c.info["tile_order"] == 2
+    for o in range(4):
+        c = cl.Conv2d(*a, padding=1, layout="nhwc", dtype="f16", algo="implicit", plan="dma:8:1:%d" % o)
+        assert (c.info["kernel"], c.info["kernel_variant"], c.info["ksplit"], c.info["tile_order"]) == (1, 8, 1, o)
+    c = cl.Conv2d(*a, padding=1, layout="nhwc", dtype="f16", algo="implicit", plan="dma:8:2:3")
+    assert (c.info["ksplit"], c.info["tile_order"]) == (2, 3)
+    for bad in ("dma:8:1:4", "dma:8:1:-1"):
+        c = cl.Conv2d(*a, padding=1, layout="nhwc", dtype="f16", algo="implicit", plan=bad)
+        assert c.info["tile_order"] == 2, bad
+    c = cl.Conv2d(32, 128, 64, 64, 128, 11, 11, padding=5, layout="nhwc", dtype="f16", algo="implicit",
+                  plan="striprb:5:1:2")
+    assert c.info["kernel"] == 5 and c.info["tile_order"] == 0

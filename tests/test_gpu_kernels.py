@@ -247,6 +247,49 @@ def test_split_contraction_parity(dev, case):
         assert_parity(to_f64(y1.cpu()), ref, yabs, dt, "split %s" % forced)
 
 
+ORDER_CASES = [
+    # (dtype, layout, algo, shape, plan without the order): tile counts not a
+    # multiple of the 8 XCDs, fewer workgroups than XCDs, a split contraction
+    ("f16", "nhwc", "implicit", (2, 64, 17, 17, 72, 3, 3, (1, 1), (1, 1), (1, 1)), "dma:8:1"),
+    ("bf16", "nhwc", "implicit", (3, 96, 9, 9, 300, 3, 3, (1, 1), (2, 2), (2, 2)), "dma:8:3"),
+    ("f16", "nhwc", "im2win", (2, 64, 17, 17, 130, 3, 3, (2, 1), (1, 1), (1, 1)), "dma:2:2"),
+    ("bf16", "nhwc", "implicit", (1, 64, 5, 5, 40, 3, 3, (1, 1), (1, 1), (1, 1)), "dma:8:1"),
+    ("f32", "nchw", "im2col", (2, 16, 13, 11, 33, 3, 3, (1, 1), (1, 1), (1, 1)), "dma:1:2"),
+    ("f16", "nhwc", "implicit", (5, 128, 14, 14, 256, 1, 1, (1, 1), (0, 0), (1, 1)), "dma:11:1"),
+]
+
+
+@pytest.mark.parametrize("case", ORDER_CASES, ids=lambda c: "%s-%s-%s-%s" % (c[0], c[1], c[2], c[4]))
+def test_tile_order_parity(dev, case):
+    """Every tile order of the pipelined kernel maps the workgroups one to one
+    onto the (split, tile) pairs: each order gives the same bits as the plain
+    order, which is in parity with the oracle."""
+    dt, lay, algo, (N, C, H, W, K, R, S, st, pd, dl), forced = case
+    g = torch.Generator().manual_seed(17)
+    x = (torch.rand(N, C, H, W, generator=g) * 2 - 1).to(TORCH_DT[dt])
+    w = (torch.randn(K, C, R, S, generator=g) / np.sqrt(C * R * S)).to(TORCH_DT[dt])
+    b = (torch.randn(K, generator=g) * 0.1).to(TORCH_DT[dt])
+    xl, wl = _perm(x, lay), _perm(w, lay)
+    xd, wd, bd = xl.to(dev), wl.to(dev), b.to(dev)
+    ref, yabs = oracle.conv2d(xl, wl, b, layout=lay, stride=st, padding=pd, dilation=dl, with_abs=True)
+    base = None
+    for order in range(4):
+        plan = "%s:%d" % (forced, order)
+        d = cl.Conv2d(N, C, H, W, K, R, S, stride=st, padding=pd, dilation=dl, layout=lay, dtype=dt, algo=algo,
+                      plan=plan)
+        assert d.info["kernel"] == 1 and d.info["tile_order"] == order, d.info
+        assert d.info["ksplit"] == int(forced.split(":")[2]), d.info
+        print("tile order case %s %s %s %s %s" % (dt, lay, algo, case[3], plan), flush=True)
+        y = d.forward(xd, wd, bd)
+        torch.cuda.synchronize()
+        yb = y.cpu().view(-1).view(torch.uint8)
+        if base is None:
+            base = yb
+            assert_parity(to_f64(y.cpu()), ref, yabs, dt, "tile order %s" % plan)
+        else:
+            assert torch.equal(yb, base), plan
+
+
 @pytest.mark.parametrize("case", [
     ("f32", "nchw", (64, 32, 30, 30, 64, 3, 3, (2, 2), (0, 0), (1, 1))),
     ("f32", "nchw", (16, 3, 30, 30, 32, 3, 3, (1, 1), (1, 1), (1, 1))),
