@@ -42,6 +42,21 @@ void launch_gemm_tile(const conv_desc& d, const GemmArgs& g, hipStream_t st) {
     if (d.p.algo != CONV_ALGO_IMPLICIT) {
         // lowered buffer (im2win strips / im2col rows) or 1x1 NHWC input in place
         const bool seg = !d.elided && d.p.algo == CONV_ALGO_IM2WIN;
+        if constexpr (sizeof(T) == 4) {
+            if (d.unpadded) {
+                // unpadded fp32 rows and packed filter rows: element gathers
+                if (seg) {
+                    using A = StridedRows<T, BM, BK, true, true>;
+                    if (nhwc) launch_core<T, BM, BN, BK, WGM, WGN, true, A, BRowsElem>(d, g, st);
+                    else launch_core<T, BM, BN, BK, WGM, WGN, false, A, BRowsElem>(d, g, st);
+                } else {
+                    using A = StridedRows<T, BM, BK, false, true>;
+                    if (nhwc) launch_core<T, BM, BN, BK, WGM, WGN, true, A, BRowsElem>(d, g, st);
+                    else launch_core<T, BM, BN, BK, WGM, WGN, false, A, BRowsElem>(d, g, st);
+                }
+                return;
+            }
+        }
         if (seg) {
             using A = StridedRows<T, BM, BK, true, false>;
             if (nhwc) launch_core<T, BM, BN, BK, WGM, WGN, true, A, BRows>(d, g, st);

@@ -51,8 +51,10 @@ bool streamk_variant(int v) {
 }
 
 // force: "<kernel>:<variant>[:<ksplit>[:<tile order>]]" (conv_create_desc_forced,
-// conv_tune), or nullptr for the default choice.
-conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force) {
+// conv_tune), or nullptr for the default choice.  lstm: the ConvLSTM step's
+// gate convolution, whose contraction reads whole 16-byte chunks of padded
+// lowered rows.
+conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force, bool lstm = false) {
     if (p.N < 0 || p.C <= 0 || p.H <= 0 || p.W <= 0 || p.K <= 0 || p.R <= 0 || p.S <= 0) return CONV_ERR_INVALID_ARG;
     if (p.stride_h <= 0 || p.stride_w <= 0 || p.dil_h <= 0 || p.dil_w <= 0 || p.pad_h < 0 || p.pad_w < 0)
         return CONV_ERR_INVALID_ARG;
@@ -75,13 +77,30 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force) {
     d.vec = 16 / d.elem;
     d.M = p.N * d.P * d.Q;
     d.Kg = p.C * p.R * p.S;
-    d.RCp = int64_t(round_up(uint64_t(p.R * p.C), uint64_t(d.vec)));
-    d.Kl = p.S * d.RCp;
     d.W_used = (d.Q - 1) * p.stride_w + (p.S - 1) * int64_t(p.dil_w) + 1;
-
     const bool nhwc = p.layout == CONV_NHWC;
     const bool c_vec = p.C % d.vec == 0;
     const bool implicit = p.algo == CONV_ALGO_IMPLICIT;
+    // Lowered rows: R*C rounded up to whole 16-byte vectors, so that every
+    // lowered row and contraction tile is read with 16-byte loads -- except
+    // fp32 windows whose R*C is not a whole number of vectors (the 3-channel
+    // first layers), whose lowered buffers are stored unpadded (one window
+    // row every R*C elements) and read element by element: padding 9 to 12
+    // would cost a third more workspace than the windows themselves
+    // ("Enabling Memory-efficient Im2win Convolution ...", abstract: im2win's
+    // point is a smaller lowered buffer than im2col's).  Only while the
+    // buffer's elements fit 32-bit indices.  (The same row length for every
+    // algorithm, so that im2win_bytes describes one layout per shape; only
+    // the lowered algorithms use it.)
+    d.unpadded = false;
+    if (!lstm && p.dtype == CONV_F32 && (p.R * p.C) % d.vec != 0) {
+        const int64_t w_el = p.N * d.P * d.W_used * p.R * p.C;
+        const int64_t c_el = d.M * p.S * p.R * p.C;
+        d.unpadded = w_el < lim && c_el < lim && d.M < lim;
+    }
+    d.RCp = d.unpadded ? p.R * p.C : int64_t(round_up(uint64_t(p.R * p.C), uint64_t(d.vec)));
+    d.Kl = p.S * d.RCp;
+
     d.elided = implicit || (nhwc && p.R == 1 && p.S == 1 && p.pad_h == 0 && p.pad_w == 0 && c_vec);
     // KRSC with R == 1 or S == 1 is already the (s, r, c) order when C fills whole vectors;
     // the implicit contraction reads the filter in its own order.
@@ -112,7 +131,7 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force) {
     const uint64_t x_bytes = uint64_t(p.N) * p.C * p.H * p.W * e;
     const uint64_t a_bytes = d.elided ? x_bytes : d.bytes_low;
     const uint64_t b_bytes = uint64_t(p.K) * (implicit ? d.Kg : d.Kl) * e;
-    const bool a_chunks = implicit ? (nhwc && c_vec) : true;
+    const bool a_chunks = implicit ? (nhwc && c_vec) : !d.unpadded;
     const bool dma_ok = a_chunks && a_bytes < (uint64_t(1) << 31) && b_bytes < (uint64_t(1) << 31);
     // fp32 NCHW fused windows: the pipelined kernel with 4-byte window loads.
     const bool nchw_ok = implicit && !nhwc && p.dtype == CONV_F32 && x_bytes < (uint64_t(1) << 31) &&
@@ -212,13 +231,13 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force) {
         d.kernel = KERN_DMA;
         d.variant = p.K <= 32 ? 0 : (p.K <= 64 ? 1 : (p.dtype == CONV_F32 ? 2 : 8));
         if (d.variant == 2 && (d.M / 256) * ((p.K + 127) / 128) >= 512) d.variant = 3;
-        // Long filter rows (S >= 9), enough 512 x 128 tiles to give most CUs
+        // Long filter rows (S >= 7), enough 512 x 128 tiles to give most CUs
         // one, and output channels filling whole 128-wide tiles: the
-        // register-streamed strip kernel (measured on the kernel-size layers:
-        // ahead of the pipelined tiles at 11 x 11, level at 7 x 7, behind at
-        // 5 x 5 and 3 x 3).
+        // register-streamed strip kernel (measured on the kernel-size layers,
+        // interleaved timing: ahead of the pipelined tiles by 5 % at 7 x 7 and
+        // by a quarter at 11 x 11, behind by 3 % at 5 x 5 and 15 % at 3 x 3).
         const StripVariant& rb = kStripRbVariants[5];
-        if (p.S >= 9 && p.K % 128 == 0 && (d.M / rb.bm) * (p.K / rb.bn) >= 192 && strip_fits(rb)) {
+        if (p.S >= 7 && p.K % 128 == 0 && (d.M / rb.bm) * (p.K / rb.bn) >= 192 && strip_fits(rb)) {
             d.kernel = KERN_STRIP_RB;
             d.variant = 5;
         }
@@ -417,7 +436,7 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force) {
     // (NCHW), one row and the most output columns that fit.
     d.band_items = 0;
     d.band_g = d.band_cw = d.band_br = d.band_tw = d.band_wl = d.band_cs = d.band_lds = 0;
-    if ((!nhwc || !c_vec) && !d.elided && p.N > 0 && d.P > 0 && d.Q > 0) {
+    if ((!nhwc || !c_vec) && !d.elided && !d.unpadded && p.N > 0 && d.P > 0 && d.Q > 0) {
         const bool win = p.algo == CONV_ALGO_IM2WIN;
         const int64_t full = win ? d.W_used : d.Q;
         const int64_t span = (p.S - 1) * int64_t(p.dil_w) + 1;
@@ -485,7 +504,7 @@ conv_status_t plan_lstm(const conv_params_t& p, int64_t c_x, conv_desc& d) {
     if (c_x <= 0 || p.K <= 0 || p.K % 4 != 0 || p.C != c_x + p.K / 4) return CONV_ERR_INVALID_ARG;
     if (p.stride_h != 1 || p.stride_w != 1) return CONV_ERR_INVALID_ARG;
     if ((p.K / 4) % 16 != 0) return CONV_ERR_UNSUPPORTED;
-    conv_status_t s = plan(p, d, nullptr);
+    conv_status_t s = plan(p, d, nullptr, true);
     if (s != CONV_OK) return s;
     if (d.P != p.H || d.Q != p.W) return CONV_ERR_INVALID_ARG;
     if (d.bytes_low / 16 > 0xffffffffull) return CONV_ERR_UNSUPPORTED;
@@ -583,6 +602,11 @@ LowerArgs lower_args(const conv_desc& d, const void* x, void* out) {
     a.fd_q = fd(d.Q);
     a.fd_nv = fd((int64_t(d.band_br) * d.p.W + d.vec - 1) / d.vec + 1);
     a.fd_w = fd(d.p.W);
+    if (d.unpadded) {
+        // element decode: per strip (im2win) or per row (im2col), per window row
+        a.fd_row = fd(win ? d.W_used * d.RCp : d.Kl);
+        a.fd_cpv = fd(d.RCp);
+    }
     return a;
 }
 
@@ -668,7 +692,18 @@ void launch_lower_args(const conv_desc& d, const LowerArgs& a, hipStream_t st) {
     const bool nhwc = d.p.layout == CONV_NHWC;
     const bool win = d.p.algo == CONV_ALGO_IM2WIN;
     const uint64_t total = (win ? d.im2win_bytes : uint64_t(d.M) * d.Kl * d.elem) / 16;
-    if (nhwc && d.p.C % VEC == 0) {
+    if (d.unpadded) {
+        const uint64_t elems = win ? d.im2win_bytes / d.elem : uint64_t(d.M) * d.Kl;
+        const uint32_t nv = uint32_t((elems + VEC - 1) / VEC);
+        if (nhwc && win)
+            lower_unpadded_kernel<T, true, false><<<grid_stride_blocks(nv), 256, 0, st>>>(a, nv, uint32_t(elems));
+        else if (nhwc)
+            lower_unpadded_kernel<T, true, true><<<grid_stride_blocks(nv), 256, 0, st>>>(a, nv, uint32_t(elems));
+        else if (win)
+            lower_unpadded_kernel<T, false, false><<<grid_stride_blocks(nv), 256, 0, st>>>(a, nv, uint32_t(elems));
+        else
+            lower_unpadded_kernel<T, false, true><<<grid_stride_blocks(nv), 256, 0, st>>>(a, nv, uint32_t(elems));
+    } else if (nhwc && d.p.C % VEC == 0) {
         if (win) {
             const uint32_t vps = uint32_t(d.W_used * d.RCp / VEC);
             dim3 grid(uint32_t(d.p.N * d.P), (vps + 256 * LOWER_U - 1) / (256 * LOWER_U));

@@ -126,6 +126,7 @@ struct conv_desc {
     bool elided;        // no lowering launch: the contraction reads x (implicit, or 1x1 NHWC unpadded)
     bool pack;          // filter needs packing into ws (lowered contraction order)
     bool frag_pack;     // filter packed into MFMA fragment order in ws (register-streamed kernel)
+    bool unpadded;      // fp32 lowered rows of R*C elements, not whole vectors (RCp == R*C)
     uint64_t off_filter, bytes_filter, off_low, bytes_low, ws_bytes;
     uint64_t im2win_bytes, im2col_bytes;
     int32_t kernel;     // KernelId

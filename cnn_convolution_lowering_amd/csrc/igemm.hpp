@@ -235,9 +235,21 @@ struct StridedRows {
             if (!ELEM) {
                 r[i] = (ok[i] && kk < g.Kc) ? load16(base + off[i] + seg + t) : zero4();
             } else {
+                // element by element; a vector may cross into the next
+                // segment (the next tap's columns of an unpadded strip)
                 Pack16<T> pk;
+                int tt = t;
+                int64_t sg = seg;
 #pragma unroll
-                for (int e = 0; e < VEC; ++e) pk.e[e] = (ok[i] && kk + e < g.Kc) ? base[off[i] + seg + t + e] : T(0);
+                for (int e = 0; e < VEC; ++e) {
+                    if (SEGMENTED)
+                        while (tt >= g.RCp) {
+                            tt -= g.RCp;
+                            sg += g.sS;
+                        }
+                    pk.e[e] = (ok[i] && kk + e < g.Kc) ? base[off[i] + sg + tt] : T(0);
+                    ++tt;
+                }
                 r[i] = pk.v;
             }
         }

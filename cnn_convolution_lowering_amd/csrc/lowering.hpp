@@ -458,6 +458,58 @@ __global__ void __launch_bounds__(256) lower_generic_kernel(LowerArgs a, uint32_
 }
 
 // ---------------------------------------------------------------------------
+// im2win and im2col with unpadded window rows (RCp == R*C, not a whole number
+// of vectors; fp32 3-channel layers): the lowered buffer is a flat array of
+// `elems` elements, each thread decoding VEC consecutive ones and storing them
+// as one 16-byte vector (the buffer starts 16-byte aligned; the last vector
+// may be partial).  Decode: fd_row divides by the elements per strip (im2win,
+// W_used*R*C) or per row (im2col, S*R*C), fd_cpv by R*C.
+template <typename T, bool NHWC, bool COL>
+__global__ void __launch_bounds__(256) lower_unpadded_kernel(LowerArgs a, uint32_t total_vec, uint32_t elems) {
+    constexpr int VEC = Vec<T>::n;
+    const T* __restrict__ x = static_cast<const T*>(a.x);
+    T* __restrict__ out = static_cast<T*>(a.out);
+    for (uint32_t v = blockIdx.x * 256u + threadIdx.x; v < total_vec; v += gridDim.x * 256u) {
+        const uint32_t f0 = v * VEC;
+        Pack16<T> pk;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            const uint32_t f = f0 + e;
+            T val = T(0);
+            if (f < elems) {
+                const uint32_t row = fdiv(f, a.fd_row);
+                const uint32_t rem = f - row * a.fd_row.d;
+                const uint32_t seg = fdiv(rem, a.fd_cpv);   // strip column j (im2win) or tap s (im2col)
+                const int t = int(rem - seg * a.fd_cpv.d);
+                const int r = int(fdiv(uint32_t(t), a.fd_c));
+                const int c = t - r * a.C;
+                int n, p, wcol;
+                if (COL) {
+                    const uint32_t np = fdiv(row, a.fd_q);
+                    const int q = int(row - np * a.fd_q.d);
+                    n = int(fdiv(np, a.fd_p));
+                    p = int(np) - n * a.P;
+                    wcol = q * a.sw - a.pw + int(seg) * a.dw;
+                } else {
+                    n = int(fdiv(row, a.fd_p));
+                    p = int(row) - n * a.P;
+                    wcol = int(seg) - a.pw;
+                }
+                val = x_at<T, NHWC>(a, x, n, c, p * a.sh - a.ph + r * a.dh, wcol);
+            }
+            pk.e[e] = val;
+        }
+        if (f0 + VEC <= elems) {
+            store16(out + f0, pk.v);
+        } else {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e)
+                if (f0 + e < elems) out[f0 + e] = pk.e[e];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Filter pack: Bp[k][s*RCp + r*C + c] = w[k, c, r, s] (zeros in the padding),
 // the filter matrix reshaped to the lowered row order.
 struct PackArgs {

@@ -106,7 +106,9 @@ typedef struct {
     int64_t M;                 /* GEMM rows = N*P*Q */
     int64_t Kg;                /* contraction length of the definition = C*R*S */
     int64_t W_used;            /* padded input columns one output row's windows touch */
-    int64_t RCp;               /* R*C rounded up to a 16-byte multiple of elements */
+    int64_t RCp;               /* lowered window row: R*C rounded up to a 16-byte multiple of
+                                * elements; R*C itself for fp32 when that is not a whole
+                                * number of vectors (unpadded rows, read element by element) */
     int64_t Kl;                /* lowered contraction length = S*RCp (zeros in the padding) */
     uint64_t ws_bytes;         /* total workspace the caller must pass */
     uint64_t ws_filter_offset, ws_filter_bytes;    /* packed filter Bp[K][Kl] */

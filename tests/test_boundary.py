@@ -161,7 +161,8 @@ def test_workspace_formula(layout, dtype, algo):
         pd = (int(rng.integers(0, 3)), int(rng.integers(0, 3)))
         c = cl.Conv2d(N, C, H, W, K, R, S, stride=st, padding=pd, layout=layout, dtype=dtype, algo=algo)
         P, Q = c.P, c.Q
-        RCp = _round_up(R * C, vec)
+        # fp32 window rows that are not whole vectors are stored unpadded
+        RCp = R * C if dtype == "f32" and (R * C) % vec else _round_up(R * C, vec)
         Kl = S * RCp
         W_used = (Q - 1) * st[1] + S
         info = c.info
@@ -188,11 +189,12 @@ def test_workload_workspace_ratios():
     """im2win strip bytes / explicit-im2col bytes per layer of the five workloads.
 
     Expected values worked out from the shapes: ratio = W_used*RCp / (Q*C*R*S),
-    0 where a 1x1 layer is read in place."""
+    0 where a 1x1 layer is read in place; the fp32 3-channel layers' window
+    rows are unpadded (RCp = R*C = 9), so c1 is 32*9 / (30*27) = 35.6 %."""
     from cnn_convolution_lowering_amd.workloads import workload_spec
     want = {
-        "c1": [32 * 12 / (30 * 27)],
-        "c2": [32 * 12 / (30 * 27), 29 * 96 / (14 * 288), 14 * 128 / (7 * 256), 6 * 256 / (3 * 512)],
+        "c1": [32 * 9 / (30 * 27)],
+        "c2": [32 * 9 / (30 * 27), 29 * 96 / (14 * 288), 14 * 128 / (7 * 256), 6 * 256 / (3 * 512)],
         "c3": [16 * 768 / (14 * 2304)],
         "c4": [229 * 24 / (112 * 147), 0.0, 9 * 1536 / (7 * 4608)],
         "c5": [0.0, 66 * 384 / (64 * 1152), 68 * 640 / (64 * 3200), 70 * 896 / (64 * 6272),

@@ -118,6 +118,31 @@ def test_integer_inputs_bit_exact(dev, dt, lay, algo):
                            want.view(torch.int16 if dt != "f32" else torch.int32)), "%s %s %s" % (dt, lay, algo)
 
 
+@pytest.mark.parametrize("lay", ["nchw", "nhwc"])
+@pytest.mark.parametrize("algo", ["im2win", "im2col"])
+def test_unpadded_rows_integer_exact(dev, lay, algo):
+    """fp32 lowered rows whose R*C is not a whole number of vectors are stored
+    unpadded and read element by element; a vector read then crosses into
+    the next tap's columns (with horizontal dilation, a different strip
+    column).  Integer inputs: the result must be the oracle's bit for bit."""
+    g = torch.Generator().manual_seed(29)
+    for (N, C, H, W, K, R, S, st, pd, dl) in [(2, 5, 13, 11, 33, 3, 2, (2, 1), (1, 0), (1, 2)),
+                                              (3, 3, 30, 30, 32, 3, 3, (1, 1), (1, 1), (1, 1)),
+                                              (1, 1, 9, 20, 70, 1, 3, (1, 2), (0, 1), (1, 3)),
+                                              (2, 7, 8, 9, 130, 3, 3, (1, 1), (1, 1), (2, 2))]:
+        d = cl.Conv2d(N, C, H, W, K, R, S, stride=st, padding=pd, dilation=dl, layout=lay, dtype="f32", algo=algo)
+        assert d.info["RCp"] == R * C and d.info["kernel"] == 0, d.info
+        x = torch.randint(-2, 3, (N, C, H, W), generator=g).to(torch.float32)
+        w = torch.randint(-2, 3, (K, C, R, S), generator=g).to(torch.float32)
+        b = torch.randint(-4, 5, (K,), generator=g).to(torch.float32)
+        xl, wl = _perm_x(x, lay), _perm_x(w, lay)
+        _say("unpadded case C%d R%d S%d dil%s %s %s" % (C, R, S, dl, lay, algo))
+        y = _run(dev, xl, wl, b, lay, st, pd, dl, algo)
+        ref = oracle.conv2d(xl, wl, b, layout=lay, stride=st, padding=pd, dilation=dl)
+        assert np.all(np.abs(ref) < 2 ** 24)
+        assert torch.equal(y, torch.from_numpy(ref).to(torch.float32)), (lay, algo, C, R, S)
+
+
 @pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("lay", ["nchw", "nhwc"])
 def test_delta_kernel_reproduces_input(dev, dt, lay):
