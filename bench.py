@@ -67,9 +67,19 @@ CSRC = os.path.join(ROOT, "cnn_convolution_lowering_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
+# Host-only sources (planner and C ABI; the peak library): not part of any
+# convolution kernel's device code.
+HOST_ONLY = ("convlower.hip", "peak.hip")
+
+
 def source_digest() -> str:
+    """Digest of the device code of the convolution kernels.  A traffic
+    record also names the plan it was taken on, so a planner change that
+    picks another kernel for the layer invalidates it as well."""
     h = hashlib.sha256()
     for name in sorted(os.listdir(CSRC)):
+        if name in HOST_ONLY:
+            continue
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(name.encode())
             h.update(f.read())
@@ -187,22 +197,30 @@ def kernel_symbol(l, stage):
         return {6: "pack_filter_frag_f32_kernel", 8: "pack_filter_tile16_kernel"}.get(info["kernel"],
                                                                                     "pack_filter_kernel")
     # NHWC with C a whole number of 16-byte vectors: the direct vector copy;
-    # otherwise the band kernel (the element-wise fallback, for a one-column
-    # tile beyond the LDS budget, occurs in none of the workloads).
+    # fp32 window rows that are not whole vectors: the unpadded element-wise
+    # lowering; otherwise the band kernel (the element-wise fallback, for a
+    # one-column tile beyond the LDS budget, occurs in none of the workloads).
+    p = d.params
+    if info["elem_bytes"] == 4 and (p.R * p.C) % 4 and info["RCp"] == p.R * p.C:
+        return "lower_unpadded_kernel"
     if d.layout == "nhwc" and d.params.C % (16 // info["elem_bytes"]) == 0:
         return "%s_nhwc_vec_kernel" % d.algo
     return "lower_%s_band_kernel" % d.layout
 
 
-def load_traffic(kernel_key: str):
+def load_traffic(kernel_key: str, plan):
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f).get(kernel_key)
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("source_sha256_16") != source_digest():
-        return None      # counters were taken on a different kernel source
+    if not rec or rec.get("source_sha256_16") != source_digest() or rec.get("plan") != list(plan):
+        return None      # counters were taken on a different kernel source or plan
     return rec.get("bytes_per_launch")
+
+
+def plan_of(info):
+    return [info["kernel"], info["kernel_variant"], info["ksplit"], info["tile_order"]]
 
 
 class Flusher:
@@ -311,7 +329,7 @@ def bench_config(name, dev, args, peaks, headline=False):
                 "frac": achieved / PEAK_HBM_GBS}
         if peaks and peaks.get("hbm_gbs"):
             roof.update({"measured_peak": peaks["hbm_gbs"], "frac_of_measured": achieved / peaks["hbm_gbs"]})
-    roof.update({"traffic": load_traffic(kernel_key), "kernel": kernel_symbol(dl, dom_stage),
+    roof.update({"traffic": load_traffic(kernel_key, plan_of(dl["desc"].info)), "kernel": kernel_symbol(dl, dom_stage),
                  "kernel_key": kernel_key, "layer": dl["spec"].label, "avg_launch_ms": dom_ms,
                  "launches_timed": len(dom_ms_list), "algorithmic_flops": flops, "algorithmic_bytes": nbytes})
 
@@ -327,7 +345,7 @@ def bench_config(name, dev, args, peaks, headline=False):
         rec = {"layer": l["spec"].label, "gflop": l["flops"] / 1e9,
                "kernels_ms": {st: round(brk[(i, st)], 5) for st in STAGES if (i, st) in brk},
                "contract_kernel": kernel_symbol(l, "contract"),
-               "plan": [info["kernel"], info["kernel_variant"], info["ksplit"]],
+               "plan": plan_of(info),
                "tflops_isolated": tfs, "bound": "mfma" if mfma_bound else "hbm",
                "frac_of_peak": (tfs / peak_f if mfma_bound else gbs / PEAK_HBM_GBS) if lay_ms else None,
                "b_min_bytes": b_min, "b_min_gbs_isolated": gbs,

@@ -427,6 +427,8 @@ void launch_gemm(const conv_desc& d, const void* x, const void* w, const void* b
                 CONVLOWER_STRIP_RB_CASE(4)
                 CONVLOWER_STRIP_RB_CASE(5)
                 CONVLOWER_STRIP_RB_CASE(6)
+                CONVLOWER_STRIP_RB_CASE(7)
+                CONVLOWER_STRIP_RB_CASE(8)
                 default: break;
             }
 #undef CONVLOWER_STRIP_RB_CASE

@@ -231,15 +231,20 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force, bool
         d.kernel = KERN_DMA;
         d.variant = p.K <= 32 ? 0 : (p.K <= 64 ? 1 : (p.dtype == CONV_F32 ? 2 : 8));
         if (d.variant == 2 && (d.M / 256) * ((p.K + 127) / 128) >= 512) d.variant = 3;
-        // Long filter rows (S >= 7), enough 512 x 128 tiles to give most CUs
+        // Filter rows of 5 taps and more, enough strip tiles to give most CUs
         // one, and output channels filling whole 128-wide tiles: the
-        // register-streamed strip kernel (measured on the kernel-size layers,
-        // interleaved timing: ahead of the pipelined tiles by 5 % at 7 x 7 and
-        // by a quarter at 11 x 11, behind by 3 % at 5 x 5 and 15 % at 3 x 3).
-        const StripVariant& rb = kStripRbVariants[5];
-        if (p.S >= 7 && p.K % 128 == 0 && (d.M / rb.bm) * (p.K / rb.bn) >= 192 && strip_fits(rb)) {
+        // register-streamed strip kernel (interleaved timing on the
+        // kernel-size layers: ahead of the pipelined tiles by 3 % at 5 x 5,
+        // 3 % at 7 x 7 and a quarter at 11 x 11, behind by 15 % at 3 x 3).
+        // From 9 taps 512 x 128 tiles over four waves, one per SIMD, the
+        // filter prefetch 4 steps ahead; below, 256 x 128 tiles whose 64 x 128
+        // wave tiles leave room for two waves per SIMD (level at 11 x 11, 3 %
+        // ahead at 5 x 5 and 7 x 7).
+        const int rbv = p.S >= 9 ? 5 : 8;
+        const StripVariant& rb = kStripRbVariants[rbv];
+        if (p.S >= 5 && p.K % 128 == 0 && (d.M / rb.bm) * (p.K / rb.bn) >= 192 && strip_fits(rb)) {
             d.kernel = KERN_STRIP_RB;
-            d.variant = 5;
+            d.variant = rbv;
         }
     } else {
         d.kernel = KERN_REG;

@@ -71,7 +71,7 @@ constexpr StripVariant kStripVariants[] = {
 constexpr StripVariant kStripRbVariants[] = {
     {512, 128, 4, 1, 2816, 2}, {512, 128, 4, 1, 2816, 3}, {256, 128, 2, 2, 1536, 2},
     {128, 128, 2, 2, 1024, 2}, {256, 256, 2, 2, 1536, 2}, {512, 128, 4, 1, 2816, 4},
-    {128, 128, 2, 2, 1024, 4},
+    {128, 128, 2, 2, 1024, 4}, {512, 128, 8, 1, 3072, 2}, {256, 128, 4, 1, 1536, 2},
 };
 // fp32 NCHW strip kernel: strip = 16-byte slots per buffer (16 channel
 // planes of ((BM-1)/Q + 2) rows x ceil(W_used/4) slots), db = filter

@@ -37,8 +37,17 @@ __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t rsrc, uint
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, int(voff), soff, 0));
 }
 
+// Waves whose accumulators take at most 128 registers (a 64 x 128 or
+// smaller wave tile) fit two to a SIMD: the register budget asks for that,
+// so one wave's waits and bookkeeping overlap the other's MFMAs.
+template <int BM, int BN, int WGM, int WGN>
+constexpr int strip_rb_min_blocks() {
+    return (BM / WGM) * (BN / WGN) / 64 <= 128 ? 512 / (64 * WGM * WGN) : 1;
+}
+
 template <typename T, int BM, int BN, int WGM, int WGN, int STRIP, int DB>
-__global__ void __launch_bounds__(64 * WGM * WGN, 1) conv_strip_rb_kernel(GemmArgs g) {
+__global__ void __launch_bounds__(64 * WGM * WGN, (strip_rb_min_blocks<BM, BN, WGM, WGN>()))
+    conv_strip_rb_kernel(GemmArgs g) {
     constexpr int NT = 64 * WGM * WGN;
     constexpr int VEC = Vec<T>::n;
     constexpr int WM = BM / WGM, WN = BN / WGN;
