@@ -182,7 +182,8 @@ def kernel_work(l, stage):
 
 CONTRACT_KERNELS = ["conv_gemm_kernel", "conv_gemm_dma_kernel", "conv_gemm_wide_kernel", "conv_nchw_f32_dma_kernel",
                     "conv_strip_kernel", "conv_strip_rb_kernel", "conv_nchw_f32_strip_kernel",
-                    "conv_nchw_f32_tile_kernel", "conv_nhwc_tile16_kernel", "conv_gemm_streamk_kernel"]
+                    "conv_nchw_f32_tile_kernel", "conv_nhwc_tile16_kernel", "conv_gemm_streamk_kernel",
+                    "conv_strip_rb2_kernel"]
 
 
 def kernel_symbol(l, stage):
@@ -192,7 +193,7 @@ def kernel_symbol(l, stage):
     if stage == "contract":
         return CONTRACT_KERNELS[info["kernel"]]
     if stage == "pack":
-        if info["kernel"] == 5:
+        if info["kernel"] in (5, 10):
             return "pack_filter_frag_kernel"
         return {6: "pack_filter_frag_f32_kernel", 8: "pack_filter_tile16_kernel"}.get(info["kernel"],
                                                                                     "pack_filter_kernel")

@@ -21,6 +21,8 @@ enum KernelId : int32_t {
     KERN_TILE16 = 8,      // 16-bit NHWC small windows: the same staging, window rows read as contiguous runs
     KERN_STREAMK = 9,     // the LDS-DMA pipeline (a kDmaVariants shape) in stream-K form: equal contraction
                           // ranges per workgroup of a persistent grid, split tiles summed from workspace slots
+    KERN_STRIP_RB2 = 10,  // the register-streamed strips with the taps unrolled (S in kStripRb2Taps, unit
+                          // horizontal dilation), padded strip rows read without conflicts
 };
 
 // One compiled tile shape: BM x BN output tile, BK-deep LDS stages (in 16-bit
@@ -68,6 +70,13 @@ constexpr StripVariant kStripVariants[] = {
 };
 // Strip kernel with register-streamed filter fragments: `bst` is the number
 // of steps the filter loads run ahead (DB).
+// Unrolled-tap form (conv_strip_rb2_kernel): `strip` counts 16-byte slots of
+// padded rows (five per row), `bst` the filter prefetch distance; compiled for
+// the filter widths in kStripRb2Taps.
+constexpr StripVariant kStripRb2Variants[] = {
+    {512, 128, 4, 1, 3584, 2}, {256, 128, 4, 1, 1792, 1},
+};
+constexpr int kStripRb2Taps[] = {3, 5, 7, 9, 11};
 constexpr StripVariant kStripRbVariants[] = {
     {512, 128, 4, 1, 2816, 2}, {512, 128, 4, 1, 2816, 3}, {256, 128, 2, 2, 1536, 2},
     {128, 128, 2, 2, 1024, 2}, {256, 256, 2, 2, 1536, 2}, {512, 128, 4, 1, 2816, 4},

@@ -134,7 +134,11 @@ typedef struct {
      * (tile, contraction step) pairs, a tile split between workgroups summed
      * in contraction order from fp32 slots in the workspace's partial area
      * (one tile_m*tile_n slot and one flag per workgroup), taken only when
-     * named (conv_create_desc_forced) or kept by conv_tune;
+     * named (conv_create_desc_forced) or kept by conv_tune, 10 the strips of
+     * 5 with the taps of a filter row unrolled at compile time (filter widths
+     * 3, 5, 7, 9, 11; unit horizontal dilation), strip rows padded to 80
+     * bytes and pixels dealt to lanes so that fragment reads are
+     * conflict-free at fixed offsets;
      * kernel_variant indexes that kernel's compiled tile shapes (for 9 the
      * shapes of 1) */
     int32_t kernel, kernel_variant;
@@ -184,8 +188,9 @@ conv_status_t conv_create_desc(const conv_params_t* p, conv_desc_t* out);
 /* As conv_create_desc, with the contraction kernel named explicitly: plan is
  * "<kernel>:<variant>", "<kernel>:<variant>:<ksplit>" or
  * "<kernel>:<variant>:<ksplit>:<tile order>" with kernel one of reg, dma,
- * wide, nchw, strip, striprb, nchwstrip, nchwtile, tile16, streamk (the
- * numbering of conv_plan_info_t.kernel, in that order) and variant an index
+ * wide, nchw, strip, striprb, nchwstrip, nchwtile, tile16, streamk,
+ * striprb2 (the numbering of conv_plan_info_t.kernel, in that order) and
+ * variant an index
  * into that kernel's compiled tile shapes; ksplit (1-8) splits the
  * contraction of the dma and wide kernels; tile order (conv_tile_order_t)
  * applies to the dma kernel.  "GPU-Accelerating MSCRED ...",

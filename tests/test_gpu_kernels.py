@@ -22,7 +22,7 @@ from parity import TORCH_DT, assert_parity, to_f64
 pytestmark = pytest.mark.gpu
 
 # kernel name -> (plan_info kernel id, number of compiled variants)
-KERNELS = {"reg": (0, 3), "dma": (1, 12), "wide": (2, 9), "nchw": (3, 12), "strip": (4, 5), "striprb": (5, 9), "nchwstrip": (6, 10), "nchwtile": (7, 6), "tile16": (8, 11), "streamk": (9, 12)}
+KERNELS = {"reg": (0, 3), "dma": (1, 12), "wide": (2, 9), "nchw": (3, 12), "strip": (4, 5), "striprb": (5, 9), "nchwstrip": (6, 10), "nchwtile": (7, 6), "tile16": (8, 11), "streamk": (9, 12), "striprb2": (10, 2)}
 # kernels compiled for some variants only
 VARIANTS = {"streamk": (8,)}
 
@@ -77,6 +77,18 @@ SHAPES_TILE16 = [
     (2, 4, 21, 19, 64, 3, 3, (1, 1), (1, 1), (1, 1)),
 ]
 # (kernel, dtype, layout, algo, shapes)
+# the unrolled-tap strip kernel: compiled filter widths, unit horizontal
+# dilation; ragged channel tiles, vertical dilation, both strides, padding
+SHAPES_RB2 = [
+    (2, 64, 17, 19, 72, 3, 3, (1, 1), (1, 1), (1, 1)),
+    (1, 32, 20, 33, 40, 5, 5, (1, 1), (2, 2), (2, 1)),
+    (3, 96, 9, 70, 130, 7, 7, (2, 1), (3, 3), (1, 1)),
+    (2, 64, 12, 64, 64, 11, 11, (1, 1), (5, 5), (1, 1)),
+    (1, 32, 16, 64, 32, 9, 9, (1, 1), (4, 4), (1, 1)),
+    (2, 32, 10, 60, 160, 3, 5, (1, 1), (1, 2), (1, 1)),
+    (1, 32, 6, 64, 96, 7, 7, (1, 1), (3, 3), (1, 1)),
+]
+
 PLANS = [
     ("reg", "f32", "nhwc", "implicit", SHAPES_SMALL_C + SHAPES_C32[:2]),
     ("reg", "f16", "nchw", "implicit", SHAPES_SMALL_C[:2]),
@@ -102,6 +114,8 @@ PLANS = [
     ("streamk", "f16", "nhwc", "im2col", SHAPES_C32[:2]),
     ("streamk", "f32", "nhwc", "implicit", SHAPES_C32[:2]),
     ("streamk", "bf16", "nchw", "im2win", SHAPES_SMALL_C[:2]),
+    ("striprb2", "f16", "nhwc", "implicit", SHAPES_RB2),
+    ("striprb2", "bf16", "nhwc", "implicit", SHAPES_RB2[::2]),
 ]
 
 
@@ -162,7 +176,7 @@ def test_forced_kernel_integer_exact(dev):
     ref = oracle.conv2d(xl, wl, b, layout="nhwc", stride=1, padding=1)
     want = torch.from_numpy(ref).to(torch.float32).to(torch.float16)
     for forced in ("strip:0", "strip:2", "strip:3", "wide:0", "wide:5", "striprb:0", "striprb:3", "striprb:4",
-                   "dma:8", "dma:9", "dma:10", "dma:11"):
+                   "dma:8", "dma:9", "dma:10", "dma:11", "striprb2:0", "striprb2:1"):
         d = cl.Conv2d(N, C, H, W, K, R, S, padding=1, layout="nhwc", dtype="f16", algo="implicit", plan=forced)
         assert d.info["kernel"] == KERNELS[forced.split(":")[0]][0], forced
         print("int case %s" % forced, flush=True)
