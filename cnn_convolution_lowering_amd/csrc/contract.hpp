@@ -10,6 +10,7 @@
 #include "igemm_dma.hpp"
 #include "igemm_nchw.hpp"
 #include "igemm_nchw_strip.hpp"
+#include "igemm_nchw_taps.hpp"
 #include "igemm_nchw_tile.hpp"
 #include "igemm_strip.hpp"
 #include "igemm_strip_rb.hpp"
@@ -18,9 +19,10 @@
 #include "igemm_tile16.hpp"
 #include "igemm_wide.hpp"
 
-static_assert(convlower::TILE_ORDER_LINEAR == CONV_TILE_LINEAR && convlower::TILE_ORDER_XCD_ROWS == CONV_TILE_XCD_ROWS &&
-                  convlower::TILE_ORDER_XCD_SERPENT == CONV_TILE_XCD_SERPENT &&
-                  convlower::TILE_ORDER_XCD_COLS == CONV_TILE_XCD_COLS,
+static_assert(int(convlower::TILE_ORDER_LINEAR) == int(CONV_TILE_LINEAR) &&
+                  int(convlower::TILE_ORDER_XCD_ROWS) == int(CONV_TILE_XCD_ROWS) &&
+                  int(convlower::TILE_ORDER_XCD_SERPENT) == int(CONV_TILE_XCD_SERPENT) &&
+                  int(convlower::TILE_ORDER_XCD_COLS) == int(CONV_TILE_XCD_COLS),
               "tile order numbering");
 
 namespace convlower {
@@ -406,6 +408,35 @@ void launch_gemm(const conv_desc& d, const void* x, const void* w, const void* b
                 default: break;
             }
 #undef CONVLOWER_NCHW_STRIP_CASE
+        }
+        return;
+    }
+    if (d.kernel == KERN_NCHW_TAPS) {
+        if constexpr (sizeof(T) == 4) {
+#define CONVLOWER_NCHW_TAPS_CASE(I, S_)                                                                         \
+    case I * 16 + S_: {                                                                                         \
+        constexpr NchwTapsVariant v = kNchwTapsVariants[I];                                                     \
+        GemmArgs h = g;                                                                                         \
+        h.tiles_n = int32_t((d.p.K + v.bn - 1) / v.bn);                                                         \
+        const uint32_t blocks = uint32_t(((uint64_t(d.M) + v.bm - 1) / v.bm) * h.tiles_n);                     \
+        conv_nchw_f32_taps_kernel<v.bm, v.bn, v.wgm, v.wgn, v.nbuf, S_><<<blocks, 256, 0, st>>>(h);             \
+        break;                                                                                                  \
+    }
+#define CONVLOWER_NCHW_TAPS_VARIANT(I) CONVLOWER_NCHW_TAPS_CASE(I, 2) CONVLOWER_NCHW_TAPS_CASE(I, 3)
+            static_assert(count_of(kNchwTapsVariants) == 6 && count_of(kNchwTapsTaps) == 2 && kNchwTapsTaps[0] == 2 &&
+                              kNchwTapsTaps[1] == 3,
+                          "compiled filter widths");
+            switch (d.variant * 16 + d.p.S) {
+                CONVLOWER_NCHW_TAPS_VARIANT(0)
+                CONVLOWER_NCHW_TAPS_VARIANT(1)
+                CONVLOWER_NCHW_TAPS_VARIANT(2)
+                CONVLOWER_NCHW_TAPS_VARIANT(3)
+                CONVLOWER_NCHW_TAPS_VARIANT(4)
+                CONVLOWER_NCHW_TAPS_VARIANT(5)
+                default: break;
+            }
+#undef CONVLOWER_NCHW_TAPS_VARIANT
+#undef CONVLOWER_NCHW_TAPS_CASE
         }
         return;
     }

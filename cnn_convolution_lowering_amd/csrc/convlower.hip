@@ -150,6 +150,15 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force, bool
                uint64_t((p.K + 15) / 16 * 16) * d.Kg * 4 < (uint64_t(1) << 31) && rows < 256 && wq < 256 &&
                rows * wq <= nchw_strip_plane(v.strip);
     };
+    // fp32 NCHW tap planes: a compiled filter width, 16-channel blocks, and
+    // the buffers of two workgroups within a CU's LDS.
+    auto nchw_taps_fits = [&](const NchwTapsVariant& v) {
+        bool taps = false;
+        for (int t : kNchwTapsTaps) taps = taps || p.S == t;
+        return nchw_ok && taps && p.C % 16 == 0 &&
+               uint64_t((p.K + 15) / 16 * 16) * d.Kg * 4 < (uint64_t(1) << 31) &&
+               nchw_taps_lds(v.bm, int32_t(p.S), v.nbuf) <= kNchwTapsLds;
+    };
     // fp32 NCHW small windows (C*R*S <= 64, K <= 64): output rows per
     // workgroup so that there are about kNchwTileWgs workgroups and a
     // block's staged input rows fit kNchwTileLds; 0 where it does not apply.
@@ -217,6 +226,24 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force, bool
             if (nchw_strip_fits(kNchwStripVariants[v])) {
                 d.kernel = KERN_NCHW_STRIP;
                 d.variant = v;
+            }
+        }
+        // Filter widths 2 and 3 that the strip kernel does not take (padded
+        // columns), and width 2: the tap-plane kernel, 64 x 64 tiles, or
+        // 64 x 128 while that still gives about 1.5 tiles per CU.  Measured
+        // cold against the pipelined kernel on padded 3x3 layers it ran 1.1
+        // to 1.45 times faster (the 128-channel layer at 28x28 1.9 times
+        // faster than the pipelined kernel's default tile for it); on the
+        // encoder's 2x2 64->128 layer 7 % faster than the strip kernel, on
+        // its 2x2 128->256 layer within 3 %.  On the encoder's 3x3 stride-2
+        // layer the strip kernel stays 14 % ahead: its 16-byte row loads
+        // move the window with a quarter of the load instructions, which
+        // counts once the input comes from HBM.
+        if (p.S >= 2 && !(p.S == 3 && d.kernel == KERN_NCHW_STRIP)) {
+            const int tv = p.K <= 64 ? 3 : ((d.M / 64) * ((p.K + 127) / 128) >= 384 ? 5 : 3);
+            if (nchw_taps_fits(kNchwTapsVariants[tv])) {
+                d.kernel = KERN_NCHW_TAPS;
+                d.variant = tv;
             }
         }
         // Small windows and few output channels: the whole filter in
@@ -336,6 +363,10 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force, bool
                        nchw_strip_fits(kNchwStripVariants[i])) {
                 d.kernel = KERN_NCHW_STRIP;
                 d.variant = i;
+            } else if (name == "nchwtaps" && i >= 0 && i < count_of(kNchwTapsVariants) &&
+                       nchw_taps_fits(kNchwTapsVariants[i])) {
+                d.kernel = KERN_NCHW_TAPS;
+                d.variant = i;
             } else if (name == "tile16" && i >= 0 && i < count_of(kTile16Variants) &&
                        tile16_rows(kTile16Variants[i]) > 0) {
                 d.kernel = KERN_TILE16;
@@ -421,6 +452,10 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force, bool
         d.tile_m = kNchwStripVariants[d.variant].bm;
         d.tile_n = kNchwStripVariants[d.variant].bn;
         d.tile_k = 16;
+    } else if (d.kernel == KERN_NCHW_TAPS) {
+        d.tile_m = kNchwTapsVariants[d.variant].bm;
+        d.tile_n = kNchwTapsVariants[d.variant].bn;
+        d.tile_k = 16;
     } else if (d.kernel == KERN_STRIP || d.kernel == KERN_STRIP_RB || d.kernel == KERN_STRIP_RB2) {
         const StripVariant& sv = d.kernel == KERN_STRIP      ? kStripVariants[d.variant]
                                  : d.kernel == KERN_STRIP_RB ? kStripRbVariants[d.variant]
@@ -443,7 +478,7 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force, bool
     // The small-window kernel's copy: one 16-byte A fragment per lane, 32-deep
     // step and 16-channel block.
     d.frag_pack = d.kernel == KERN_STRIP_RB || d.kernel == KERN_STRIP_RB2 || d.kernel == KERN_NCHW_STRIP ||
-                  d.kernel == KERN_TILE16;
+                  d.kernel == KERN_NCHW_TAPS || d.kernel == KERN_TILE16;
     if (d.frag_pack) {
         const int64_t kpad =
             d.kernel == KERN_STRIP_RB || d.kernel == KERN_STRIP_RB2 ? (p.K + 31) / 32 * 32 : (p.K + 15) / 16 * 16;
@@ -529,6 +564,7 @@ constexpr KernelFamily kKernelFamilies[] = {
     {"tile16", KERN_TILE16, count_of(kTile16Variants)},
     {"streamk", KERN_STREAMK, count_of(kDmaVariants)},
     {"striprb2", KERN_STRIP_RB2, count_of(kStripRb2Variants)},
+    {"nchwtaps", KERN_NCHW_TAPS, count_of(kNchwTapsVariants)},
 };
 
 // A ConvLSTM step: the gate convolution over concat(x, h) of p (C = c_x +

@@ -23,6 +23,8 @@ enum KernelId : int32_t {
                           // ranges per workgroup of a persistent grid, split tiles summed from workspace slots
     KERN_STRIP_RB2 = 10,  // the register-streamed strips with the taps unrolled (S in kStripRb2Taps, unit
                           // horizontal dilation), padded strip rows read without conflicts
+    KERN_NCHW_TAPS = 11,  // fp32 NCHW: per-tap planes of the tile's window elements (4-byte LDS-DMA
+                          // gathers), register-streamed filter, taps unrolled (S in kNchwTapsTaps, C % 16 == 0)
 };
 
 // One compiled tile shape: BM x BN output tile, BK-deep LDS stages (in 16-bit
@@ -95,6 +97,27 @@ constexpr NchwStripVariant kNchwStripVariants[] = {
     {64, 64, 2, 2, 1024, 6, 3},  {128, 32, 4, 1, 1536, 4, 3}, {64, 32, 4, 1, 1024, 4, 3},
     {64, 64, 4, 1, 1024, 4, 3},
 };
+// fp32 NCHW tap-plane kernel: BM x BN tiles over wgm x wgn waves, nbuf LDS
+// buffers of one (filter row, 16-channel block) each; compiled for the
+// filter widths in kNchwTapsTaps.
+struct NchwTapsVariant {
+    int bm, bn, wgm, wgn, nbuf;
+};
+constexpr NchwTapsVariant kNchwTapsVariants[] = {
+    {128, 64, 2, 2, 2}, {128, 64, 2, 2, 3}, {128, 128, 2, 2, 2}, {64, 64, 2, 2, 2}, {64, 64, 2, 2, 3}, {64, 128, 2, 2, 2},
+};
+constexpr int kNchwTapsTaps[] = {2, 3};
+// LDS bytes of one buffer of the tap-plane kernel: 16 channels x S taps
+// planes of nchw_taps_plane(bm, S) words.
+constexpr int32_t nchw_taps_plane(int32_t bm, int32_t S) {
+    for (int32_t p = bm; p < bm + 64; ++p)
+        if ((4 * S * p) % 64 == 16 || (4 * S * p) % 64 == 48) return p;
+    return bm;
+}
+constexpr int64_t nchw_taps_lds(int32_t bm, int32_t S, int32_t nbuf) {
+    return int64_t(nbuf) * 16 * S * nchw_taps_plane(bm, S) * 4;
+}
+constexpr int64_t kNchwTapsLds = 81920;   // two workgroups per CU
 // fp32 NCHW small-window kernel: ks 16-deep steps (C*R*S <= 16*ks), tn
 // 16-channel blocks (K <= 16*tn).
 struct NchwTileVariant {

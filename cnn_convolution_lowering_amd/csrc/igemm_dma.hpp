@@ -68,21 +68,31 @@ __device__ __forceinline__ int div_small(int a, int d, float rcp) {
     return q;
 }
 
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-// 16 bytes from rsrc+voffset into LDS at m0 + 16*lane (m0 wave-uniform).
-__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voffset, uint32_t m0) {
-    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-                 :
-                 : "v"(voffset), "s"(rsrc), "s"(m0)
-                 : "memory", "m0");
+// The descriptor as the buffer-resource type of the LDS-DMA builtins.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t as_rsrc(i32x4 r) {
+    const uint64_t a = (uint64_t(uint32_t(r[1]) & 0xffff) << 32) | uint32_t(r[0]);
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(a), 0, r[2], r[3]);
 }
-#pragma clang diagnostic pop
 
+// 16 bytes from rsrc+voffset into LDS at m0 + 16*lane (m0 wave-uniform).
+// Issued through the builtin, so that the compiler counts these loads in its
+// own vmcnt bookkeeping: its waits for the registers of later ordinary loads
+// then leave LDS-DMA loads issued after those registers' loads in flight.
+// The compiler does not order LDS reads after these writes: every read of
+// data they bring waits on vmcnt explicitly (wait_vmcnt) and, across
+// waves, behind a barrier.
+__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voffset, uint32_t m0) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(as_rsrc(rsrc), (__attribute__((address_space(3))) void*)uintptr_t(m0), 16,
+                                             voffset, 0, 0, 0);
+}
+
+// Wait until at most N vector-memory loads of this wave are in flight (the
+// s_waitcnt builtin, which the compiler's own vmcnt bookkeeping takes into
+// account).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
-    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
 }
 
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" : : : "memory"); }

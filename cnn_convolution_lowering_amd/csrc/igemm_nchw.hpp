@@ -27,16 +27,12 @@
 
 namespace convlower {
 
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-// 4 bytes from rsrc+voffset into LDS at m0 + 4*lane (m0 wave-uniform).
+// 4 bytes from rsrc+voffset into LDS at m0 + 4*lane (m0 wave-uniform); the
+// builtin, as dma16.
 __device__ __forceinline__ void dma4(i32x4 rsrc, uint32_t voffset, uint32_t m0) {
-    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen lds"
-                 :
-                 : "v"(voffset), "s"(rsrc), "s"(m0)
-                 : "memory", "m0");
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(as_rsrc(rsrc), (__attribute__((address_space(3))) void*)uintptr_t(m0), 4,
+                                             voffset, 0, 0, 0);
 }
-#pragma clang diagnostic pop
 
 // Contraction position (c, r, s) of a wave-uniform element index, stepped
 // forward without division.

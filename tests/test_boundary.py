@@ -462,3 +462,26 @@ def test_tile_order_plan():
     c = cl.Conv2d(32, 128, 64, 64, 128, 11, 11, padding=5, layout="nhwc", dtype="f16", algo="implicit",
                   plan="striprb:5:1:2")
     assert c.info["kernel"] == 5 and c.info["tile_order"] == 0
+
+
+def test_tap_plane_plan():
+    """fp32 NCHW with C a multiple of 16: 3-wide filters without horizontal
+    padding stay on the row-strip kernel (6); 2-wide filters, and 2- or
+    3-wide filters with padded columns (which the row strips cannot take),
+    go to the tap-plane kernel (11) with its packed filter in the workspace;
+    other widths are not compiled there, and a forced plan checks the width."""
+    def plan(N, C, H, W, K, R, S, st, pd, forced=None):
+        c = cl.Conv2d(N, C, H, W, K, R, S, stride=st, padding=pd, layout="nchw", dtype="f32", algo="implicit",
+                      plan=forced)
+        return c.info["kernel"], c.info["kernel_variant"], c.info["ws_bytes"]
+    assert plan(1280, 32, 30, 30, 64, 3, 3, 2, 0)[0] == 6
+    assert plan(1280, 64, 14, 14, 128, 2, 2, 2, 0)[:2] == (11, 5)
+    assert plan(1280, 128, 7, 7, 256, 2, 2, 2, 0)[:2] == (11, 3)
+    k, v, ws = plan(64, 64, 28, 28, 64, 3, 3, 1, 1)
+    assert (k, v) == (11, 3) and ws == 64 * 64 * 9 * 4   # the fp32 fragment copy, K padded to 16
+    assert plan(32, 128, 28, 28, 128, 3, 3, 1, 1)[:2] == (11, 5)
+    assert plan(8, 32, 20, 20, 64, 5, 5, 1, 2)[0] != 11          # width 5: not compiled
+    assert plan(8, 24, 20, 20, 64, 3, 3, 1, 1)[0] != 11          # C not a multiple of 16
+    assert plan(8, 32, 20, 20, 64, 5, 5, 1, 2, "nchwtaps:0")[0] != 11
+    for v in range(6):
+        assert plan(8, 32, 20, 20, 64, 3, 3, 1, 1, "nchwtaps:%d" % v)[:2] == (11, v)

@@ -22,7 +22,7 @@ from parity import TORCH_DT, assert_parity, to_f64
 pytestmark = pytest.mark.gpu
 
 # kernel name -> (plan_info kernel id, number of compiled variants)
-KERNELS = {"reg": (0, 3), "dma": (1, 12), "wide": (2, 9), "nchw": (3, 12), "strip": (4, 5), "striprb": (5, 9), "nchwstrip": (6, 10), "nchwtile": (7, 6), "tile16": (8, 11), "streamk": (9, 12), "striprb2": (10, 2)}
+KERNELS = {"reg": (0, 3), "dma": (1, 12), "wide": (2, 9), "nchw": (3, 12), "strip": (4, 5), "striprb": (5, 9), "nchwstrip": (6, 10), "nchwtile": (7, 6), "tile16": (8, 11), "streamk": (9, 12), "striprb2": (10, 2), "nchwtaps": (11, 6)}
 # kernels compiled for some variants only
 VARIANTS = {"streamk": (8,)}
 
@@ -47,6 +47,20 @@ SHAPES_NCHW_F32 = [
     (2, 16, 13, 22, 40, 3, 4, (1, 1), (1, 0), (1, 1)),
     (1, 48, 20, 17, 70, 2, 3, (1, 2), (0, 0), (2, 1)),
     (2, 32, 9, 40, 33, 3, 2, (2, 1), (2, 0), (1, 3)),
+]
+# fp32 NCHW tap planes (filter widths 2 and 3, C % 16 == 0, any padding):
+# the encoder's strided layers, padding on both axes, dilation on both
+# axes, stride 3, ragged pixel and channel tiles, and strip counts (R times
+# the 16-channel blocks) that leave a last strip outside the three-buffer
+# variants' two-strip passes
+SHAPES_NCHW_TAPS = [
+    (3, 32, 30, 30, 64, 3, 3, (2, 2), (0, 0), (1, 1)),
+    (2, 64, 14, 14, 128, 2, 2, (2, 2), (0, 0), (1, 1)),
+    (2, 128, 7, 7, 256, 2, 2, (2, 2), (0, 0), (1, 1)),
+    (2, 16, 13, 22, 40, 3, 3, (1, 1), (1, 1), (1, 1)),
+    (1, 48, 20, 17, 70, 2, 3, (1, 2), (0, 1), (2, 1)),
+    (2, 32, 9, 40, 33, 3, 2, (2, 1), (2, 1), (1, 3)),
+    (1, 16, 5, 70, 20, 3, 3, (3, 3), (1, 1), (1, 1)),
 ]
 # fp32 NCHW small windows (C*R*S <= 64, K <= 64): padding, strides, dilation, ragged pixel blocks
 SHAPES_SMALL_KG = [
@@ -104,6 +118,7 @@ PLANS = [
     ("striprb", "f16", "nhwc", "implicit", SHAPES_C32),
     ("striprb", "bf16", "nhwc", "implicit", SHAPES_C32[:3]),
     ("nchwstrip", "f32", "nchw", "implicit", SHAPES_NCHW_F32),
+    ("nchwtaps", "f32", "nchw", "implicit", SHAPES_NCHW_TAPS),
     ("nchwtile", "f32", "nchw", "implicit", SHAPES_SMALL_KG),
     ("tile16", "bf16", "nhwc", "implicit", SHAPES_TILE16),
     ("tile16", "f16", "nhwc", "implicit", SHAPES_TILE16),
@@ -183,6 +198,26 @@ def test_forced_kernel_integer_exact(dev):
         y = d.forward(xl.to(dev), wl.to(dev), b.to(dev))
         torch.cuda.synchronize()
         assert torch.equal(y.cpu().view(torch.int16), want.view(torch.int16)), forced
+
+
+def test_tap_plane_kernel_integer_exact(dev):
+    """Integer inputs through every variant of the fp32 tap-plane kernel (a
+    strided, padded 3x3 layer and a 2x2 one): exact fp32 sums, so the result
+    equals the reference bit for bit."""
+    for (N, C, H, W, K, R, S, st, pd) in ((2, 32, 15, 16, 48, 3, 3, 2, 1), (3, 48, 11, 9, 70, 2, 2, 2, 0)):
+        g = torch.Generator().manual_seed(79 + R)
+        x = torch.randint(-2, 3, (N, C, H, W), generator=g).to(torch.float32)
+        w = torch.randint(-2, 3, (K, C, R, S), generator=g).to(torch.float32)
+        b = torch.randint(-4, 5, (K,), generator=g).to(torch.float32)
+        want = torch.from_numpy(oracle.conv2d(x, w, b, layout="nchw", stride=st, padding=pd)).to(torch.float32)
+        for v in range(KERNELS["nchwtaps"][1]):
+            d = cl.Conv2d(N, C, H, W, K, R, S, stride=st, padding=pd, layout="nchw", dtype="f32", algo="implicit",
+                          plan="nchwtaps:%d" % v)
+            assert d.info["kernel"] == KERNELS["nchwtaps"][0] and d.info["kernel_variant"] == v, v
+            print("int case nchwtaps:%d R=%d" % (v, R), flush=True)
+            y = d.forward(x.to(dev), w.to(dev), b.to(dev))
+            torch.cuda.synchronize()
+            assert torch.equal(y.cpu(), want), (v, R)
 
 
 def test_small_window_kernel_integer_exact(dev):
