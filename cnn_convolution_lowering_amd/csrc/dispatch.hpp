@@ -25,6 +25,8 @@ enum KernelId : int32_t {
                           // horizontal dilation), padded strip rows read without conflicts
     KERN_NCHW_TAPS = 11,  // fp32 NCHW: per-tap planes of the tile's window elements (4-byte LDS-DMA
                           // gathers), register-streamed filter, taps unrolled (S in kNchwTapsTaps, C % 16 == 0)
+    KERN_STRIP_RB3 = 12,  // the unrolled-tap strips on 16x16x32 MFMAs (S in kStripRb2Taps, unit horizontal
+                          // dilation), 96-byte strip rows
 };
 
 // One compiled tile shape: BM x BN output tile, BK-deep LDS stages (in 16-bit
@@ -79,6 +81,10 @@ constexpr StripVariant kStripRb2Variants[] = {
     {512, 128, 4, 1, 3584, 2}, {256, 128, 4, 1, 1792, 1},
 };
 constexpr int kStripRb2Taps[] = {3, 5, 7, 9, 11};
+// The 16x16 form: the same padded rows.
+// (The filter two steps ahead instead of one measured level or slower on the
+// kernel-size layers, with more registers.)
+constexpr StripVariant kStripRb3Variants[] = {{512, 128, 4, 1, 3584, 1}, {256, 128, 4, 1, 1792, 1}};
 constexpr StripVariant kStripRbVariants[] = {
     {512, 128, 4, 1, 2816, 2}, {512, 128, 4, 1, 2816, 3}, {256, 128, 2, 2, 1536, 2},
     {128, 128, 2, 2, 1024, 2}, {256, 256, 2, 2, 1536, 2}, {512, 128, 4, 1, 2816, 4},

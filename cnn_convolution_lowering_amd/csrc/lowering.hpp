@@ -571,6 +571,28 @@ __global__ void __launch_bounds__(256) pack_filter_frag_kernel(FragPackArgs a) {
     }
 }
 
+// Filter in 16x16x32 MFMA A-fragment order (the 16x16 unrolled-tap strip
+// kernel): Af[nb][kk][lane][8] = w[nb*16 + lane%16][kk*32 + (lane/16)*8 + e]
+// (KRSC rows, contraction index (r*S + s)*C + c), zero for output channels
+// >= K.  One 16-byte chunk per thread; NB = ceil(K/16), Kg % 32 == 0.
+template <typename T>
+__global__ void __launch_bounds__(256) pack_filter_frag16_kernel(FragPackArgs a) {
+    const int KK = a.Kg / 32;
+    const int64_t total = int64_t(a.NB) * KK * 64;
+    const T* __restrict__ w = static_cast<const T*>(a.w);
+    T* __restrict__ out = static_cast<T*>(a.out);
+    for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < total; i += int64_t(gridDim.x) * 256) {
+        const int lane = int(i & 63);
+        const int64_t blk = i >> 6;
+        const int kk = int(blk % KK);
+        const int nb = int(blk / KK);
+        const int n = nb * 16 + (lane & 15);
+        u32x4 v = zero4();
+        if (n < a.K) v = load16(w + int64_t(n) * a.Kg + kk * 32 + (lane >> 4) * 8);
+        store16(out + i * 8, v);
+    }
+}
+
 // fp32 KCRS filter in the MFMA fragment order of the fp32 NCHW strip
 // kernel: contraction index k' = (r*C + c)*S + s (filter row outermost), and
 // Bf[nb][kk][lane][4] = w[nb*16 + lane%16][k' = kk*16 + 4*(lane/16) + e],
