@@ -273,6 +273,20 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force, bool
         // more, smaller pieces; interleaved timing on the kernel-size sweep's
         // 1x1 layer: 11 % faster than the 128 x 128 default)
         if (d.variant == 8 && p.R == 1 && p.S == 1 && (d.M / 256) * ((p.K + 127) / 128) >= 512) d.variant = 3;
+        // Fewer 128 x 128 tiles than CUs: 64 x 128 tiles over four waves
+        // (twice the workgroups), or for 1x1 layers 128 x 128 over four waves.
+        // conv_tune's picks on the 3x3 256- and 512-channel layers at 14x14
+        // and 7x7 (10 and 7 % faster than the default, the latter without its
+        // split) and on the 1x1 1024-channel layer at 14x14 (7 %).
+        if (d.variant == 8 && (d.M / 128) * ((p.K + 127) / 128) < 256) d.variant = (p.R == 1 && p.S == 1) ? 9 : 11;
+        else if (d.variant == 8 && p.R == 1 && p.S == 1) d.variant = 9;
+        // 3x3 with at least two 256 x 128 strip tiles per CU: the unrolled-tap
+        // strips on 16x16x32 MFMAs, 256 x 128 tiles (conv_tune's pick on the
+        // kernel-size sweep's 3x3 layer, 12 % faster than the pipelined tiles).
+        if (p.S == 3 && p.K % 128 == 0 && (d.M / 256) * (p.K / 128) >= 512 && strip3_fits(kStripRb3Variants[1])) {
+            d.kernel = KERN_STRIP_RB3;
+            d.variant = 1;
+        }
         // Filter rows of 5 taps and more, enough strip tiles to give most CUs
         // one, and output channels filling whole 128-wide tiles: the
         // register-streamed strip kernel (interleaved timing on the
@@ -396,7 +410,7 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force, bool
     // Split contraction for the pipelined DMA kernel, in two: when the
     // output tiles leave three CUs in four idle (at most 64 of them) or the
     // contraction is very long (4096 elements and more) while there are fewer
-    // than two tiles per CU, and the contraction has at least 16 tiles.  A
+    // tiles than CUs, and the contraction has at least 16 tiles.  A
     // sweep over 3x3 and 1x1 layers found more splits, or splits with ~100
     // tiles and shorter contractions, slower than none: the fp32 partials
     // cost a write and a read of ksplit*M*K*4 bytes.  Every split non-empty.
@@ -434,7 +448,7 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force, bool
         int64_t ks = 1;
         if (force_ks > 0) {
             ks = force_ks < 8 ? force_ks : 8;
-        } else if (d.kernel == KERN_DMA && tiles > 0 && tiles < 512 && nkt >= 16 && (tiles <= 64 || kc >= 4096)) {
+        } else if (d.kernel == KERN_DMA && tiles > 0 && tiles < 256 && nkt >= 16 && (tiles <= 64 || kc >= 4096)) {
             ks = 2;
         }
         if (ks > nkt) ks = nkt;

@@ -42,7 +42,7 @@ def _bits(t):
 # split contraction's partials, the register-streamed strip kernel's filter copy,
 # the fp32 strip kernel's filter copy, a lowered im2win buffer
 CASES = [
-    ("bf16", "nhwc", "implicit", (128, 512, 7, 7, 512, 3, 3), (16, 512, 7, 7, 512, 3, 3), 1, 1),
+    ("bf16", "nhwc", "implicit", (32, 512, 7, 7, 512, 3, 3), (8, 512, 7, 7, 512, 3, 3), 1, 1),
     ("f16", "nhwc", "implicit", (32, 128, 64, 64, 128, 11, 11), (4, 128, 32, 32, 128, 11, 11), 5, 1),
     ("f32", "nchw", "implicit", (1280, 32, 30, 30, 64, 3, 3), (64, 32, 30, 30, 64, 3, 3), 0, 2),
     ("f16", "nhwc", "im2win", (8, 64, 20, 20, 96, 3, 3), (2, 64, 12, 12, 96, 3, 3), 1, 1),
