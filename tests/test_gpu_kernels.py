@@ -103,6 +103,18 @@ SHAPES_RB2 = [
     (1, 32, 6, 64, 96, 7, 7, (1, 1), (3, 3), (1, 1)),
 ]
 
+# more for the 16x16 form: a last output-channel tile of one 16-channel
+# block, narrow rows for its 256-pixel tiles
+SHAPES_RB3 = [
+    (2, 64, 17, 19, 64, 3, 3, (1, 1), (1, 1), (1, 1)),
+    (1, 32, 20, 33, 48, 5, 5, (1, 1), (2, 2), (2, 1)),
+    (3, 96, 9, 70, 144, 7, 7, (2, 1), (3, 3), (1, 1)),
+    (2, 64, 12, 64, 64, 11, 11, (1, 1), (5, 5), (1, 1)),
+    (1, 32, 16, 64, 32, 9, 9, (1, 1), (4, 4), (1, 1)),
+    (2, 32, 10, 60, 160, 3, 5, (1, 1), (1, 2), (1, 1)),
+    (2, 32, 9, 30, 80, 3, 3, (1, 1), (0, 1), (1, 1)),
+]
+
 PLANS = [
     ("reg", "f32", "nhwc", "implicit", SHAPES_SMALL_C + SHAPES_C32[:2]),
     ("reg", "f16", "nchw", "implicit", SHAPES_SMALL_C[:2]),
@@ -131,8 +143,8 @@ PLANS = [
     ("streamk", "bf16", "nchw", "im2win", SHAPES_SMALL_C[:2]),
     ("striprb2", "f16", "nhwc", "implicit", SHAPES_RB2),
     ("striprb2", "bf16", "nhwc", "implicit", SHAPES_RB2[::2]),
-    ("striprb3", "f16", "nhwc", "implicit", SHAPES_RB2),
-    ("striprb3", "bf16", "nhwc", "implicit", SHAPES_RB2[1::2]),
+    ("striprb3", "f16", "nhwc", "implicit", SHAPES_RB2 + SHAPES_RB3),
+    ("striprb3", "bf16", "nhwc", "implicit", SHAPES_RB3[::2]),
 ]
 
 
