@@ -273,13 +273,18 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force, bool
         // more, smaller pieces; interleaved timing on the kernel-size sweep's
         // 1x1 layer: 11 % faster than the 128 x 128 default)
         if (d.variant == 8 && p.R == 1 && p.S == 1 && (d.M / 256) * ((p.K + 127) / 128) >= 512) d.variant = 3;
-        // Fewer 128 x 128 tiles than CUs: 64 x 128 tiles over four waves
-        // (twice the workgroups), or for 1x1 layers 128 x 128 over four waves.
-        // conv_tune's picks on the 3x3 256- and 512-channel layers at 14x14
-        // and 7x7 (10 and 7 % faster than the default, the latter without its
-        // split) and on the 1x1 1024-channel layer at 14x14 (7 %).
-        if (d.variant == 8 && (d.M / 128) * ((p.K + 127) / 128) < 256) d.variant = (p.R == 1 && p.S == 1) ? 9 : 11;
-        else if (d.variant == 8 && p.R == 1 && p.S == 1) d.variant = 9;
+        // Fewer 128 x 128 tiles than CUs and a contraction shorter than 4096:
+        // 64 x 128 tiles over four waves (twice the workgroups); 1x1 layers:
+        // 128 x 128 over four waves.  conv_tune's picks on the 3x3 256-channel
+        // layer at 14x14 (6 % faster cold) and the 1x1 1024-channel layer at
+        // 14x14 (2-7 %).  On the 3x3 512-channel layer at 7x7 (a 4608-long
+        // contraction) the 64 x 128 tiles were faster warm but 4 % slower
+        // cold than 128 x 128 tiles split in two, which stay.
+        const int64_t kc16 = implicit ? d.Kg : d.Kl;
+        if (d.variant == 8 && p.R == 1 && p.S == 1)
+            d.variant = 9;
+        else if (d.variant == 8 && (d.M / 128) * ((p.K + 127) / 128) < 256 && kc16 < 4096)
+            d.variant = 11;
         // 3x3 with at least two 256 x 128 strip tiles per CU: the unrolled-tap
         // strips on 16x16x32 MFMAs, 256 x 128 tiles (conv_tune's pick on the
         // kernel-size sweep's 3x3 layer, 12 % faster than the pipelined tiles).
