@@ -183,7 +183,8 @@ def kernel_work(l, stage):
 CONTRACT_KERNELS = ["conv_gemm_kernel", "conv_gemm_dma_kernel", "conv_gemm_wide_kernel", "conv_nchw_f32_dma_kernel",
                     "conv_strip_kernel", "conv_strip_rb_kernel", "conv_nchw_f32_strip_kernel",
                     "conv_nchw_f32_tile_kernel", "conv_nhwc_tile16_kernel", "conv_gemm_streamk_kernel",
-                    "conv_strip_rb2_kernel", "conv_nchw_f32_taps_kernel", "conv_strip_rb3_kernel"]
+                    "conv_strip_rb2_kernel", "conv_nchw_f32_taps_kernel", "conv_strip_rb3_kernel",
+                    "conv_strip_rb4_kernel"]
 
 
 def kernel_symbol(l, stage):
@@ -196,7 +197,8 @@ def kernel_symbol(l, stage):
         if info["kernel"] in (5, 10):
             return "pack_filter_frag_kernel"
         return {6: "pack_filter_frag_f32_kernel", 11: "pack_filter_frag_f32_kernel",
-                8: "pack_filter_tile16_kernel", 12: "pack_filter_frag16_kernel"}.get(info["kernel"],
+                8: "pack_filter_tile16_kernel", 12: "pack_filter_frag16_kernel",
+                13: "pack_filter_frag16_kernel"}.get(info["kernel"],
                                                                                     "pack_filter_kernel")
     # NHWC with C a whole number of 16-byte vectors: the direct vector copy;
     # fp32 window rows that are not whole vectors: the unpadded element-wise

@@ -16,6 +16,7 @@
 #include "igemm_strip_rb.hpp"
 #include "igemm_strip_rb2.hpp"
 #include "igemm_strip_rb3.hpp"
+#include "igemm_strip_rb4.hpp"
 #include "igemm_streamk.hpp"
 #include "igemm_tile16.hpp"
 #include "igemm_wide.hpp"
@@ -534,6 +535,40 @@ void launch_gemm(const conv_desc& d, const void* x, const void* w, const void* b
             }
 #undef CONVLOWER_STRIP_RB3_CASE
 #undef CONVLOWER_STRIP_RB3_LAUNCH
+        }
+        return;
+    }
+    if (d.kernel == KERN_STRIP_RB4) {
+        if constexpr (sizeof(T) == 2) {
+#define CONVLOWER_STRIP_RB4_LAUNCH(I, S_)                                                                     \
+    case S_: {                                                                                                \
+        constexpr StripVariant v = kStripRb4Variants[I];                                                      \
+        conv_strip_rb4_kernel<T, v.bm, v.bn, v.wgm, v.wgn, v.strip, S_, v.bst><<<blocks, 64 * v.wgm * v.wgn, 0, st>>>(h); \
+        break;                                                                                                \
+    }
+#define CONVLOWER_STRIP_RB4_CASE(I)                                                                           \
+    case I: {                                                                                                 \
+        constexpr StripVariant v = kStripRb4Variants[I];                                                      \
+        GemmArgs h = g;                                                                                       \
+        h.tiles_n = int32_t((d.p.K + v.bn - 1) / v.bn);                                                       \
+        const uint32_t blocks = uint32_t(((uint64_t(d.M) + v.bm - 1) / v.bm) * h.tiles_n);                   \
+        switch (d.p.S) {                                                                                      \
+            CONVLOWER_STRIP_RB4_LAUNCH(I, 3)                                                                  \
+            CONVLOWER_STRIP_RB4_LAUNCH(I, 5)                                                                  \
+            CONVLOWER_STRIP_RB4_LAUNCH(I, 7)                                                                  \
+            CONVLOWER_STRIP_RB4_LAUNCH(I, 9)                                                                  \
+            CONVLOWER_STRIP_RB4_LAUNCH(I, 11)                                                                 \
+            default: break;                                                                                   \
+        }                                                                                                     \
+        break;                                                                                                \
+    }
+            static_assert(count_of(kStripRb4Variants) == 1, "compiled variants");
+            switch (d.variant) {
+                CONVLOWER_STRIP_RB4_CASE(0)
+                default: break;
+            }
+#undef CONVLOWER_STRIP_RB4_CASE
+#undef CONVLOWER_STRIP_RB4_LAUNCH
         }
         return;
     }

@@ -181,7 +181,9 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force, bool
     auto strip2_fits = [&](const StripVariant& v) {
         bool taps = false;
         for (int t : kStripRb2Taps) taps = taps || p.S == t;
-        const int64_t rows = (v.bm - 1) / d.Q + 2;
+        // output rows a tile touches: bm / Q where Q divides bm (tiles start
+        // on a row), else at most (bm - 1) / Q + 2
+        const int64_t rows = v.bm % d.Q == 0 ? v.bm / d.Q : (v.bm - 1) / d.Q + 2;
         return wide_ok && taps && p.dil_w == 1 && rows * d.W_used * 5 <= v.strip;
     };
     // Its 16x16 form: the same.
@@ -324,6 +326,16 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force, bool
                 }
             }
         }
+        // Up to 7 taps, with at least two 256 x 128 strip tiles per CU: the
+        // same strips with the filter shared through LDS, two workgroups per
+        // CU (interleaved timing on the kernel-size layers: 5 % faster at
+        // 3 x 3 and 5 x 5, 1 % at 7 x 7; 1 % and 3 % slower at 9 x 9 and
+        // 11 x 11, which keep the 512 x 128 tiles).
+        if ((p.S == 3 || p.S == 5 || p.S == 7) && p.K % 128 == 0 && (d.M / 256) * (p.K / 128) >= 512 &&
+            (d.kernel == KERN_STRIP_RB3 || d.kernel == KERN_STRIP_RB2) && strip3_fits(kStripRb4Variants[0])) {
+            d.kernel = KERN_STRIP_RB4;
+            d.variant = 0;
+        }
     } else {
         d.kernel = KERN_REG;
         d.variant = p.K <= 32 ? 2 : (p.K <= 64 ? 1 : 0);
@@ -394,6 +406,10 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force, bool
             } else if (name == "striprb3" && i >= 0 && i < count_of(kStripRb3Variants) &&
                        strip3_fits(kStripRb3Variants[i])) {
                 d.kernel = KERN_STRIP_RB3;
+                d.variant = i;
+            } else if (name == "striprb4" && i >= 0 && i < count_of(kStripRb4Variants) &&
+                       strip3_fits(kStripRb4Variants[i])) {
+                d.kernel = KERN_STRIP_RB4;
                 d.variant = i;
             } else if (name == "nchwtaps" && i >= 0 && i < count_of(kNchwTapsVariants) &&
                        nchw_taps_fits(kNchwTapsVariants[i])) {
@@ -489,11 +505,12 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force, bool
         d.tile_n = kNchwTapsVariants[d.variant].bn;
         d.tile_k = 16;
     } else if (d.kernel == KERN_STRIP || d.kernel == KERN_STRIP_RB || d.kernel == KERN_STRIP_RB2 ||
-               d.kernel == KERN_STRIP_RB3) {
+               d.kernel == KERN_STRIP_RB3 || d.kernel == KERN_STRIP_RB4) {
         const StripVariant& sv = d.kernel == KERN_STRIP       ? kStripVariants[d.variant]
                                  : d.kernel == KERN_STRIP_RB  ? kStripRbVariants[d.variant]
                                  : d.kernel == KERN_STRIP_RB2 ? kStripRb2Variants[d.variant]
-                                                              : kStripRb3Variants[d.variant];
+                                 : d.kernel == KERN_STRIP_RB3 ? kStripRb3Variants[d.variant]
+                                                              : kStripRb4Variants[d.variant];
         d.tile_m = sv.bm;
         d.tile_n = sv.bn;
         d.tile_k = 32;
@@ -512,6 +529,7 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force, bool
     // The small-window kernel's copy: one 16-byte A fragment per lane, 32-deep
     // step and 16-channel block.
     d.frag_pack = d.kernel == KERN_STRIP_RB || d.kernel == KERN_STRIP_RB2 || d.kernel == KERN_STRIP_RB3 ||
+                  d.kernel == KERN_STRIP_RB4 ||
                   d.kernel == KERN_NCHW_STRIP || d.kernel == KERN_NCHW_TAPS || d.kernel == KERN_TILE16;
     if (d.frag_pack) {
         const int64_t kpad =
@@ -600,6 +618,7 @@ constexpr KernelFamily kKernelFamilies[] = {
     {"striprb2", KERN_STRIP_RB2, count_of(kStripRb2Variants)},
     {"nchwtaps", KERN_NCHW_TAPS, count_of(kNchwTapsVariants)},
     {"striprb3", KERN_STRIP_RB3, count_of(kStripRb3Variants)},
+    {"striprb4", KERN_STRIP_RB4, count_of(kStripRb4Variants)},
 };
 
 // A ConvLSTM step: the gate convolution over concat(x, h) of p (C = c_x +
@@ -737,7 +756,7 @@ void launch_pack(const conv_desc& d, const void* w, void* out, hipStream_t st) {
         }
         return;
     }
-    if (d.frag_pack && d.kernel == KERN_STRIP_RB3) {
+    if (d.frag_pack && (d.kernel == KERN_STRIP_RB3 || d.kernel == KERN_STRIP_RB4)) {
         if constexpr (sizeof(T) == 2) {
             const int32_t NB = int32_t((d.p.K + 15) / 16);
             FragPackArgs a{w, out, int32_t(d.p.K), int32_t(d.Kg), NB};

@@ -26,7 +26,8 @@ enum KernelId : int32_t {
     KERN_NCHW_TAPS = 11,  // fp32 NCHW: per-tap planes of the tile's window elements (4-byte LDS-DMA
                           // gathers), register-streamed filter, taps unrolled (S in kNchwTapsTaps, C % 16 == 0)
     KERN_STRIP_RB3 = 12,  // the unrolled-tap strips on 16x16x32 MFMAs (S in kStripRb2Taps, unit horizontal
-                          // dilation), 96-byte strip rows
+                          // dilation), 80-byte strip rows
+    KERN_STRIP_RB4 = 13,  // the same with each tap's filter fragments loaded once per workgroup into an LDS ring
 };
 
 // One compiled tile shape: BM x BN output tile, BK-deep LDS stages (in 16-bit
@@ -85,6 +86,10 @@ constexpr int kStripRb2Taps[] = {3, 5, 7, 9, 11};
 // (The filter two steps ahead instead of one measured level or slower on the
 // kernel-size layers, with more registers.)
 constexpr StripVariant kStripRb3Variants[] = {{512, 128, 4, 1, 3584, 1}, {256, 128, 4, 1, 1792, 1}};
+// The LDS-shared filter form: bst = how many taps ahead the filter slots are
+// loaded (a ring of bst + 1 slots of BN/16 KiB beside the two strip buffers;
+// 80 KiB in all, two workgroups per CU).
+constexpr StripVariant kStripRb4Variants[] = {{256, 128, 4, 1, 1792, 2}};
 constexpr StripVariant kStripRbVariants[] = {
     {512, 128, 4, 1, 2816, 2}, {512, 128, 4, 1, 2816, 3}, {256, 128, 2, 2, 1536, 2},
     {128, 128, 2, 2, 1024, 2}, {256, 256, 2, 2, 1536, 2}, {512, 128, 4, 1, 2816, 4},

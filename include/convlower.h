@@ -143,8 +143,10 @@ typedef struct {
      * tile's pixels gathered by 4-byte LDS-DMA loads into a plane of its own
      * (any padding, stride and dilation; filter widths 2 and 3; C % 16 == 0),
      * read without bank conflicts, filter streamed as for 6, 12 the
-     * unrolled-tap strips of 10 on 16x16x32 MFMAs (strip rows padded to 96
-     * bytes; the filter copy in 16x16x32 fragment order);
+     * unrolled-tap strips of 10 on 16x16x32 MFMAs (the same 80-byte strip
+     * rows; the filter copy in 16x16x32 fragment order), 13 the strips of 12
+     * with each tap's filter fragments loaded once per workgroup into a ring
+     * of LDS slots a few taps ahead and read from there by every wave;
      * kernel_variant indexes that kernel's compiled tile shapes (for 9 the
      * shapes of 1) */
     int32_t kernel, kernel_variant;
@@ -195,7 +197,7 @@ conv_status_t conv_create_desc(const conv_params_t* p, conv_desc_t* out);
  * "<kernel>:<variant>", "<kernel>:<variant>:<ksplit>" or
  * "<kernel>:<variant>:<ksplit>:<tile order>" with kernel one of reg, dma,
  * wide, nchw, strip, striprb, nchwstrip, nchwtile, tile16, streamk,
- * striprb2, nchwtaps, striprb3 (the numbering of conv_plan_info_t.kernel,
+ * striprb2, nchwtaps, striprb3, striprb4 (the numbering of conv_plan_info_t.kernel,
  * in that order) and
  * variant an index
  * into that kernel's compiled tile shapes; ksplit (1-8) splits the

@@ -425,7 +425,7 @@ def test_streamk_plan():
             if low:
                 assert i["ws_partial_offset"] >= i["ws_lowered_offset"] + low
     c = cl.Conv2d(32, 128, 64, 64, 128, 3, 3, padding=1, layout="nhwc", dtype="f16", algo="implicit")
-    assert c.info["kernel"] == 12 and c.info["ws_partial_bytes"] == 0   # the 16x16 strip kernel
+    assert c.info["kernel"] == 13 and c.info["ws_partial_bytes"] == 0   # the LDS-shared-filter strip kernel
     c = cl.Conv2d(64, 256, 14, 14, 256, 3, 3, padding=1, layout="nhwc", dtype="f16", algo="implicit", plan="dma:8")
     assert (c.info["kernel"], c.info["ksplit"], c.info["ws_partial_bytes"]) == (1, 1, 0)
     c = cl.Conv2d(2, 64, 17, 17, 72, 3, 3, padding=1, layout="nhwc", dtype="f16", algo="implicit", plan="streamk:8")
