@@ -323,6 +323,10 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force, bool
                 if (strip3_fits(kStripRb3Variants[0])) {
                     d.kernel = KERN_STRIP_RB3;
                     d.variant = 0;
+                    // the same tiles with a strip buffer cut to what the rows
+                    // need where they fit it (two fewer strip loads a lane;
+                    // about 1 % at 9 x 9 and 11 x 11)
+                    if (strip3_fits(kStripRb3Variants[2])) d.variant = 2;
                 }
             }
         }

@@ -85,7 +85,10 @@ constexpr int kStripRb2Taps[] = {3, 5, 7, 9, 11};
 // The 16x16 form: the same padded rows.
 // (The filter two steps ahead instead of one measured level or slower on the
 // kernel-size layers, with more registers.)
-constexpr StripVariant kStripRb3Variants[] = {{512, 128, 4, 1, 3584, 1}, {256, 128, 4, 1, 1792, 1}};
+// Variant 2: variant 0's tiles with strip buffers of 48 KiB (eight output
+// rows of up to 76 strip rows where Q divides 512).
+constexpr StripVariant kStripRb3Variants[] = {
+    {512, 128, 4, 1, 3584, 1}, {256, 128, 4, 1, 1792, 1}, {512, 128, 4, 1, 3072, 1}};
 // The LDS-shared filter form: bst = how many taps ahead the filter slots are
 // loaded (a ring of bst + 1 slots of BN/16 KiB beside the two strip buffers;
 // 80 KiB in all, two workgroups per CU).
