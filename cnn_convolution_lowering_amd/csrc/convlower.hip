@@ -334,11 +334,13 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force, bool
         // same strips with the filter shared through LDS, two workgroups per
         // CU (interleaved timing on the kernel-size layers: 5 % faster at
         // 3 x 3 and 5 x 5, 1 % at 7 x 7; 1 % and 3 % slower at 9 x 9 and
-        // 11 x 11, which keep the 512 x 128 tiles).
+        // 11 x 11, which keep the 512 x 128 tiles).  Where the rows fit the
+        // smaller strip buffers, those with the filter three taps ahead
+        // (another 3 % at 3 x 3, 1 % at 5 x 5 and 7 x 7).
         if ((p.S == 3 || p.S == 5 || p.S == 7) && p.K % 128 == 0 && (d.M / 256) * (p.K / 128) >= 512 &&
             (d.kernel == KERN_STRIP_RB3 || d.kernel == KERN_STRIP_RB2) && strip3_fits(kStripRb4Variants[0])) {
             d.kernel = KERN_STRIP_RB4;
-            d.variant = 0;
+            d.variant = strip3_fits(kStripRb4Variants[1]) ? 1 : 0;
         }
     } else {
         d.kernel = KERN_REG;

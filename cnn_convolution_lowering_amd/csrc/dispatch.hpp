@@ -91,8 +91,10 @@ constexpr StripVariant kStripRb3Variants[] = {
     {512, 128, 4, 1, 3584, 1}, {256, 128, 4, 1, 1792, 1}, {512, 128, 4, 1, 3072, 1}};
 // The LDS-shared filter form: bst = how many taps ahead the filter slots are
 // loaded (a ring of bst + 1 slots of BN/16 KiB beside the two strip buffers;
-// 80 KiB in all, two workgroups per CU).
-constexpr StripVariant kStripRb4Variants[] = {{256, 128, 4, 1, 1792, 2}};
+// 80 KiB in all, two workgroups per CU).  Variant 1: strip buffers of 24 KiB
+// (four output rows of up to 76 strip rows where Q divides 256) and the
+// filter three taps ahead.
+constexpr StripVariant kStripRb4Variants[] = {{256, 128, 4, 1, 1792, 2}, {256, 128, 4, 1, 1536, 3}};
 constexpr StripVariant kStripRbVariants[] = {
     {512, 128, 4, 1, 2816, 2}, {512, 128, 4, 1, 2816, 3}, {256, 128, 2, 2, 1536, 2},
     {128, 128, 2, 2, 1024, 2}, {256, 256, 2, 2, 1536, 2}, {512, 128, 4, 1, 2816, 4},
