@@ -184,7 +184,7 @@ CONTRACT_KERNELS = ["conv_gemm_kernel", "conv_gemm_dma_kernel", "conv_gemm_wide_
                     "conv_strip_kernel", "conv_strip_rb_kernel", "conv_nchw_f32_strip_kernel",
                     "conv_nchw_f32_tile_kernel", "conv_nhwc_tile16_kernel", "conv_gemm_streamk_kernel",
                     "conv_strip_rb2_kernel", "conv_nchw_f32_taps_kernel", "conv_strip_rb3_kernel",
-                    "conv_strip_rb4_kernel"]
+                    "conv_strip_rb4_kernel", "conv_1x1_stream_kernel"]
 
 
 def kernel_symbol(l, stage):

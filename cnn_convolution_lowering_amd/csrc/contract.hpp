@@ -17,6 +17,7 @@
 #include "igemm_strip_rb2.hpp"
 #include "igemm_strip_rb3.hpp"
 #include "igemm_strip_rb4.hpp"
+#include "igemm_stream1x1.hpp"
 #include "igemm_streamk.hpp"
 #include "igemm_tile16.hpp"
 #include "igemm_wide.hpp"
@@ -536,6 +537,36 @@ void launch_gemm(const conv_desc& d, const void* x, const void* w, const void* b
             }
 #undef CONVLOWER_STRIP_RB3_CASE
 #undef CONVLOWER_STRIP_RB3_LAUNCH
+        }
+        return;
+    }
+    if (d.kernel == KERN_STREAM1X1) {
+        if constexpr (sizeof(T) == 2) {
+            // persistent: minb workgroups per CU, at most one 16-pixel block
+            // per wave to start with
+            auto launch = [&](auto kernel, int minb) {
+                const int64_t waves = (d.M + 15) / 16;
+                const uint32_t blocks = uint32_t(std::max<int64_t>(
+                    1, std::min<int64_t>((waves + 3) / 4, int64_t(minb) * kStreamKCus)));
+                kernel<<<blocks, 256, 0, st>>>(g);
+            };
+#define CONVLOWER_STREAM1X1_CASE(I)                                                                        \
+    case I: {                                                                                              \
+        constexpr Stream1x1Variant v = kStream1x1Variants[I];                                              \
+        if (d.p.C == 32) launch(conv_1x1_stream_kernel<T, 1, v.d, v.minb>, v.minb);                        \
+        else if (d.p.C == 64) launch(conv_1x1_stream_kernel<T, 2, v.d, v.minb>, v.minb);                   \
+        else if (d.p.C == 128) launch(conv_1x1_stream_kernel<T, 4, v.d, v.minb>, v.minb);                  \
+        break;                                                                                             \
+    }
+            static_assert(count_of(kStream1x1Variants) == 4, "compiled variants");
+            switch (d.variant) {
+                CONVLOWER_STREAM1X1_CASE(0)
+                CONVLOWER_STREAM1X1_CASE(1)
+                CONVLOWER_STREAM1X1_CASE(2)
+                CONVLOWER_STREAM1X1_CASE(3)
+                default: break;
+            }
+#undef CONVLOWER_STREAM1X1_CASE
         }
         return;
     }

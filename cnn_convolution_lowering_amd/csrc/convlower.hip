@@ -195,6 +195,12 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force, bool
                            (p.C * int64_t(p.stride_w)) % 2 == 0 && (p.W * int64_t(p.C)) % 2 == 0 &&
                            p.S * int64_t(p.C) <= 256 && p.pad_w <= 65536 &&
                            uint64_t(p.C) * p.H * p.W * e < (uint64_t(1) << 31);
+    // The streaming 1x1 kernel: unit stride and no padding make x the
+    // pixel-row matrix itself; its whole filter fits one LDS fragment copy.
+    const bool stream1x1_ok = p.dtype != CONV_F32 && nhwc && d.elided && p.R == 1 && p.S == 1 &&
+                              p.stride_h == 1 && p.stride_w == 1 && p.pad_h == 0 && p.pad_w == 0 &&
+                              (p.C == 32 || p.C == 64 || p.C == 128) && p.K <= 128 && p.K % 4 == 0 &&
+                              x_bytes < (uint64_t(1) << 31) && uint64_t(d.M) * p.K * e < (uint64_t(1) << 31);
     // Its output rows per tile for a variant (the window rows in at most
     // 4*ks chunks, K <= 16*tn*split): about kTile16Tiles tiles, two tiles' staged
     // rows within kTile16Lds; 0 where it does not apply.
@@ -287,6 +293,16 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force, bool
             d.variant = 9;
         else if (d.variant == 8 && (d.M / 128) * ((p.K + 127) / 128) < 256 && kc16 < 4096)
             d.variant = 11;
+        // 1x1 layers the streaming kernel takes, from 16384 pixels: it
+        // (C = K = 128 at 64x64, by interleaved timing after a 512 MiB
+        // read-modify-write pass: 13 % faster than the 256 x 128 tiles at 32
+        // images, 21 % at 128; 13 % faster than 128 x 128 tiles at 8 images)
+        // -- two workgroups per CU with two blocks in flight per wave below
+        // 131072 pixels, one with four from there.
+        if (stream1x1_ok && d.M >= 16384) {
+            d.kernel = KERN_STREAM1X1;
+            d.variant = d.M >= 131072 ? 3 : 2;
+        }
         // 3x3 with at least two 256 x 128 strip tiles per CU: the unrolled-tap
         // strips on 16x16x32 MFMAs, 256 x 128 tiles (conv_tune's pick on the
         // kernel-size sweep's 3x3 layer, 12 % faster than the pipelined tiles).
@@ -413,6 +429,9 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force, bool
                        strip3_fits(kStripRb3Variants[i])) {
                 d.kernel = KERN_STRIP_RB3;
                 d.variant = i;
+            } else if (name == "stream1x1" && stream1x1_ok && i >= 0 && i < count_of(kStream1x1Variants)) {
+                d.kernel = KERN_STREAM1X1;
+                d.variant = i;
             } else if (name == "striprb4" && i >= 0 && i < count_of(kStripRb4Variants) &&
                        strip3_fits(kStripRb4Variants[i])) {
                 d.kernel = KERN_STRIP_RB4;
@@ -506,6 +525,10 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force, bool
         d.tile_m = kNchwStripVariants[d.variant].bm;
         d.tile_n = kNchwStripVariants[d.variant].bn;
         d.tile_k = 16;
+    } else if (d.kernel == KERN_STREAM1X1) {
+        d.tile_m = 16;
+        d.tile_n = 128;
+        d.tile_k = 32;
     } else if (d.kernel == KERN_NCHW_TAPS) {
         d.tile_m = kNchwTapsVariants[d.variant].bm;
         d.tile_n = kNchwTapsVariants[d.variant].bn;
@@ -625,6 +648,7 @@ constexpr KernelFamily kKernelFamilies[] = {
     {"nchwtaps", KERN_NCHW_TAPS, count_of(kNchwTapsVariants)},
     {"striprb3", KERN_STRIP_RB3, count_of(kStripRb3Variants)},
     {"striprb4", KERN_STRIP_RB4, count_of(kStripRb4Variants)},
+    {"stream1x1", KERN_STREAM1X1, count_of(kStream1x1Variants)},
 };
 
 // A ConvLSTM step: the gate convolution over concat(x, h) of p (C = c_x +

@@ -28,6 +28,9 @@ enum KernelId : int32_t {
     KERN_STRIP_RB3 = 12,  // the unrolled-tap strips on 16x16x32 MFMAs (S in kStripRb2Taps, unit horizontal
                           // dilation), 80-byte strip rows
     KERN_STRIP_RB4 = 13,  // the same with each tap's filter fragments loaded once per workgroup into an LDS ring
+    KERN_STREAM1X1 = 14,  // 16-bit NHWC 1x1, unit stride, no padding, C in {32, 64, 128}, K <= 128 and a multiple
+                          // of 4: persistent waves streaming 16-pixel blocks through LDS rings, the filter in
+                          // registers
 };
 
 // One compiled tile shape: BM x BN output tile, BK-deep LDS stages (in 16-bit
@@ -94,6 +97,12 @@ constexpr StripVariant kStripRb3Variants[] = {
 // 80 KiB in all, two workgroups per CU).  Variant 1: strip buffers of 24 KiB
 // (four output rows of up to 76 strip rows where Q divides 256) and the
 // filter three taps ahead.
+// The streaming 1x1 kernel: d = pixel blocks in flight per wave, minb =
+// workgroups per CU (the persistent grid is minb per CU).
+struct Stream1x1Variant {
+    int d, minb;
+};
+constexpr Stream1x1Variant kStream1x1Variants[] = {{3, 2}, {4, 2}, {2, 2}, {4, 1}};   // d * (C/32 + 8) < 64
 constexpr StripVariant kStripRb4Variants[] = {{256, 128, 4, 1, 1792, 2}, {256, 128, 4, 1, 1536, 3}};
 constexpr StripVariant kStripRbVariants[] = {
     {512, 128, 4, 1, 2816, 2}, {512, 128, 4, 1, 2816, 3}, {256, 128, 2, 2, 1536, 2},

@@ -146,7 +146,10 @@ typedef struct {
      * unrolled-tap strips of 10 on 16x16x32 MFMAs (the same 80-byte strip
      * rows; the filter copy in 16x16x32 fragment order), 13 the strips of 12
      * with each tap's filter fragments loaded once per workgroup into a ring
-     * of LDS slots a few taps ahead and read from there by every wave;
+     * of LDS slots a few taps ahead and read from there by every wave,
+     * 14 16-bit NHWC 1x1 layers with unit stride, no padding, C of 32, 64
+     * or 128 and K <= 128: a persistent grid whose waves stream 16-pixel
+     * blocks of x (several in flight each) against the filter held in LDS;
      * kernel_variant indexes that kernel's compiled tile shapes (for 9 the
      * shapes of 1) */
     int32_t kernel, kernel_variant;
@@ -197,7 +200,7 @@ conv_status_t conv_create_desc(const conv_params_t* p, conv_desc_t* out);
  * "<kernel>:<variant>", "<kernel>:<variant>:<ksplit>" or
  * "<kernel>:<variant>:<ksplit>:<tile order>" with kernel one of reg, dma,
  * wide, nchw, strip, striprb, nchwstrip, nchwtile, tile16, streamk,
- * striprb2, nchwtaps, striprb3, striprb4 (the numbering of conv_plan_info_t.kernel,
+ * striprb2, nchwtaps, striprb3, striprb4, stream1x1 (the numbering of conv_plan_info_t.kernel,
  * in that order) and
  * variant an index
  * into that kernel's compiled tile shapes; ksplit (1-8) splits the

@@ -22,7 +22,7 @@ from parity import TORCH_DT, assert_parity, to_f64
 pytestmark = pytest.mark.gpu
 
 # kernel name -> (plan_info kernel id, number of compiled variants)
-KERNELS = {"reg": (0, 3), "dma": (1, 12), "wide": (2, 9), "nchw": (3, 12), "strip": (4, 5), "striprb": (5, 9), "nchwstrip": (6, 10), "nchwtile": (7, 6), "tile16": (8, 11), "streamk": (9, 12), "striprb2": (10, 2), "nchwtaps": (11, 6), "striprb3": (12, 3), "striprb4": (13, 2)}
+KERNELS = {"reg": (0, 3), "dma": (1, 12), "wide": (2, 9), "nchw": (3, 12), "strip": (4, 5), "striprb": (5, 9), "nchwstrip": (6, 10), "nchwtile": (7, 6), "tile16": (8, 11), "streamk": (9, 12), "striprb2": (10, 2), "nchwtaps": (11, 6), "striprb3": (12, 3), "striprb4": (13, 2), "stream1x1": (14, 4)}
 # kernels compiled for some variants only
 VARIANTS = {"streamk": (8,)}
 
@@ -103,8 +103,9 @@ SHAPES_RB2 = [
     (1, 32, 6, 64, 96, 7, 7, (1, 1), (3, 3), (1, 1)),
 ]
 
-# more for the 16x16 form: a last output-channel tile of one 16-channel
-# block, narrow rows for its 256-pixel tiles
+# more for the 16x16 forms: a last output-channel tile of one 16-channel
+# block, narrow rows for its 256-pixel tiles, one-row filters (a single
+# strip of 32 channels; two strips and a partial output-channel tile)
 SHAPES_RB3 = [
     (2, 64, 17, 19, 64, 3, 3, (1, 1), (1, 1), (1, 1)),
     (1, 32, 20, 33, 48, 5, 5, (1, 1), (2, 2), (2, 1)),
@@ -113,6 +114,20 @@ SHAPES_RB3 = [
     (1, 32, 16, 64, 32, 9, 9, (1, 1), (4, 4), (1, 1)),
     (2, 32, 10, 60, 160, 3, 5, (1, 1), (1, 2), (1, 1)),
     (2, 32, 9, 30, 80, 3, 3, (1, 1), (0, 1), (1, 1)),
+    (1, 32, 9, 40, 64, 1, 3, (1, 1), (0, 1), (1, 1)),
+    (2, 64, 8, 70, 48, 1, 7, (1, 1), (0, 3), (1, 1)),
+]
+
+# the streaming 1x1 kernel: pixel counts off the 16-row block, partial and
+# odd output-channel counts, each channel count it compiles, and one layer
+# with several blocks per wave (the persistent loop's passes and its tail)
+SHAPES_1X1 = [
+    (3, 128, 9, 13, 128, 1, 1, (1, 1), (0, 0), (1, 1)),
+    (2, 64, 7, 9, 48, 1, 1, (1, 1), (0, 0), (1, 1)),
+    (1, 32, 5, 11, 20, 1, 1, (1, 1), (0, 0), (1, 1)),
+    (2, 128, 6, 10, 100, 1, 1, (1, 1), (0, 0), (1, 1)),
+    (1, 64, 3, 5, 30, 1, 1, (1, 1), (0, 0), (1, 1)),
+    (50, 64, 64, 64, 64, 1, 1, (1, 1), (0, 0), (1, 1)),
 ]
 
 PLANS = [
@@ -147,6 +162,8 @@ PLANS = [
     ("striprb3", "bf16", "nhwc", "implicit", SHAPES_RB3[::2]),
     ("striprb4", "f16", "nhwc", "implicit", SHAPES_RB2 + SHAPES_RB3),
     ("striprb4", "bf16", "nhwc", "implicit", SHAPES_RB3[1::2]),
+    ("stream1x1", "f16", "nhwc", "implicit", SHAPES_1X1),
+    ("stream1x1", "bf16", "nhwc", "im2col", SHAPES_1X1[:4]),
 ]
 
 
