@@ -281,17 +281,18 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force, bool
         // more, smaller pieces; interleaved timing on the kernel-size sweep's
         // 1x1 layer: 11 % faster than the 128 x 128 default)
         if (d.variant == 8 && p.R == 1 && p.S == 1 && (d.M / 256) * ((p.K + 127) / 128) >= 512) d.variant = 3;
-        // Fewer 128 x 128 tiles than CUs and a contraction shorter than 4096:
-        // 64 x 128 tiles over four waves (twice the workgroups); 1x1 layers:
-        // 128 x 128 over four waves.  conv_tune's picks on the 3x3 256-channel
-        // layer at 14x14 (6 % faster cold) and the 1x1 1024-channel layer at
-        // 14x14 (2-7 %).  On the 3x3 512-channel layer at 7x7 (a 4608-long
-        // contraction) the 64 x 128 tiles were faster warm but 4 % slower
-        // cold than 128 x 128 tiles split in two, which stay.
-        const int64_t kc16 = implicit ? d.Kg : d.Kl;
+        // Fewer 128 x 128 tiles than CUs: 64 x 128 tiles over four waves
+        // (twice the workgroups) with three 64-deep stages (two workgroups
+        // per CU still fit); 1x1 layers: 128 x 128 over four waves.  On the
+        // 3x3 256-channel layer at 14x14: 6 % faster cold than the 128 x 128
+        // tiles with two stages, another 9 % with the third stage; on the 3x3
+        // 512-channel layer at 7x7 (a 4608-long contraction) level with the
+        // 128 x 128 tiles split in two, whose fp32 partials it does without
+        // (51 of the 91 MB that layer moved).  The 1x1 1024-channel layer at
+        // 14x14: 2-7 % (conv_tune's pick).
         if (d.variant == 8 && p.R == 1 && p.S == 1)
             d.variant = 9;
-        else if (d.variant == 8 && (d.M / 128) * ((p.K + 127) / 128) < 256 && kc16 < 4096)
+        else if (d.variant == 8 && (d.M / 128) * ((p.K + 127) / 128) < 256)
             d.variant = 11;
         // 1x1 layers the streaming kernel takes, from 16384 pixels: it
         // (C = K = 128 at 64x64, by interleaved timing after a 512 MiB

@@ -49,7 +49,7 @@ constexpr TileVariant kRegVariants[] = {
 constexpr TileVariant kDmaVariants[] = {
     {128, 32, 32, 4, 1, 4}, {128, 64, 32, 2, 2, 4}, {128, 128, 32, 2, 2, 4}, {256, 128, 32, 2, 2, 3},
     {256, 128, 32, 4, 2, 4}, {256, 256, 32, 4, 2, 3}, {128, 128, 64, 2, 2, 2}, {128, 128, 64, 4, 2, 2},
-    {128, 128, 64, 4, 2, 2, 1}, {128, 128, 64, 2, 2, 2, 1}, {256, 128, 64, 4, 2, 2, 1}, {64, 128, 64, 2, 2, 2, 1},
+    {128, 128, 64, 4, 2, 2, 1}, {128, 128, 64, 2, 2, 2, 1}, {256, 128, 64, 4, 2, 2, 1}, {64, 128, 64, 2, 2, 3, 1},
 };
 // The ConvLSTM step's contraction: 64 packed gate rows per tile, one wave
 // across them (the cell update needs all four gates of a hidden channel).

@@ -341,8 +341,8 @@ def test_split_contraction_plan():
     partials take ksplit*M*K*4 bytes after the other workspace parts,
     256-byte aligned, and a forced split is honoured (within the contraction
     tiles, every split non-empty)."""
-    for a in [(128, 512, 7, 7, 512, 3, 3, 1), (32, 512, 7, 7, 512, 3, 3, 1), (8, 192, 20, 20, 96, 3, 3, 1)]:
-        # 4608-long over 196 and 52 tiles; 25 tiles
+    for a in [(32, 512, 7, 7, 512, 3, 3, 1), (8, 192, 20, 20, 96, 3, 3, 1)]:
+        # 4608-long over 100 tiles of 64 x 128; 50 tiles
         c = cl.Conv2d(*a[:7], padding=a[7], layout="nhwc", dtype="bf16", algo="implicit")
         i = c.info
         assert i["kernel"] == 1 and i["ksplit"] == 2, a
@@ -350,10 +350,11 @@ def test_split_contraction_plan():
         assert i["ws_partial_offset"] % 256 == 0
         assert i["ws_partial_offset"] >= i["ws_filter_offset"] + i["ws_filter_bytes"]
         assert c.workspace_bytes == i["ws_partial_offset"] + i["ws_partial_bytes"]
-    # plenty of output tiles, a contraction of moderate length over 196 tiles
-    # (taken as 392 tiles of 64 x 128), or a short contraction: no split
+    # plenty of output tiles, 196 tiles of 128 x 128 taken as 392 of 64 x 128
+    # (a contraction of moderate length or a 4608-long one), or a short
+    # contraction: no split
     for a in [(32, 128, 64, 64, 128, 3, 3, 1), (128, 1024, 14, 14, 256, 1, 1, 0), (2, 32, 8, 8, 32, 1, 1, 0),
-              (64, 256, 14, 14, 256, 3, 3, 1)]:
+              (64, 256, 14, 14, 256, 3, 3, 1), (128, 512, 7, 7, 512, 3, 3, 1)]:
         for algo in ("implicit", "im2win", "im2col"):
             c = cl.Conv2d(*a[:7], padding=a[7], layout="nhwc", dtype="f16", algo=algo)
             assert c.info["ksplit"] == 1 and c.info["ws_partial_bytes"] == 0, (a, algo)
