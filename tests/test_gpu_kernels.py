@@ -119,8 +119,9 @@ SHAPES_RB3 = [
 ]
 
 # the streaming 1x1 kernel: pixel counts off the 16-row block, partial and
-# odd output-channel counts, each channel count it compiles, and one layer
-# with several blocks per wave (the persistent loop's passes and its tail)
+# odd output-channel counts, each channel count it compiles, and layers
+# with several blocks per wave (the persistent loop's passes and its tail,
+# the last with a pixel count off the block)
 SHAPES_1X1 = [
     (3, 128, 9, 13, 128, 1, 1, (1, 1), (0, 0), (1, 1)),
     (2, 64, 7, 9, 48, 1, 1, (1, 1), (0, 0), (1, 1)),
@@ -128,6 +129,7 @@ SHAPES_1X1 = [
     (2, 128, 6, 10, 100, 1, 1, (1, 1), (0, 0), (1, 1)),
     (1, 64, 3, 5, 30, 1, 1, (1, 1), (0, 0), (1, 1)),
     (50, 64, 64, 64, 64, 1, 1, (1, 1), (0, 0), (1, 1)),
+    (1, 32, 3, 32771, 32, 1, 1, (1, 1), (0, 0), (1, 1)),
 ]
 
 PLANS = [
