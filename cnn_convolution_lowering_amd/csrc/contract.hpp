@@ -594,10 +594,11 @@ void launch_gemm(const conv_desc& d, const void* x, const void* w, const void* b
         }                                                                                                     \
         break;                                                                                                \
     }
-            static_assert(count_of(kStripRb4Variants) == 2, "compiled variants");
+            static_assert(count_of(kStripRb4Variants) == 3, "compiled variants");
             switch (d.variant) {
                 CONVLOWER_STRIP_RB4_CASE(0)
                 CONVLOWER_STRIP_RB4_CASE(1)
+                CONVLOWER_STRIP_RB4_CASE(2)
                 default: break;
             }
 #undef CONVLOWER_STRIP_RB4_CASE

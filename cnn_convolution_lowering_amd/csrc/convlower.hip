@@ -359,6 +359,17 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force, bool
             d.kernel = KERN_STRIP_RB4;
             d.variant = strip3_fits(kStripRb4Variants[1]) ? 1 : 0;
         }
+        // From 5 taps, where the register-streamed 512 x 128 tiles were
+        // chosen: the same tiles over eight waves (two per SIMD, one
+        // workgroup per CU) with the filter shared through LDS -- one filter
+        // load per wave and tap instead of two, and 8 instead of 32 per
+        // workgroup in the register form (interleaved timing: 2-3 % faster
+        // from 7 x 7 to 11 x 11 than both, level at 5 x 5, slower at 3 x 3).
+        if (p.S >= 5 && (d.kernel == KERN_STRIP_RB3 || d.kernel == KERN_STRIP_RB4) &&
+            (d.M / 512) * (p.K / 128) >= 192 && strip3_fits(kStripRb4Variants[2])) {
+            d.kernel = KERN_STRIP_RB4;
+            d.variant = 2;
+        }
     } else {
         d.kernel = KERN_REG;
         d.variant = p.K <= 32 ? 2 : (p.K <= 64 ? 1 : 0);
