@@ -575,7 +575,8 @@ void launch_gemm(const conv_desc& d, const void* x, const void* w, const void* b
 #define CONVLOWER_STRIP_RB4_LAUNCH(I, S_)                                                                     \
     case S_: {                                                                                                \
         constexpr StripVariant v = kStripRb4Variants[I];                                                      \
-        conv_strip_rb4_kernel<T, v.bm, v.bn, v.wgm, v.wgn, v.strip, S_, v.bst><<<blocks, 64 * v.wgm * v.wgn, 0, st>>>(h); \
+        conv_strip_rb4_kernel<T, v.bm, v.bn, v.wgm, v.wgn, v.strip, S_, v.bst, kStripRb4Direct[I]>              \
+            <<<blocks, 64 * v.wgm * v.wgn, 0, st>>>(h);                                                        \
         break;                                                                                                \
     }
 #define CONVLOWER_STRIP_RB4_CASE(I)                                                                           \
@@ -594,11 +595,13 @@ void launch_gemm(const conv_desc& d, const void* x, const void* w, const void* b
         }                                                                                                     \
         break;                                                                                                \
     }
-            static_assert(count_of(kStripRb4Variants) == 3, "compiled variants");
+            static_assert(count_of(kStripRb4Variants) == 5 && count_of(kStripRb4Direct) == 5, "compiled variants");
             switch (d.variant) {
                 CONVLOWER_STRIP_RB4_CASE(0)
                 CONVLOWER_STRIP_RB4_CASE(1)
                 CONVLOWER_STRIP_RB4_CASE(2)
+                CONVLOWER_STRIP_RB4_CASE(3)
+                CONVLOWER_STRIP_RB4_CASE(4)
                 default: break;
             }
 #undef CONVLOWER_STRIP_RB4_CASE

@@ -359,16 +359,20 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force, bool
             d.kernel = KERN_STRIP_RB4;
             d.variant = strip3_fits(kStripRb4Variants[1]) ? 1 : 0;
         }
-        // From 5 taps, where the register-streamed 512 x 128 tiles were
-        // chosen: the same tiles over eight waves (two per SIMD, one
-        // workgroup per CU) with the filter shared through LDS -- one filter
-        // load per wave and tap instead of two, and 8 instead of 32 per
-        // workgroup in the register form (interleaved timing: 2-3 % faster
-        // from 7 x 7 to 11 x 11 than both, level at 5 x 5, slower at 3 x 3).
-        if (p.S >= 5 && (d.kernel == KERN_STRIP_RB3 || d.kernel == KERN_STRIP_RB4) &&
-            (d.M / 512) * (p.K / 128) >= 192 && strip3_fits(kStripRb4Variants[2])) {
+        // Where either strip form was chosen and there are enough 512 x 128
+        // tiles to give most CUs one: those tiles over eight waves (two per
+        // SIMD, one workgroup per CU) with the filter shared through LDS --
+        // one filter load per wave and tap instead of two, and 8 instead of
+        // 32 per workgroup in the register form (interleaved timing: 2-3 %
+        // faster from 7 x 7 to 11 x 11 than both).  Up to 7 taps reading the
+        // caller's KRSC filter rows, which saves the packing pass (with it, 6 %
+        // faster than the 256 x 128 tiles at 3 x 3 and 3 % at 5 x 5, 1 % at
+        // 7 x 7); from 9 taps the packed copy (the rows cost the kernel more
+        // than the pass there).
+        if ((d.kernel == KERN_STRIP_RB3 || d.kernel == KERN_STRIP_RB4) && (d.M / 512) * (p.K / 128) >= 192 &&
+            strip3_fits(kStripRb4Variants[2])) {
             d.kernel = KERN_STRIP_RB4;
-            d.variant = 2;
+            d.variant = p.S <= 7 ? 3 : 2;
         }
     } else {
         d.kernel = KERN_REG;
@@ -570,7 +574,7 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force, bool
     // The small-window kernel's copy: one 16-byte A fragment per lane, 32-deep
     // step and 16-channel block.
     d.frag_pack = d.kernel == KERN_STRIP_RB || d.kernel == KERN_STRIP_RB2 || d.kernel == KERN_STRIP_RB3 ||
-                  d.kernel == KERN_STRIP_RB4 ||
+                  (d.kernel == KERN_STRIP_RB4 && !kStripRb4Direct[d.variant]) ||
                   d.kernel == KERN_NCHW_STRIP || d.kernel == KERN_NCHW_TAPS || d.kernel == KERN_TILE16;
     if (d.frag_pack) {
         const int64_t kpad =

@@ -97,14 +97,19 @@ constexpr StripVariant kStripRb3Variants[] = {
 // 80 KiB in all, two workgroups per CU).  Variant 1: strip buffers of 24 KiB
 // (four output rows of up to 76 strip rows where Q divides 256) and the
 // filter three taps ahead.  Variant 2: 512 x 128 tiles over eight waves, 48 KiB
-// strip buffers, the filter three taps ahead (128 KiB, one workgroup per CU).
+// strip buffers, the filter three taps ahead (128 KiB, one workgroup per CU);
+// variant 3 the same reading the KRSC filter rows, variant 4 variant 1 so.
 // The streaming 1x1 kernel: d = pixel blocks in flight per wave, minb =
 // workgroups per CU (the persistent grid is minb per CU).
 struct Stream1x1Variant {
     int d, minb;
 };
 constexpr Stream1x1Variant kStream1x1Variants[] = {{3, 2}, {4, 2}, {2, 2}, {4, 1}};   // d * (C/32 + 8) < 64
-constexpr StripVariant kStripRb4Variants[] = {{256, 128, 4, 1, 1792, 2}, {256, 128, 4, 1, 1536, 3}, {512, 128, 8, 1, 3072, 3}};
+constexpr StripVariant kStripRb4Variants[] = {
+    {256, 128, 4, 1, 1792, 2}, {256, 128, 4, 1, 1536, 3}, {512, 128, 8, 1, 3072, 3}, {512, 128, 8, 1, 3072, 3},
+    {256, 128, 4, 1, 1536, 3}};
+// Variants that read the caller's KRSC filter rows instead of a packed copy.
+constexpr bool kStripRb4Direct[] = {false, false, false, true, true};
 constexpr StripVariant kStripRbVariants[] = {
     {512, 128, 4, 1, 2816, 2}, {512, 128, 4, 1, 2816, 3}, {256, 128, 2, 2, 1536, 2},
     {128, 128, 2, 2, 1024, 2}, {256, 256, 2, 2, 1536, 2}, {512, 128, 4, 1, 2816, 4},

@@ -35,7 +35,10 @@ constexpr int rb4_strip_loads_between(int p0, int p1, int S, int DSTEPS, int PER
 }
 
 // FD: how many taps ahead the filter slots are loaded (the ring holds FD+1).
-template <typename T, int BM, int BN, int WGM, int WGN, int STRIP, int S, int FD>
+// DIRECT: the filter is read as the caller's KRSC rows (a fragment lane's 8
+// channels are 16 contiguous bytes of one row) instead of the 16x16x32
+// fragment-order copy, so the layer needs no packing pass.
+template <typename T, int BM, int BN, int WGM, int WGN, int STRIP, int S, int FD, bool DIRECT>
 __global__ void __launch_bounds__(64 * WGM * WGN, (strip_rb_min_blocks<BM, BN, WGM, WGN>()))
     conv_strip_rb4_kernel(GemmArgs g) {
     constexpr int NT = 64 * WGM * WGN;
@@ -98,17 +101,26 @@ __global__ void __launch_bounds__(64 * WGM * WGN, (strip_rb_min_blocks<BM, BN, W
     // f = wave*FPW + q of each tap (output-channel block n0/16 + f, the
     // copy's last block again past it: its outputs are never stored), the
     // whole offset in the range-checked part.
+    //
+    // DIRECT: lane l of fragment (nb, kk) reads 16 bytes of KRSC row
+    // nb*16 + l%16 at element kk*32 + 8*(l/16); rows past K lie past the
+    // filter's K*Kc elements (below 2^31 bytes, checked on the host) and read
+    // as zero.  Tap positions below are in bytes of the packed copy (1 KiB per
+    // 32-deep step) or of a KRSC row (64 bytes per step).
     const int KK = g.Kc / 32;
     const int NBt = (g.K + 15) / 16;
-    const i32x4 frsrc = make_rsrc(g.b, uint32_t(int64_t(NBt) * KK * 1024));
+    const i32x4 frsrc = DIRECT ? make_rsrc(g.b, uint32_t(int64_t(g.K) * g.Kc * int(sizeof(T))))
+                               : make_rsrc(g.b, uint32_t(int64_t(NBt) * KK * 1024));
     uint32_t flane[FPW];
 #pragma unroll
     for (int q = 0; q < FPW; ++q) {
         const int nb = min(n0 / 16 + wave * FPW + q, NBt - 1);
-        flane[q] = uint32_t((int64_t(nb) * KK * 64 + lane) * 16);
+        flane[q] = DIRECT ? uint32_t((int64_t(nb * 16 + (lane & 15)) * g.Kc + (lane >> 4) * 8) * int(sizeof(T)))
+                          : uint32_t((int64_t(nb) * KK * 64 + lane) * 16);
     }
-    const int tap_bytes = g.C * 32;                                          // one tap of the filter rows
-    auto kbase = [&](int r, int cb) { return (r * S * g.C + cb * 32) * 32; };   // tap 0 of strip (r, cb)
+    constexpr int FB = DIRECT ? 2 : 32;                                          // bytes per filter element position
+    const int tap_bytes = g.C * FB;                                               // one tap of the filter rows
+    auto kbase = [&](int r, int cb) { return (r * S * g.C + cb * 32) * FB; };    // tap 0 of strip (r, cb)
 
     const uint32_t lds0 = lds_offset(smem);
     const uint32_t slots0 = lds0 + uint32_t(2 * BUF);

@@ -22,7 +22,7 @@ from parity import TORCH_DT, assert_parity, to_f64
 pytestmark = pytest.mark.gpu
 
 # kernel name -> (plan_info kernel id, number of compiled variants)
-KERNELS = {"reg": (0, 3), "dma": (1, 12), "wide": (2, 9), "nchw": (3, 12), "strip": (4, 5), "striprb": (5, 9), "nchwstrip": (6, 10), "nchwtile": (7, 6), "tile16": (8, 11), "streamk": (9, 12), "striprb2": (10, 2), "nchwtaps": (11, 6), "striprb3": (12, 3), "striprb4": (13, 3), "stream1x1": (14, 4)}
+KERNELS = {"reg": (0, 3), "dma": (1, 12), "wide": (2, 9), "nchw": (3, 12), "strip": (4, 5), "striprb": (5, 9), "nchwstrip": (6, 10), "nchwtile": (7, 6), "tile16": (8, 11), "streamk": (9, 12), "striprb2": (10, 2), "nchwtaps": (11, 6), "striprb3": (12, 3), "striprb4": (13, 5), "stream1x1": (14, 4)}
 # kernels compiled for some variants only
 VARIANTS = {"streamk": (8,)}
 
