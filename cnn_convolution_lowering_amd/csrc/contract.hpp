@@ -575,7 +575,8 @@ void launch_gemm(const conv_desc& d, const void* x, const void* w, const void* b
 #define CONVLOWER_STRIP_RB4_LAUNCH(I, S_)                                                                     \
     case S_: {                                                                                                \
         constexpr StripVariant v = kStripRb4Variants[I];                                                      \
-        conv_strip_rb4_kernel<T, v.bm, v.bn, v.wgm, v.wgn, v.strip, S_, v.bst, kStripRb4Direct[I]>              \
+        conv_strip_rb4_kernel<T, v.bm, v.bn, v.wgm, v.wgn, v.strip, S_, (v.bst < S_ ? v.bst : S_),              \
+                              kStripRb4Direct[I]>                                                        \
             <<<blocks, 64 * v.wgm * v.wgn, 0, st>>>(h);                                                        \
         break;                                                                                                \
     }

@@ -93,7 +93,7 @@ constexpr int kStripRb2Taps[] = {3, 5, 7, 9, 11};
 constexpr StripVariant kStripRb3Variants[] = {
     {512, 128, 4, 1, 3584, 1}, {256, 128, 4, 1, 1792, 1}, {512, 128, 4, 1, 3072, 1}};
 // The LDS-shared filter form: bst = how many taps ahead the filter slots are
-// loaded (a ring of bst + 1 slots of BN/16 KiB beside the two strip buffers;
+// loaded, at most S (a ring of bst + 1 slots of BN/16 KiB beside the two strip buffers;
 // 80 KiB in all, two workgroups per CU).  Variant 1: strip buffers of 24 KiB
 // (four output rows of up to 76 strip rows where Q divides 256) and the
 // filter three taps ahead.  Variant 2: 512 x 128 tiles over eight waves, 48 KiB
