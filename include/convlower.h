@@ -279,7 +279,7 @@ conv_status_t conv2d_fwd(conv_desc_t d, const void* x, const void* w, const void
  * it, so nothing is cleared between calls).  Errors as conv2d_fwd, and
  * CONV_ERR_UNSUPPORTED (nothing enqueued) when conv_workspace_size(d) exceeds
  * CONV_NOALLOC_SCRATCH_BYTES (for scale: the fused path of a 3x3, 512- to
- * 512-channel layer over 128 images of 7x7 keeps 26 MB of split-contraction
+ * 512-channel layer over 64 images of 7x7 keeps 12.8 MB of split-contraction
  * partial sums; lowered im2win / im2col buffers of large layers exceed it). */
 conv_status_t conv2d_fwd_noalloc(conv_desc_t d, const void* x, const void* w, const void* bias, void* y,
                                  void* stream);
@@ -289,9 +289,10 @@ conv_status_t conv2d_fwd_noalloc(conv_desc_t d, const void* x, const void* w, co
  * filter matrix" of "GPU-Accelerating MSCRED ...", section "Transforming
  * Conv2D into im2col and GEMM" -- or, for the register-streamed and
  * small-window kernels, into the order their MFMAs consume it.  A no-op when
- * the plan reads w in place (the fused path's pipelined kernels, and NHWC
- * with R == 1 or S == 1 and C a multiple of the 16-byte vector).  Pointer
- * rules and errors as conv2d_fwd. */
+ * the plan reads w in place (the fused path's pipelined and streaming 1x1
+ * kernels, the variants of kernel 13 that read the KRSC rows, and NHWC with
+ * R == 1 or S == 1 and C a multiple of the 16-byte vector).  Pointer rules
+ * and errors as conv2d_fwd. */
 conv_status_t conv_pack_filter(conv_desc_t d, const void* w, void* ws, void* stream);
 
 /* Stage 2: lower x into ws -- im2win strips ("Enabling Memory-efficient
