@@ -38,23 +38,24 @@ def _bits(t):
     return t.view(torch.int16 if t.element_size() == 2 else torch.int32)
 
 
-# (dtype, layout, algo, first shape, second smaller shape, padding, stride): the
-# split contraction's partials, the register-streamed strip kernel's filter copy,
-# the fp32 strip kernel's filter copy, a lowered im2win buffer
+# (dtype, layout, algo, first shape, second smaller shape, padding, stride,
+# plan): the split contraction's partials, the LDS-filter strip kernel's packed
+# filter copy (named: by default it reads the KRSC rows), the fp32 strip
+# kernel's filter copy, a lowered im2win buffer
 CASES = [
-    ("bf16", "nhwc", "implicit", (32, 512, 7, 7, 512, 3, 3), (8, 512, 7, 7, 512, 3, 3), 1, 1),
-    ("f16", "nhwc", "implicit", (32, 128, 64, 64, 128, 11, 11), (4, 128, 32, 32, 128, 11, 11), 5, 1),
-    ("f32", "nchw", "implicit", (1280, 32, 30, 30, 64, 3, 3), (64, 32, 30, 30, 64, 3, 3), 0, 2),
-    ("f16", "nhwc", "im2win", (8, 64, 20, 20, 96, 3, 3), (2, 64, 12, 12, 96, 3, 3), 1, 1),
+    ("bf16", "nhwc", "implicit", (32, 512, 7, 7, 512, 3, 3), (8, 512, 7, 7, 512, 3, 3), 1, 1, None),
+    ("f16", "nhwc", "implicit", (32, 128, 64, 64, 128, 11, 11), (4, 128, 32, 32, 128, 11, 11), 5, 1, "striprb4:2"),
+    ("f32", "nchw", "implicit", (1280, 32, 30, 30, 64, 3, 3), (64, 32, 30, 30, 64, 3, 3), 0, 2, None),
+    ("f16", "nhwc", "im2win", (8, 64, 20, 20, 96, 3, 3), (2, 64, 12, 12, 96, 3, 3), 1, 1, None),
 ]
 
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "%s-%s-%s" % c[:3])
 def test_noalloc_matches_conv2d_fwd(dev, case):
-    dt, lay, algo, first, second, pad, st = case
+    dt, lay, algo, first, second, pad, st, plan = case
     for i, shape in enumerate((first, second)):
         N, C, H, W, K, R, S = shape
-        d = cl.Conv2d(N, C, H, W, K, R, S, stride=st, padding=pad, layout=lay, dtype=dt, algo=algo)
+        d = cl.Conv2d(N, C, H, W, K, R, S, stride=st, padding=pad, layout=lay, dtype=dt, algo=algo, plan=plan)
         assert 0 < d.workspace_bytes <= SCRATCH or (i == 1 and d.workspace_bytes <= SCRATCH), d.info
         x, w, b = _inputs(N, C, H, W, K, R, S, dt, lay, 500 + i)
         xd, wd, bd = x.to(dev), w.to(dev), b.to(dev)
