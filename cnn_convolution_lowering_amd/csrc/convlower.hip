@@ -364,14 +364,15 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force, bool
         // SIMD, one workgroup per CU) with the filter shared through LDS --
         // one filter load per wave and tap instead of two, and 8 instead of
         // 32 per workgroup in the register form (interleaved timing: 2-3 %
-        // faster from 7 x 7 to 11 x 11 than both) -- reading the caller's
-        // KRSC filter rows, which saves the packing pass (with it, 6 % faster
-        // than the 256 x 128 tiles at 3 x 3 and 3 % at 5 x 5, 1 % at 7 x 7;
-        // at 9 x 9 and 11 x 11 level with the packed copy and its pass).
+        // faster from 7 x 7 to 11 x 11 than both).  Up to 7 taps reading the
+        // caller's KRSC filter rows, which saves the packing pass (with it, 6 %
+        // faster than the 256 x 128 tiles at 3 x 3 and 3 % at 5 x 5, 1 % at
+        // 7 x 7); from 9 taps the packed copy (level at 9 x 9, and at 11 x 11
+        // 1 % faster after a cache flush, pass included).
         if ((d.kernel == KERN_STRIP_RB3 || d.kernel == KERN_STRIP_RB4) && (d.M / 512) * (p.K / 128) >= 192 &&
             strip3_fits(kStripRb4Variants[3])) {
             d.kernel = KERN_STRIP_RB4;
-            d.variant = 3;
+            d.variant = p.S <= 7 ? 3 : 2;
         }
     } else {
         d.kernel = KERN_REG;
