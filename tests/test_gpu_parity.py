@@ -6,9 +6,10 @@ and both lowerings (several tiles and ragged tails in every GEMM dimension);
 integer-valued inputs, where fp32 accumulation is exact and the result must
 equal the reference rounded to the storage type bit for bit; delta kernels
 (y == x bit for bit); the lowered buffers and packed filter byte for byte;
-determinism; the staged entry points; error paths; and every output of the
-five workloads at their full sizes in the launch configuration the benchmark
-times, under all three algorithms.
+determinism; the staged entry points; error paths; mid-size layers whose
+default plans take the kernels chosen only for many tiles; and every output
+of the five workloads at their full sizes in the launch configuration the
+benchmark times, under all three algorithms.
 """
 from __future__ import annotations
 
@@ -90,6 +91,35 @@ def test_fuzz_parity(dev, case):
     w = (torch.randn(K, C, R, S, generator=g) / np.sqrt(C * R * S)).to(TORCH_DT[dt])
     b = (torch.randn(K, generator=g) * 0.1).to(TORCH_DT[dt]) if i % 4 != 3 else None
     _check_full(dev, _perm_x(x, lay), _perm_x(w, lay), b, lay, st, pd, dl, algo, dt, "fuzz %d" % i)
+
+
+# ------------------------------------------------- default plans, mid-size
+
+# Shapes large enough that the default plan takes the kernels chosen only for
+# many tiles, with sizes off their blocks: the LDS-filter strips on 512 x 128
+# tiles reading the KRSC rows (3x3 at an output width that does not divide the
+# tile, 5x5) and the packed copy (a 1x9 filter), and the streaming 1x1 kernel
+# (a pixel count off its 16-row blocks, K = 100).  (dtype, N, C, H, W, K, R,
+# S, padding, expected kernel, expected variant)
+MID_CASES = [
+    ("f16", 56, 32, 40, 48, 256, 3, 3, (1, 1), 13, 3),
+    ("bf16", 12, 32, 64, 64, 256, 5, 5, (2, 2), 13, 3),
+    ("f16", 12, 32, 64, 64, 256, 1, 9, (0, 4), 13, 2),
+    ("bf16", 5, 64, 60, 61, 100, 1, 1, (0, 0), 14, 2),
+]
+
+
+@pytest.mark.parametrize("case", MID_CASES, ids=lambda c: "%s-N%dC%dH%dW%dK%dR%dS%d" % c[:8])
+def test_default_plans_mid_size(dev, case):
+    dt, N, C, H, W, K, R, S, pd, kern, var = case
+    d = cl.Conv2d(N, C, H, W, K, R, S, padding=pd, layout="nhwc", dtype=dt, algo="implicit")
+    assert (d.info["kernel"], d.info["kernel_variant"]) == (kern, var), d.info
+    g = torch.Generator().manual_seed(4000 + N * 7 + S)
+    x = (torch.rand(N, C, H, W, generator=g) * 2 - 1).to(TORCH_DT[dt])
+    w = (torch.randn(K, C, R, S, generator=g) / np.sqrt(C * R * S)).to(TORCH_DT[dt])
+    b = (torch.randn(K, generator=g) * 0.1).to(TORCH_DT[dt])
+    _check_full(dev, _perm_x(x, "nhwc"), _perm_x(w, "nhwc"), b, "nhwc", (1, 1), pd, (1, 1), "implicit", dt,
+                "default plan %s" % (case,))
 
 
 # ---------------------------------------------------------------- exactness
