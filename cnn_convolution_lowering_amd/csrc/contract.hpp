@@ -314,6 +314,7 @@ void launch_gemm(const conv_desc& d, const void* x, const void* w, const void* b
             CONVLOWER_DMA_CASE(9)
             CONVLOWER_DMA_CASE(10)
             CONVLOWER_DMA_CASE(11)
+            CONVLOWER_DMA_CASE(12)
             default: break;
         }
 #undef CONVLOWER_DMA_CASE

@@ -47,7 +47,7 @@ conv_status_t from_hip(hipError_t e) { return e == hipSuccess ? CONV_OK : CONV_E
 // the blocked window loader or lowered rows) leave two workgroups per CU.
 bool streamk_variant(int v) {
     return v >= 0 && v < count_of(kDmaVariants) && kDmaVariants[v].bm == 128 && kDmaVariants[v].bn == 128 &&
-           kDmaVariants[v].early == 1 && kDmaVariants[v].wgm * kDmaVariants[v].wgn == 8;
+           kDmaVariants[v].early == 1 && kDmaVariants[v].wgm * kDmaVariants[v].wgn == 8 && kDmaVariants[v].stages == 2;
 }
 
 // force: "<kernel>:<variant>[:<ksplit>[:<tile order>]]" (conv_create_desc_forced,
@@ -281,19 +281,24 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force, bool
         // more, smaller pieces; interleaved timing on the kernel-size sweep's
         // 1x1 layer: 11 % faster than the 128 x 128 default)
         if (d.variant == 8 && p.R == 1 && p.S == 1 && (d.M / 256) * ((p.K + 127) / 128) >= 512) d.variant = 3;
-        // Fewer 128 x 128 tiles than CUs: 64 x 128 tiles over four waves
+        // Fewer 128 x 128 tiles than CUs: 1x1 layers, 128 x 128 over four
+        // waves (the 1x1 1024-channel layer at 14x14: 2-7 %, conv_tune's
+        // pick).  Otherwise, from half as many tiles as CUs, one round of
+        // 128 x 128 tiles over eight waves with four 64-deep stages (128 KiB
+        // of LDS, one workgroup per CU): cold, 2-3 % faster than the 64 x 128
+        // tiles below on the 3x3 256-channel layer at 14x14 and the 3x3
+        // 512-channel layer at 7x7 (both 196 tiles), 20 % faster than the
+        // same tiles with two stages; five stages level, six or eight 32-deep
+        // ones 15-24 % slower.  Below that, 64 x 128 tiles over four waves
         // (twice the workgroups) with three 64-deep stages (two workgroups
-        // per CU still fit); 1x1 layers: 128 x 128 over four waves.  On the
-        // 3x3 256-channel layer at 14x14: 6 % faster cold than the 128 x 128
-        // tiles with two stages, another 9 % with the third stage; on the 3x3
-        // 512-channel layer at 7x7 (a 4608-long contraction) level with the
-        // 128 x 128 tiles split in two, whose fp32 partials it does without
-        // (51 of the 91 MB that layer moved).  The 1x1 1024-channel layer at
-        // 14x14: 2-7 % (conv_tune's pick).
+        // per CU fit; on the 3x3 256-channel layer at 14x14 6 % faster cold
+        // than the 128 x 128 two-stage tiles, another 9 % with the third
+        // stage).
+        const int64_t tiles128 = (d.M / 128) * ((p.K + 127) / 128);
         if (d.variant == 8 && p.R == 1 && p.S == 1)
             d.variant = 9;
-        else if (d.variant == 8 && (d.M / 128) * ((p.K + 127) / 128) < 256)
-            d.variant = 11;
+        else if (d.variant == 8 && tiles128 < 256)
+            d.variant = tiles128 >= 128 ? kDmaOneRound : 11;
         // 1x1 layers the streaming kernel takes, from 16384 pixels: it
         // (C = K = 128 at 64x64, by interleaved timing after a 512 MiB
         // read-modify-write pass: 13 % faster than the 256 x 128 tiles at 32
@@ -510,7 +515,8 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force, bool
         int64_t ks = 1;
         if (force_ks > 0) {
             ks = force_ks < 8 ? force_ks : 8;
-        } else if (d.kernel == KERN_DMA && tiles > 0 && tiles < 256 && nkt >= 16 && (tiles <= 64 || kc >= 4096)) {
+        } else if (d.kernel == KERN_DMA && d.variant != kDmaOneRound && tiles > 0 && tiles < 256 && nkt >= 16 &&
+                   (tiles <= 64 || kc >= 4096)) {
             ks = 2;
         }
         if (ks > nkt) ks = nkt;

@@ -350,9 +350,9 @@ def test_split_contraction_plan():
         assert i["ws_partial_offset"] % 256 == 0
         assert i["ws_partial_offset"] >= i["ws_filter_offset"] + i["ws_filter_bytes"]
         assert c.workspace_bytes == i["ws_partial_offset"] + i["ws_partial_bytes"]
-    # plenty of output tiles, 196 tiles of 128 x 128 taken as 392 of 64 x 128
-    # (a contraction of moderate length or a 4608-long one), or a short
-    # contraction: no split
+    # plenty of output tiles, 196 tiles of 128 x 128 taken in one round of the
+    # four-stage tiles (a contraction of moderate length or a 4608-long one),
+    # or a short contraction: no split
     for a in [(32, 128, 64, 64, 128, 3, 3, 1), (128, 1024, 14, 14, 256, 1, 1, 0), (2, 32, 8, 8, 32, 1, 1, 0),
               (64, 256, 14, 14, 256, 3, 3, 1), (128, 512, 7, 7, 512, 3, 3, 1)]:
         for algo in ("implicit", "im2win", "im2col"):
@@ -438,7 +438,7 @@ def test_streamk_plan():
         c = cl.Conv2d(2, args["C"], 17, 17, 72, 3, 3, padding=1, layout=args["layout"], dtype=args["dtype"],
                       algo="implicit", plan="streamk:8")
         assert c.info["kernel"] != 9, kw
-    for v in (0, 7, 9, 10, 11):
+    for v in (0, 7, 9, 10, 11, 12):
         c = cl.Conv2d(2, 64, 17, 17, 72, 3, 3, padding=1, layout="nhwc", dtype="f16", algo="implicit",
                       plan="streamk:%d" % v)
         assert c.info["kernel"] != 9, v
