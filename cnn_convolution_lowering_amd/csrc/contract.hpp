@@ -315,6 +315,7 @@ void launch_gemm(const conv_desc& d, const void* x, const void* w, const void* b
             CONVLOWER_DMA_CASE(10)
             CONVLOWER_DMA_CASE(11)
             CONVLOWER_DMA_CASE(12)
+            CONVLOWER_DMA_CASE(13)
             default: break;
         }
 #undef CONVLOWER_DMA_CASE

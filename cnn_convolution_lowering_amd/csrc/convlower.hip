@@ -282,8 +282,12 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force, bool
         // 1x1 layer: 11 % faster than the 128 x 128 default)
         if (d.variant == 8 && p.R == 1 && p.S == 1 && (d.M / 256) * ((p.K + 127) / 128) >= 512) d.variant = 3;
         // Fewer 128 x 128 tiles than CUs: 1x1 layers, 128 x 128 over four
-        // waves (the 1x1 1024-channel layer at 14x14: 2-7 %, conv_tune's
-        // pick).  Otherwise, from half as many tiles as CUs, one round of
+        // waves (the 1x1 1024-channel layer at 14x14: 2-7 % ahead of the
+        // eight-wave tiles, conv_tune's pick) -- or, with 128 to 255 tiles
+        // of 256 x 128, those in one round, over eight waves with three
+        // 64-deep stages (144 KiB of LDS; that layer, 196 such tiles: 8 %
+        // faster cold than the four-wave 128 x 128 tiles, 5 % ahead of
+        // 128 x 256 tiles).  Otherwise, from half as many tiles as CUs, one round of
         // 128 x 128 tiles over eight waves with four 64-deep stages (128 KiB
         // of LDS, one workgroup per CU): cold, 2-3 % faster than the 64 x 128
         // tiles below on the 3x3 256-channel layer at 14x14 and the 3x3
@@ -295,8 +299,9 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force, bool
         // than the 128 x 128 two-stage tiles, another 9 % with the third
         // stage).
         const int64_t tiles128 = (d.M / 128) * ((p.K + 127) / 128);
+        const int64_t tiles256 = (d.M / 256) * ((p.K + 127) / 128);
         if (d.variant == 8 && p.R == 1 && p.S == 1)
-            d.variant = 9;
+            d.variant = tiles256 >= 128 && tiles256 < 256 ? kDmaOneRound1x1 : 9;
         else if (d.variant == 8 && tiles128 < 256)
             d.variant = tiles128 >= 128 ? kDmaOneRound : 11;
         // 1x1 layers the streaming kernel takes, from 16384 pixels: it
@@ -515,7 +520,7 @@ conv_status_t plan(const conv_params_t& p, conv_desc& d, const char* force, bool
         int64_t ks = 1;
         if (force_ks > 0) {
             ks = force_ks < 8 ? force_ks : 8;
-        } else if (d.kernel == KERN_DMA && d.variant != kDmaOneRound && tiles > 0 && tiles < 256 && nkt >= 16 &&
+        } else if (d.kernel == KERN_DMA && d.variant != kDmaOneRound && d.variant != kDmaOneRound1x1 && tiles > 0 && tiles < 256 && nkt >= 16 &&
                    (tiles <= 64 || kc >= 4096)) {
             ks = 2;
         }

@@ -50,12 +50,14 @@ constexpr TileVariant kDmaVariants[] = {
     {128, 32, 32, 4, 1, 4}, {128, 64, 32, 2, 2, 4}, {128, 128, 32, 2, 2, 4}, {256, 128, 32, 2, 2, 3},
     {256, 128, 32, 4, 2, 4}, {256, 256, 32, 4, 2, 3}, {128, 128, 64, 2, 2, 2}, {128, 128, 64, 4, 2, 2},
     {128, 128, 64, 4, 2, 2, 1}, {128, 128, 64, 2, 2, 2, 1}, {256, 128, 64, 4, 2, 2, 1}, {64, 128, 64, 2, 2, 3, 1},
-    {128, 128, 64, 4, 2, 4, 1},
+    {128, 128, 64, 4, 2, 4, 1}, {256, 128, 64, 4, 2, 3, 1},
 };
-// The pipelined shape planned for one round of tiles (fewer 128 x 128 tiles
-// than CUs): never split, as its point is one tile per CU.
+// The pipelined shapes planned for one round of tiles (fewer tiles than CUs;
+// 1x1 layers: 256 x 128 tiles): never split, as their point is one tile per CU.
 constexpr int kDmaOneRound = 12;
+constexpr int kDmaOneRound1x1 = 13;
 static_assert(kDmaVariants[kDmaOneRound].bm == 128 && kDmaVariants[kDmaOneRound].stages == 4, "one-round shape");
+static_assert(kDmaVariants[kDmaOneRound1x1].bm == 256 && kDmaVariants[kDmaOneRound1x1].stages == 3, "one-round shape");
 // The ConvLSTM step's contraction: 64 packed gate rows per tile, one wave
 // across them (the cell update needs all four gates of a hidden channel).
 constexpr TileVariant kLstmVariant = {128, 64, 32, 4, 1, 4};

@@ -438,7 +438,7 @@ def test_streamk_plan():
         c = cl.Conv2d(2, args["C"], 17, 17, 72, 3, 3, padding=1, layout=args["layout"], dtype=args["dtype"],
                       algo="implicit", plan="streamk:8")
         assert c.info["kernel"] != 9, kw
-    for v in (0, 7, 9, 10, 11, 12):
+    for v in (0, 7, 9, 10, 11, 12, 13):
         c = cl.Conv2d(2, 64, 17, 17, 72, 3, 3, padding=1, layout="nhwc", dtype="f16", algo="implicit",
                       plan="streamk:%d" % v)
         assert c.info["kernel"] != 9, v

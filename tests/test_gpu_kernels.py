@@ -22,7 +22,7 @@ from parity import TORCH_DT, assert_parity, to_f64
 pytestmark = pytest.mark.gpu
 
 # kernel name -> (plan_info kernel id, number of compiled variants)
-KERNELS = {"reg": (0, 3), "dma": (1, 13), "wide": (2, 9), "nchw": (3, 12), "strip": (4, 5), "striprb": (5, 9), "nchwstrip": (6, 10), "nchwtile": (7, 6), "tile16": (8, 11), "streamk": (9, 12), "striprb2": (10, 2), "nchwtaps": (11, 6), "striprb3": (12, 3), "striprb4": (13, 5), "stream1x1": (14, 4)}
+KERNELS = {"reg": (0, 3), "dma": (1, 14), "wide": (2, 9), "nchw": (3, 12), "strip": (4, 5), "striprb": (5, 9), "nchwstrip": (6, 10), "nchwtile": (7, 6), "tile16": (8, 11), "streamk": (9, 12), "striprb2": (10, 2), "nchwtaps": (11, 6), "striprb3": (12, 3), "striprb4": (13, 5), "stream1x1": (14, 4)}
 # kernels compiled for some variants only
 VARIANTS = {"streamk": (8,)}
 
@@ -226,7 +226,7 @@ def test_forced_kernel_integer_exact(dev):
     ref = oracle.conv2d(xl, wl, b, layout="nhwc", stride=1, padding=1)
     want = torch.from_numpy(ref).to(torch.float32).to(torch.float16)
     for forced in ("strip:0", "strip:2", "strip:3", "wide:0", "wide:5", "striprb:0", "striprb:3", "striprb:4",
-                   "dma:8", "dma:9", "dma:10", "dma:11", "dma:12", "striprb2:0", "striprb2:1", "striprb3:0", "striprb3:1",
+                   "dma:8", "dma:9", "dma:10", "dma:11", "dma:12", "dma:13", "striprb2:0", "striprb2:1", "striprb3:0", "striprb3:1",
                    "striprb4:0"):
         d = cl.Conv2d(N, C, H, W, K, R, S, padding=1, layout="nhwc", dtype="f16", algo="implicit", plan=forced)
         assert d.info["kernel"] == KERNELS[forced.split(":")[0]][0], forced
