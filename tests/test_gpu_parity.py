@@ -98,14 +98,21 @@ def test_fuzz_parity(dev, case):
 # Shapes large enough that the default plan takes the kernels chosen only for
 # many tiles, with sizes off their blocks: the LDS-filter strips on 512 x 128
 # tiles reading the KRSC rows (3x3 at an output width that does not divide the
-# tile, 5x5) and the packed copy (a 1x9 filter), and the streaming 1x1 kernel
-# (a pixel count off its 16-row blocks, K = 100).  (dtype, N, C, H, W, K, R,
+# tile, 5x5) and the packed copy (a 1x9 filter), the streaming 1x1 kernel
+# (a pixel count off its 16-row blocks, K = 100), and the pipelined kernel's
+# one-round tile shapes.  (dtype, N, C, H, W, K, R,
 # S, padding, expected kernel, expected variant)
 MID_CASES = [
     ("f16", 56, 32, 40, 48, 256, 3, 3, (1, 1), 13, 3),
     ("bf16", 12, 32, 64, 64, 256, 5, 5, (2, 2), 13, 3),
     ("f16", 12, 32, 64, 64, 256, 1, 9, (0, 4), 13, 2),
     ("bf16", 5, 64, 60, 61, 100, 1, 1, (0, 0), 14, 2),
+    # one round of the pipelined kernel's 128 x 128 four-stage tiles (164 of
+    # them, last row of tiles and last column ragged), and of its 256 x 128
+    # tiles on a 1x1 layer the streaming kernel does not take (96 channels;
+    # 202 tiles, both ragged)
+    ("bf16", 20, 64, 23, 23, 200, 3, 3, (1, 1), 1, 12),
+    ("f16", 7, 96, 61, 61, 136, 1, 1, (0, 0), 1, 13),
 ]
 
 
