@@ -446,11 +446,15 @@ def test_streamk_plan():
 
 def test_tile_order_plan():
     """The pipelined kernel's tile order is the fourth field of a forced plan
-    and defaults to XCD ranges in serpentine order (2); other kernels ignore
-    it."""
+    and defaults to XCD ranges in serpentine order (2), column-major ranges
+    (3) for the one-round 128 x 128 tiles; other kernels ignore it."""
     a = (64, 256, 14, 14, 256, 3, 3)
     c = cl.Conv2d(*a, padding=1, layout="nhwc", dtype="f16", algo="implicit")
-    assert c.info["kernel"] == 1 and c.info["tile_order"] == 2
+    assert (c.info["kernel"], c.info["kernel_variant"], c.info["tile_order"]) == (1, 12, 3)
+    c = cl.Conv2d(*a, padding=1, layout="nhwc", dtype="f16", algo="implicit", plan="dma:12:1")
+    assert c.info["tile_order"] == 3
+    c = cl.Conv2d(128, 1024, 14, 14, 256, 1, 1, layout="nhwc", dtype="bf16", algo="implicit")
+    assert (c.info["kernel"], c.info["kernel_variant"], c.info["tile_order"]) == (1, 13, 2)
     c = cl.Conv2d(*a, padding=1, layout="nhwc", dtype="f16", algo="implicit", plan="dma:8:1")
     assert c.info["tile_order"] == 2
     for o in range(4):
